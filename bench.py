@@ -1,0 +1,189 @@
+"""Benchmark: single-token decode MoE layer with MXFP4 routed experts on one
+MI355X.
+
+Workload (one step = one whole decode layer for one token): router GEMV over
+a bf16 896x7168 router, sigmoid top-16 of 896 with renormalised weights, the
+16 selected SwiGLU experts (hidden 7168, inter 1536, MXFP4) read straight from
+their packed bytes, and the rank-order weighted combine to bf16. All 896
+experts (15.7 GB packed) are resident in HBM before timing starts. Each step
+takes a fresh token (a bank of distinct seeded tokens, so expert sets differ
+step to step) and one of several copies of the router (so the router is not
+served from the last-level cache either).
+
+Prints one JSON line. `value` is the effective HBM rate of MXFP4 expert
+weights: packed bytes of the 16 experts a token touches divided by the whole
+layer's time per step (router and selection included in the time but not in
+the bytes). `roofline` covers the dominant kernel (the gate/up + SwiGLU
+stage), timed live with HIP events on its stream; `cpu_baseline` is the
+oracle (plain C, fp64) timed on the host's cores over a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective HBM GB/s of MXFP4 expert weights (% of 8 TB/s); MoE-layer tokens/s"
+PEAK_HBM_GBS = 8000.0
+BYTES_PER_EXPERT = 17547264            # 3 x 7168 x 1536 weights at 0.53125 B
+GATE_UP_BYTES_PER_EXPERT = 11698176    # 2 x 1536 x 7168 x 0.53125
+ROUTER_BYTES = 896 * 7168 * 2
+
+
+def log(msg):
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle as it stands on a bounded sample: whole decode layers for
+    fresh tokens until ~budget_s of oracle time is spent."""
+    import gen
+    import oracle
+    from gen import workloads as W
+    threads = min(16, os.cpu_count() or 1)
+    oracle.set_threads(threads)
+    R = W.router_bf16(0, W.C3)
+    spent, tokens = 0.0, 0
+    while spent < budget_s and tokens < 64:
+        x = W.tokens_bf16(0, W.C3, 1, batch=10_000 + tokens)[0]
+        idx, _ = oracle.topk(oracle.router_logits(x, R), W.TOPK)
+        experts = {int(e): W.expert_weights(0, W.C3, int(e)) for e in idx}
+        t0 = time.perf_counter()
+        oracle.moe_layer(x, R, experts, W.TOPK, W.HIDDEN, W.INTER)
+        spent += time.perf_counter() - t0
+        tokens += 1
+    per_token = spent / tokens
+    return {"value": round(BYTES_PER_EXPERT * W.TOPK / per_token / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "tokens_per_s": round(1.0 / per_token, 4),
+            "sample": f"{tokens} fresh decode tokens through the full oracle layer (router "
+                      f"896x7168 + 16 experts 7168/1536, fp64), {spent:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--tokens", type=int, default=512, help="distinct tokens in the bank")
+    ap.add_argument("--router-copies", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the sharding design is described in DESIGN.md); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mxfp4_packed_weight_amd as K
+    from gen import device as D
+    from gen import workloads as W
+
+    dev = torch.device("cuda:0")
+    n, hidden, inter, k = W.N_EXPERTS, W.HIDDEN, W.INTER, W.TOPK
+    t0 = time.time()
+    pool = D.build_expert_pool(0, W.C3, n, device=dev, log=log)
+    log(f"expert pool ready in {time.time() - t0:.1f} s")
+    R = D.to_device(W.router_bf16(0, W.C3).view(np.int16), dev)
+    routers = [R] + [R.clone() for _ in range(args.router_copies - 1)]
+    bank = D.to_device(W.tokens_bf16(0, W.C3, args.tokens, batch=1).view(np.int16), dev)
+    ws = torch.empty(K.k3_moe_workspace_bytes(1, n, hidden, inter, k), dtype=torch.uint8,
+                     device=dev)
+    y = torch.empty(hidden, dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        K.k3_moe_layer(bank[i % args.tokens], routers[i % len(routers)], pool.table, n, hidden,
+                       inter, k, y, ws, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    expert_bytes = k * BYTES_PER_EXPERT
+    value = expert_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"layer: {ms_per_step * 1e3:.2f} us/step, {value:.1f} GB/s expert weights")
+
+    # Dominant kernel: the gate/up + SwiGLU stage over the 16 selected experts,
+    # launched back to back on fresh tokens' routing, timed with HIP events on
+    # the same stream.
+    T = args.tokens
+    lg = torch.empty((T, n), dtype=torch.float64, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    K.k3_router(bank, R, T, hidden, n, lg)
+    K.k3_router_topk(lg, None, T, n, k, idx, w)
+    h = torch.empty((k, inter), dtype=torch.float32, device=dev)
+    reps = max(args.steps, 50)
+    for i in range(10):
+        K.k3_expert_gate_up(bank[i % T], pool.table, idx[i % T], k, hidden, inter, h)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(reps):
+        K.k3_expert_gate_up(bank[i % T], pool.table, idx[i % T], k, hidden, inter, h)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    gu_us = ev0.elapsed_time(ev1) / reps * 1e3
+    gu_bytes = k * GATE_UP_BYTES_PER_EXPERT
+    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
+    log(f"gate/up stage: {gu_us:.2f} us/launch, {achieved:.1f} GB/s")
+
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "gate_up_c3_traffic.json")
+    if os.path.exists(tpath):
+        with open(tpath) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_hash") == _kernel_hash():
+            traffic = tr.get("bytes_per_launch")
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "decode MoE layer, 1 token: bf16 router 896x7168, sigmoid "
+                               "top-16 of 896 MXFP4 experts (hidden 7168, inter 1536, 15.7 GB "
+                               "resident), SwiGLU, rank-order combine to bf16",
+                   "tokens_per_step": 1, "n_experts": n, "topk": k, "hidden": hidden,
+                   "inter": inter, "expert_bytes_per_step": expert_bytes,
+                   "router_bytes_per_step": ROUTER_BYTES},
+        "tokens_per_s": round(1e3 / ms_per_step, 1),
+        "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "all_bytes_GBs": round((expert_bytes + ROUTER_BYTES) / (ms_per_step * 1e-3) / 1e9, 2),
+        "roofline": {"kernel": "gate_up_kernel (k3_expert_gate_up)", "bound": "hbm",
+                     "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "launch_us": round(gu_us, 3), "algorithmic_bytes_per_launch": gu_bytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host (bounded sample)")
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out))
+
+
+def _kernel_hash():
+    import hashlib
+    hsh = hashlib.sha256()
+    for f in ("k3_decode.h", "k3_expert.hip"):
+        with open(os.path.join(ROOT, "mxfp4_packed_weight_amd", "csrc", f), "rb") as fh:
+            hsh.update(fh.read())
+    return hsh.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,215 @@
+/*
+ * k3moe — MXFP4 routed-expert MoE path for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libk3moe.so. Every pointer named *_d, and every tensor argument of
+ * a compute call, is a DEVICE pointer; *_host functions take host pointers.
+ * bf16 values travel as uint16_t bit patterns. Nothing here allocates: the
+ * caller owns every buffer, including the workspace. Compute calls validate
+ * all arguments on the host before anything is enqueued (on error nothing is
+ * launched), then enqueue asynchronously on `stream` and never synchronise.
+ * Calls on different streams with different outputs and workspaces may run
+ * concurrently.
+ *
+ * Sources (web pages describing the kimi-k3-in-c engine), cited below as:
+ *  [A176] "kimi-k3-in-c: A 176 KB Engine That Runs a 2.78T-Parameter MoE in
+ *         8 GB of RAM"
+ *  [SAT]  ai.thesatyajit.com, "kimi-k3-in-c" explainer
+ *  [ZOR]  "Running Kimi K3 locally: activation sparsity as architecture"
+ *
+ * MXFP4: a weight is a 4-bit E2M1 code; 32 consecutive weights of a row share
+ * one 8-bit E8M0 exponent e meaning 2^(e-127); 0.53125 bytes per weight
+ * ([A176] "The four reductions"). Exponent byte 255 (the format's NaN) makes
+ * its group contribute nothing, even where the activations are not finite
+ * ([A176] "What byte-identical actually costs"). Exact-domain contract: for
+ * exponent bytes in [2, 252] every decoded weight is an fp32 normal number;
+ * outside that range results follow fp32 (under/overflow) and are not gated.
+ *
+ * Canonical layout (the checkpoint's bytes): nib[rows][cols/2] with element
+ * 2b in the LOW nibble of byte b and element 2b+1 in the high nibble ([ZOR]
+ * "What are the four reductions, and why is the answer unchanged?"), and
+ * sc[rows][cols/32]. The compute calls read the device tile layout written by
+ * k3_mxfp4_pack / k3_expert_pack (a one-time re-tiling, see k3_mxfp4_pack).
+ *
+ * Status codes: K3_ERR_ARG for a NULL or misaligned pointer (all device
+ * pointers must be 16-byte aligned); K3_ERR_CONFIG for dimensions the path
+ * does not support or that contradict each other (the call names them in
+ * k3_last_error; nothing is defaulted, following the pages' config reader
+ * that refuses to guess, [A176] "What byte-identical actually costs");
+ * K3_ERR_MEMORY when the workspace is smaller than the call needs (the
+ * message gives both sizes: a memory limit, not an engine ceiling, [A176]
+ * "The interesting design decisions"); K3_ERR_DEVICE when the HIP runtime
+ * reports a launch or runtime error.
+ */
+#ifndef K3MOE_H
+#define K3MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t; NULL means the default stream. */
+typedef struct ihipStream_t *k3_stream_t;
+
+typedef int k3_status;
+#define K3_OK 0
+#define K3_ERR_ARG 1
+#define K3_ERR_CONFIG 2
+#define K3_ERR_MEMORY 3
+#define K3_ERR_DEVICE 4
+
+/* Largest expert count and top-k the routing kernels handle, and the largest
+ * expert dimensions (the expert kernels keep one activation vector in LDS). */
+#define K3_MAX_EXPERTS 4096
+#define K3_MAX_TOPK 64
+#define K3_MAX_HIDDEN 16384
+#define K3_MAX_INTER 8192
+
+const char *k3_strerror(k3_status s);
+/* Detail of the last failed call on the calling thread ("" if none). */
+const char *k3_last_error(void);
+int k3_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Layout. A matrix W[rows][cols] (cols % 32 == 0) is stored as ceil(rows/64)
+ * tiles of 64 rows. With G = cols/32 groups and G4 = ceil(G/4), tile t is G4
+ * quad blocks of 4352 bytes; quad block q of tile t holds, for l = 0..63:
+ *   bytes [1024*b + 16*l, +16)  the 16 canonical bytes (32 codes) of group
+ *                               g = 4q+b of row 64t + l (zero for g >= G);
+ *   byte  4096 + 4*l + b        the exponent byte of that group (255 for
+ *                               g >= G).
+ * so lane l of a wave reads its row's group g with one 16-byte load, the
+ * wave's 64 loads are one contiguous KiB, and a wave walking a row range
+ * reads one contiguous stream. Rows past `rows` are zero codes with exponent
+ * 255. Tile size 4352*G4 bytes (no padding when G % 4 == 0). Groups of 32
+ * are 16 packed bytes ([SAT] "Reduction one"), which is what makes a group
+ * one 128-bit load.
+ * ---------------------------------------------------------------------- */
+size_t k3_mxfp4_packed_bytes(int rows, int cols);
+/* Host re-tiling; tiles must hold k3_mxfp4_packed_bytes(rows, cols). */
+k3_status k3_mxfp4_pack_host(const uint8_t *nib, const uint8_t *sc, int rows,
+                             int cols, uint8_t *tiles);
+k3_status k3_mxfp4_unpack_host(const uint8_t *tiles, int rows, int cols,
+                               uint8_t *nib, uint8_t *sc);
+/* Same re-tiling on the device (all pointers device). */
+k3_status k3_mxfp4_pack(const uint8_t *nib_d, const uint8_t *sc_d, int rows,
+                        int cols, uint8_t *tiles_d, k3_stream_t stream);
+k3_status k3_mxfp4_unpack(const uint8_t *tiles_d, int rows, int cols,
+                          uint8_t *nib_d, uint8_t *sc_d, k3_stream_t stream);
+
+/* A routed expert ([SAT] "Reduction one": three MXFP4 matrices, gate and up
+ * [inter][hidden], down [hidden][inter]) is one blob:
+ *   [gate/up tiles][down tiles]
+ * The gate/up part is the tile layout above over 2*inter virtual rows in
+ * which tile t holds gate rows 32t..32t+31 in lanes 0..31 and up rows
+ * 32t..32t+31 in lanes 32..63 (so one tile yields both inputs of the SwiGLU
+ * for 32 rows). The down part is the plain tile layout of W_down.
+ * hidden % 32 == 0 and inter % 32 == 0 are required, hidden <= K3_MAX_HIDDEN,
+ * inter <= K3_MAX_INTER. */
+size_t k3_expert_packed_bytes(int hidden, int inter);
+k3_status k3_expert_pack_host(const uint8_t *gate_nib, const uint8_t *gate_sc,
+                              const uint8_t *up_nib, const uint8_t *up_sc,
+                              const uint8_t *down_nib, const uint8_t *down_sc,
+                              int hidden, int inter, uint8_t *expert);
+k3_status k3_expert_pack(const uint8_t *gate_nib_d, const uint8_t *gate_sc_d,
+                         const uint8_t *up_nib_d, const uint8_t *up_sc_d,
+                         const uint8_t *down_nib_d, const uint8_t *down_sc_d,
+                         int hidden, int inter, uint8_t *expert_d,
+                         k3_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * y[rows] = W[rows][cols] . x[cols] read straight from the packed bytes,
+ * never expanded to floats ([SAT] "Reduction one"). Each 32-group is summed
+ * and then scaled once by its exponent; exponent 255 contributes nothing.
+ * fp32 accumulation in a fixed order: each row is reduced by one workgroup
+ * along a fixed tree, so results are bit-identical from run to run (the
+ * pages' fixed-order rule, [SAT] "A floating-point contract, not a
+ * convention"). x fp32 [cols], tiles from k3_mxfp4_pack, y fp32 [rows].
+ * ---------------------------------------------------------------------- */
+k3_status k3_mxfp4_gemv(const float *x, const uint8_t *tiles, int rows,
+                        int cols, float *y, k3_stream_t stream);
+
+/* One routed expert, SwiGLU: g = W_gate x, u = W_up x, h = SiLU(g) * u
+ * (fp32, not rounded to bf16), y = W_down h. x bf16 [hidden]; expert from
+ * k3_expert_pack; y fp32 [hidden]; h fp32 [inter] receives h (it is also the
+ * call's only scratch). */
+k3_status k3_expert_swiglu(const uint16_t *x, const uint8_t *expert,
+                           int hidden, int inter, float *y, float *h,
+                           k3_stream_t stream);
+
+/* The two stages of k3_expert_swiglu over k routing slots of one token, and
+ * the weighted combine, as separate calls (k3_moe_layer runs exactly these):
+ *   k3_expert_gate_up:  h[j][inter] = SiLU(W_gate(e_j) x) * (W_up(e_j) x)
+ *   k3_expert_down:     yp[j][hidden] = W_down(e_j) h[j]
+ *   k3_moe_combine:     y[i] = sum_{j<k} w[j] * yp[j][i] in rank order (fp32),
+ *                       y_f32 (optional) the fp32 value, y bf16 (RNE).
+ * with e_j = idx[j] (device int32 [k], each in [0, n_experts)) and experts the
+ * device pointer table of k3_moe_layer. 1 <= k <= K3_MAX_TOPK. */
+k3_status k3_expert_gate_up(const uint16_t *x, const uint8_t *const *experts,
+                            const int32_t *idx, int k, int hidden, int inter,
+                            float *h, k3_stream_t stream);
+k3_status k3_expert_down(const float *h, const uint8_t *const *experts,
+                         const int32_t *idx, int k, int hidden, int inter,
+                         float *yp, k3_stream_t stream);
+k3_status k3_moe_combine(const float *yp, const float *w, int k, int hidden,
+                         uint16_t *y, float *y_f32, k3_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Router. logits[t][e] = sum_k x[t][k] * R[e][k] over bf16 operands, with
+ * products and sums in fp64 (routers stay in the resident bf16 set, [ZOR]
+ * "How does a 2.78-trillion-parameter model fit in 8 GB?"). x [T][hidden],
+ * router_w [n_experts][hidden] row-major, logits fp64 [T][n_experts].
+ * ---------------------------------------------------------------------- */
+k3_status k3_router(const uint16_t *x, const uint16_t *router_w, int T,
+                    int hidden, int n_experts, double *logits,
+                    k3_stream_t stream);
+
+/* Top-k per token. Key = logit without bias, sigmoid(logit) + bias[e] with
+ * one; selection by key, ties to the lower expert index, idx in descending
+ * key order. Weights from the UNBIASED scores s = sigmoid(logit),
+ * renormalised w_j = s_j / sum s (the bias steers selection only, [ZOR]
+ * "How is the C engine actually built?", invariant 3). Keys, sigmoid and the
+ * sums are fp64. logits [T][n_experts] (fp64 or fp32 variant), bias fp32
+ * [n_experts] or NULL, idx int32 [T][k], w fp32 [T][k].
+ * 1 <= k <= min(n_experts, K3_MAX_TOPK), n_experts <= K3_MAX_EXPERTS. */
+k3_status k3_router_topk(const double *logits, const float *bias, int T,
+                         int n_experts, int k, int32_t *idx, float *w,
+                         k3_stream_t stream);
+k3_status k3_router_topk_f32(const float *logits, const float *bias, int T,
+                             int n_experts, int k, int32_t *idx, float *w,
+                             k3_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Whole decode MoE layer for one token: router GEMV -> sigmoid top-k ->
+ * the k selected SwiGLU experts -> y = sum_j w_j * y_j in rank order (fp32)
+ * -> bf16 (round to nearest even). 16 of 896 experts per token in the
+ * pages' model ([A176] opening section).
+ *   x         bf16 [hidden]
+ *   router_w  bf16 [n_experts][hidden]
+ *   experts   device array of n_experts device pointers, experts[e] -> blob
+ *             of k3_expert_pack for expert e
+ *   y         bf16 [hidden]
+ *   ws        workspace of >= k3_moe_workspace_bytes(1, n_experts, hidden,
+ *             inter, k) bytes
+ * k3_moe_layer_ex also writes (any may be NULL) y_f32 [hidden] (the value
+ * before the bf16 cast), idx int32 [k], w fp32 [k], logits fp64 [n_experts].
+ * ---------------------------------------------------------------------- */
+size_t k3_moe_workspace_bytes(int T, int n_experts, int hidden, int inter,
+                              int k);
+k3_status k3_moe_layer(const uint16_t *x, const uint16_t *router_w,
+                       const uint8_t *const *experts, int n_experts,
+                       int hidden, int inter, int k, uint16_t *y, void *ws,
+                       size_t ws_bytes, k3_stream_t stream);
+k3_status k3_moe_layer_ex(const uint16_t *x, const uint16_t *router_w,
+                          const uint8_t *const *experts, int n_experts,
+                          int hidden, int inter, int k, uint16_t *y,
+                          float *y_f32, int32_t *idx, float *w,
+                          double *logits, void *ws, size_t ws_bytes,
+                          k3_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

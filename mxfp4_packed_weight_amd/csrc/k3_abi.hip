@@ -1,0 +1,426 @@
+// C ABI of libk3moe.so: argument validation, workspace carving and the
+// launch sequence of each entry point. Every check happens before the first
+// launch, so a refused call enqueues nothing (the pages' config reader that
+// refuses to guess, [A176] "What byte-identical actually costs"; the up-front
+// memory refusal, [A176] "The interesting design decisions").
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "k3_internal.h"
+
+namespace k3 {
+
+void pack_plain_host(const uint8_t *nib, const uint8_t *sc, int rows, int cols,
+                     uint8_t *tiles);
+void unpack_plain_host(const uint8_t *tiles, int rows, int cols, uint8_t *nib,
+                       uint8_t *sc);
+void pack_expert_host(const uint8_t *gn, const uint8_t *gs, const uint8_t *un,
+                      const uint8_t *us, const uint8_t *dn, const uint8_t *ds,
+                      int hidden, int inter, uint8_t *dst);
+
+namespace {
+thread_local char g_err[512];
+
+constexpr int kMaxDim = 1 << 20;  // rows / cols / hidden / inter / T bound
+
+struct WsLayout {
+  size_t logits, idx, w, h, yp, total;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(int T, int n, int hidden, int inter, int k) {
+  WsLayout L;
+  size_t off = 0;
+  L.logits = off;
+  off += align256((size_t)T * n * sizeof(double));
+  L.idx = off;
+  off += align256((size_t)T * k * sizeof(int32_t));
+  L.w = off;
+  off += align256((size_t)T * k * sizeof(float));
+  L.h = off;
+  off += align256((size_t)T * k * inter * sizeof(float));
+  L.yp = off;
+  off += align256((size_t)T * k * hidden * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+k3_status fail(k3_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+int num_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+            hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+void set_error(const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+}
+
+k3_status device_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return K3_OK;
+  return fail(K3_ERR_DEVICE, "%s: HIP error %d (%s)", what, (int)e,
+              hipGetErrorString(e));
+}
+
+}  // namespace k3
+
+using namespace k3;
+
+#define K3_NEED_PTR(fn, p)                                                    \
+  do {                                                                        \
+    if (!(p)) return fail(K3_ERR_ARG, "%s: %s is NULL", fn, #p);              \
+    if (!aligned16(p))                                                        \
+      return fail(K3_ERR_ARG, "%s: %s is not 16-byte aligned", fn, #p);       \
+  } while (0)
+
+#define K3_NEED(fn, cond, ...)                                                \
+  do {                                                                        \
+    if (!(cond)) return fail(K3_ERR_CONFIG, __VA_ARGS__);                     \
+  } while (0)
+
+#define K3_LAUNCH(fn, expr)                                                   \
+  do {                                                                        \
+    const hipError_t e_ = (expr);                                             \
+    if (e_ != hipSuccess) return device_status(e_, fn);                       \
+  } while (0)
+
+static k3_status check_mat(const char *fn, int rows, int cols) {
+  K3_NEED(fn, rows >= 1 && rows <= kMaxDim, "%s: rows=%d outside [1, %d]", fn,
+          rows, kMaxDim);
+  K3_NEED(fn, cols >= 32 && cols <= kMaxDim && cols % 32 == 0,
+          "%s: cols=%d must be a positive multiple of the group size 32 "
+          "(<= %d)",
+          fn, cols, kMaxDim);
+  return K3_OK;
+}
+
+static k3_status check_expert_dims(const char *fn, int hidden, int inter) {
+  K3_NEED(fn, hidden >= 32 && hidden <= K3_MAX_HIDDEN && hidden % 32 == 0,
+          "%s: hidden=%d must be a positive multiple of 32 (<= %d)", fn,
+          hidden, K3_MAX_HIDDEN);
+  K3_NEED(fn, inter >= 32 && inter <= K3_MAX_INTER && inter % 32 == 0,
+          "%s: inter=%d must be a positive multiple of 32 (<= %d)", fn, inter,
+          K3_MAX_INTER);
+  return K3_OK;
+}
+
+static k3_status check_routing(const char *fn, int T, int n, int k) {
+  K3_NEED(fn, T >= 1 && T <= kMaxDim, "%s: T=%d outside [1, %d]", fn, T,
+          kMaxDim);
+  K3_NEED(fn, n >= 1 && n <= K3_MAX_EXPERTS, "%s: n_experts=%d outside [1, %d]",
+          fn, n, K3_MAX_EXPERTS);
+  K3_NEED(fn, k >= 1 && k <= n && k <= K3_MAX_TOPK,
+          "%s: k=%d outside [1, min(n_experts=%d, %d)]", fn, k, n,
+          K3_MAX_TOPK);
+  return K3_OK;
+}
+
+extern "C" {
+
+const char *k3_strerror(k3_status s) {
+  switch (s) {
+    case K3_OK: return "ok";
+    case K3_ERR_ARG: return "invalid argument (NULL or misaligned pointer)";
+    case K3_ERR_CONFIG: return "unsupported or contradictory configuration";
+    case K3_ERR_MEMORY:
+      return "workspace too small: a memory limit, not an engine ceiling";
+    case K3_ERR_DEVICE: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *k3_last_error(void) { return g_err; }
+
+int k3_abi_version(void) { return 1; }
+
+size_t k3_mxfp4_packed_bytes(int rows, int cols) {
+  if (check_mat("k3_mxfp4_packed_bytes", rows, cols) != K3_OK) return 0;
+  return mat_layout(rows, cols).bytes();
+}
+
+k3_status k3_mxfp4_pack_host(const uint8_t *nib, const uint8_t *sc, int rows,
+                             int cols, uint8_t *tiles) {
+  const char *fn = "k3_mxfp4_pack_host";
+  if (!nib || !sc || !tiles) return fail(K3_ERR_ARG, "%s: NULL pointer", fn);
+  if (k3_status s = check_mat(fn, rows, cols)) return s;
+  pack_plain_host(nib, sc, rows, cols, tiles);
+  return K3_OK;
+}
+
+k3_status k3_mxfp4_unpack_host(const uint8_t *tiles, int rows, int cols,
+                               uint8_t *nib, uint8_t *sc) {
+  const char *fn = "k3_mxfp4_unpack_host";
+  if (!nib || !sc || !tiles) return fail(K3_ERR_ARG, "%s: NULL pointer", fn);
+  if (k3_status s = check_mat(fn, rows, cols)) return s;
+  unpack_plain_host(tiles, rows, cols, nib, sc);
+  return K3_OK;
+}
+
+k3_status k3_mxfp4_pack(const uint8_t *nib_d, const uint8_t *sc_d, int rows,
+                        int cols, uint8_t *tiles_d, k3_stream_t stream) {
+  const char *fn = "k3_mxfp4_pack";
+  K3_NEED_PTR(fn, nib_d);
+  if (!sc_d) return fail(K3_ERR_ARG, "%s: sc_d is NULL", fn);
+  K3_NEED_PTR(fn, tiles_d);
+  if (k3_status s = check_mat(fn, rows, cols)) return s;
+  K3_LAUNCH(fn, launch_pack(nib_d, sc_d, rows, cols, tiles_d, stream));
+  return K3_OK;
+}
+
+k3_status k3_mxfp4_unpack(const uint8_t *tiles_d, int rows, int cols,
+                          uint8_t *nib_d, uint8_t *sc_d, k3_stream_t stream) {
+  const char *fn = "k3_mxfp4_unpack";
+  K3_NEED_PTR(fn, tiles_d);
+  K3_NEED_PTR(fn, nib_d);
+  if (!sc_d) return fail(K3_ERR_ARG, "%s: sc_d is NULL", fn);
+  if (k3_status s = check_mat(fn, rows, cols)) return s;
+  K3_LAUNCH(fn, launch_unpack(tiles_d, rows, cols, nib_d, sc_d, stream));
+  return K3_OK;
+}
+
+size_t k3_expert_packed_bytes(int hidden, int inter) {
+  if (check_expert_dims("k3_expert_packed_bytes", hidden, inter) != K3_OK)
+    return 0;
+  return expert_layout(hidden, inter).bytes();
+}
+
+k3_status k3_expert_pack_host(const uint8_t *gate_nib, const uint8_t *gate_sc,
+                              const uint8_t *up_nib, const uint8_t *up_sc,
+                              const uint8_t *down_nib, const uint8_t *down_sc,
+                              int hidden, int inter, uint8_t *expert) {
+  const char *fn = "k3_expert_pack_host";
+  if (!gate_nib || !gate_sc || !up_nib || !up_sc || !down_nib || !down_sc ||
+      !expert)
+    return fail(K3_ERR_ARG, "%s: NULL pointer", fn);
+  if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
+  pack_expert_host(gate_nib, gate_sc, up_nib, up_sc, down_nib, down_sc, hidden,
+                   inter, expert);
+  return K3_OK;
+}
+
+k3_status k3_expert_pack(const uint8_t *gate_nib_d, const uint8_t *gate_sc_d,
+                         const uint8_t *up_nib_d, const uint8_t *up_sc_d,
+                         const uint8_t *down_nib_d, const uint8_t *down_sc_d,
+                         int hidden, int inter, uint8_t *expert_d,
+                         k3_stream_t stream) {
+  const char *fn = "k3_expert_pack";
+  K3_NEED_PTR(fn, gate_nib_d);
+  K3_NEED_PTR(fn, up_nib_d);
+  K3_NEED_PTR(fn, down_nib_d);
+  K3_NEED_PTR(fn, expert_d);
+  if (!gate_sc_d || !up_sc_d || !down_sc_d)
+    return fail(K3_ERR_ARG, "%s: a scale pointer is NULL", fn);
+  if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
+  K3_LAUNCH(fn, launch_expert_pack(gate_nib_d, gate_sc_d, up_nib_d, up_sc_d,
+                                   down_nib_d, down_sc_d, hidden, inter,
+                                   expert_d, stream));
+  return K3_OK;
+}
+
+k3_status k3_mxfp4_gemv(const float *x, const uint8_t *tiles, int rows,
+                        int cols, float *y, k3_stream_t stream) {
+  const char *fn = "k3_mxfp4_gemv";
+  K3_NEED_PTR(fn, x);
+  K3_NEED_PTR(fn, tiles);
+  K3_NEED_PTR(fn, y);
+  if (k3_status s = check_mat(fn, rows, cols)) return s;
+  K3_LAUNCH(fn, launch_gemv_f32(x, tiles, rows, cols, y, stream));
+  return K3_OK;
+}
+
+k3_status k3_expert_swiglu(const uint16_t *x, const uint8_t *expert,
+                           int hidden, int inter, float *y, float *h,
+                           k3_stream_t stream) {
+  const char *fn = "k3_expert_swiglu";
+  K3_NEED_PTR(fn, x);
+  K3_NEED_PTR(fn, expert);
+  K3_NEED_PTR(fn, y);
+  K3_NEED_PTR(fn, h);
+  if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
+  K3_LAUNCH(fn, launch_gate_up(x, nullptr, nullptr, expert, 1, hidden, inter,
+                               h, stream));
+  K3_LAUNCH(fn, launch_down(h, nullptr, nullptr, expert, 1, hidden, inter, y,
+                            stream));
+  return K3_OK;
+}
+
+k3_status k3_expert_gate_up(const uint16_t *x, const uint8_t *const *experts,
+                            const int32_t *idx, int k, int hidden, int inter,
+                            float *h, k3_stream_t stream) {
+  const char *fn = "k3_expert_gate_up";
+  K3_NEED_PTR(fn, x);
+  K3_NEED_PTR(fn, experts);
+  K3_NEED_PTR(fn, idx);
+  K3_NEED_PTR(fn, h);
+  K3_NEED(fn, k >= 1 && k <= K3_MAX_TOPK, "%s: k=%d outside [1, %d]", fn, k,
+          K3_MAX_TOPK);
+  if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
+  K3_LAUNCH(fn, launch_gate_up(x, experts, idx, nullptr, k, hidden, inter, h,
+                               stream));
+  return K3_OK;
+}
+
+k3_status k3_expert_down(const float *h, const uint8_t *const *experts,
+                         const int32_t *idx, int k, int hidden, int inter,
+                         float *yp, k3_stream_t stream) {
+  const char *fn = "k3_expert_down";
+  K3_NEED_PTR(fn, h);
+  K3_NEED_PTR(fn, experts);
+  K3_NEED_PTR(fn, idx);
+  K3_NEED_PTR(fn, yp);
+  K3_NEED(fn, k >= 1 && k <= K3_MAX_TOPK, "%s: k=%d outside [1, %d]", fn, k,
+          K3_MAX_TOPK);
+  if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
+  K3_LAUNCH(fn, launch_down(h, experts, idx, nullptr, k, hidden, inter, yp,
+                            stream));
+  return K3_OK;
+}
+
+k3_status k3_moe_combine(const float *yp, const float *w, int k, int hidden,
+                         uint16_t *y, float *y_f32, k3_stream_t stream) {
+  const char *fn = "k3_moe_combine";
+  K3_NEED_PTR(fn, yp);
+  K3_NEED_PTR(fn, w);
+  if (!y && !y_f32) return fail(K3_ERR_ARG, "%s: y and y_f32 are both NULL", fn);
+  if ((y && !aligned16(y)) || (y_f32 && !aligned16(y_f32)))
+    return fail(K3_ERR_ARG, "%s: an output is not 16-byte aligned", fn);
+  K3_NEED(fn, k >= 1 && k <= K3_MAX_TOPK, "%s: k=%d outside [1, %d]", fn, k,
+          K3_MAX_TOPK);
+  K3_NEED(fn, hidden >= 1 && hidden <= kMaxDim, "%s: hidden=%d outside [1, %d]",
+          fn, hidden, kMaxDim);
+  K3_LAUNCH(fn, launch_combine(yp, w, k, hidden, y, y_f32, stream));
+  return K3_OK;
+}
+
+k3_status k3_router(const uint16_t *x, const uint16_t *router_w, int T,
+                    int hidden, int n_experts, double *logits,
+                    k3_stream_t stream) {
+  const char *fn = "k3_router";
+  K3_NEED_PTR(fn, x);
+  K3_NEED_PTR(fn, router_w);
+  K3_NEED_PTR(fn, logits);
+  K3_NEED(fn, T >= 1 && T <= kMaxDim, "%s: T=%d outside [1, %d]", fn, T,
+          kMaxDim);
+  K3_NEED(fn, hidden >= 8 && hidden <= kMaxDim && hidden % 8 == 0,
+          "%s: hidden=%d must be a positive multiple of 8 (<= %d)", fn, hidden,
+          kMaxDim);
+  K3_NEED(fn, n_experts >= 1 && n_experts <= K3_MAX_EXPERTS,
+          "%s: n_experts=%d outside [1, %d]", fn, n_experts, K3_MAX_EXPERTS);
+  K3_LAUNCH(fn, launch_router(x, router_w, T, hidden, n_experts, logits,
+                              stream));
+  return K3_OK;
+}
+
+k3_status k3_router_topk(const double *logits, const float *bias, int T,
+                         int n_experts, int k, int32_t *idx, float *w,
+                         k3_stream_t stream) {
+  const char *fn = "k3_router_topk";
+  K3_NEED_PTR(fn, logits);
+  K3_NEED_PTR(fn, idx);
+  K3_NEED_PTR(fn, w);
+  if (bias && !aligned16(bias))
+    return fail(K3_ERR_ARG, "%s: bias is not 16-byte aligned", fn);
+  if (k3_status s = check_routing(fn, T, n_experts, k)) return s;
+  K3_LAUNCH(fn, launch_topk_f64(logits, bias, T, n_experts, k, idx, w, stream));
+  return K3_OK;
+}
+
+k3_status k3_router_topk_f32(const float *logits, const float *bias, int T,
+                             int n_experts, int k, int32_t *idx, float *w,
+                             k3_stream_t stream) {
+  const char *fn = "k3_router_topk_f32";
+  K3_NEED_PTR(fn, logits);
+  K3_NEED_PTR(fn, idx);
+  K3_NEED_PTR(fn, w);
+  if (bias && !aligned16(bias))
+    return fail(K3_ERR_ARG, "%s: bias is not 16-byte aligned", fn);
+  if (k3_status s = check_routing(fn, T, n_experts, k)) return s;
+  K3_LAUNCH(fn, launch_topk_f32(logits, bias, T, n_experts, k, idx, w, stream));
+  return K3_OK;
+}
+
+size_t k3_moe_workspace_bytes(int T, int n_experts, int hidden, int inter,
+                              int k) {
+  if (check_routing("k3_moe_workspace_bytes", T, n_experts, k) != K3_OK ||
+      check_expert_dims("k3_moe_workspace_bytes", hidden, inter) != K3_OK)
+    return 0;
+  return ws_layout(T, n_experts, hidden, inter, k).total;
+}
+
+k3_status k3_moe_layer_ex(const uint16_t *x, const uint16_t *router_w,
+                          const uint8_t *const *experts, int n_experts,
+                          int hidden, int inter, int k, uint16_t *y,
+                          float *y_f32, int32_t *idx, float *w,
+                          double *logits, void *ws, size_t ws_bytes,
+                          k3_stream_t stream) {
+  const char *fn = "k3_moe_layer";
+  K3_NEED_PTR(fn, x);
+  K3_NEED_PTR(fn, router_w);
+  K3_NEED_PTR(fn, experts);
+  K3_NEED_PTR(fn, y);
+  K3_NEED_PTR(fn, ws);
+  if ((y_f32 && !aligned16(y_f32)) || (idx && !aligned16(idx)) ||
+      (w && !aligned16(w)) || (logits && !aligned16(logits)))
+    return fail(K3_ERR_ARG, "%s: an optional output is not 16-byte aligned",
+                fn);
+  if (k3_status s = check_routing(fn, 1, n_experts, k)) return s;
+  if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
+  const WsLayout L = ws_layout(1, n_experts, hidden, inter, k);
+  if (ws_bytes < L.total)
+    return fail(K3_ERR_MEMORY,
+                "%s: workspace of %zu bytes is below the %zu bytes this call "
+                "needs; this is a memory limit, not an engine ceiling",
+                fn, ws_bytes, L.total);
+  uint8_t *base = static_cast<uint8_t *>(ws);
+  double *lg = logits ? logits : reinterpret_cast<double *>(base + L.logits);
+  int32_t *ix = idx ? idx : reinterpret_cast<int32_t *>(base + L.idx);
+  float *wt = w ? w : reinterpret_cast<float *>(base + L.w);
+  float *h = reinterpret_cast<float *>(base + L.h);
+  float *yp = reinterpret_cast<float *>(base + L.yp);
+  K3_LAUNCH(fn, launch_router(x, router_w, 1, hidden, n_experts, lg, stream));
+  K3_LAUNCH(fn, launch_topk_f64(lg, nullptr, 1, n_experts, k, ix, wt, stream));
+  K3_LAUNCH(fn, launch_gate_up(x, experts, ix, nullptr, k, hidden, inter, h,
+                               stream));
+  K3_LAUNCH(fn, launch_down(h, experts, ix, nullptr, k, hidden, inter, yp,
+                            stream));
+  K3_LAUNCH(fn, launch_combine(yp, wt, k, hidden, y, y_f32, stream));
+  return K3_OK;
+}
+
+k3_status k3_moe_layer(const uint16_t *x, const uint16_t *router_w,
+                       const uint8_t *const *experts, int n_experts,
+                       int hidden, int inter, int k, uint16_t *y, void *ws,
+                       size_t ws_bytes, k3_stream_t stream) {
+  return k3_moe_layer_ex(x, router_w, experts, n_experts, hidden, inter, k, y,
+                         nullptr, nullptr, nullptr, nullptr, ws, ws_bytes,
+                         stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,284 @@
+// Device-side MXFP4 decode and per-row dot products for gfx950.
+//
+// Decode uses gfx950's scaled FP4 conversions, which turn the two E2M1 codes
+// of one byte into two fp32 (or two bf16) values in a single instruction,
+// element 2b from the low nibble; the 16-entry table lives in the hardware
+// instead of in memory, so a group of 32 codes costs 16 conversions. The
+// group's dot product is accumulated in fp32 and its E8M0 exponent is applied
+// once, after the group ([SAT] "Reduction one"): acc += 2^(e-127) * sub, with
+// exponent byte 255 skipped by a select so that non-finite activations inside
+// such a group cannot reach the row ([A176] "What byte-identical actually
+// costs").
+//
+// Activations are wave-uniform (every lane owns a different row but all lanes
+// read the same x group), so the compiler keeps them in scalar registers and
+// each VALU operation takes x straight from an SGPR.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "k3_internal.h"
+
+namespace k3 {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// sum_{i<32} E2M1(code_i) * x_i for x bf16 (16 packed pairs at xg).
+__device__ __forceinline__ float group_dot_bf16(const u32x4 w,
+                                                const uint32_t *__restrict__ xg) {
+  float s = 0.f;
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const bf16x2 w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], 1.0f, 0);
+    const bf16x2 w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], 1.0f, 1);
+    const bf16x2 w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], 1.0f, 2);
+    const bf16x2 w3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], 1.0f, 3);
+    s = __builtin_amdgcn_fdot2_f32_bf16(w0, __builtin_bit_cast(bf16x2, xg[4 * d + 0]), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(w1, __builtin_bit_cast(bf16x2, xg[4 * d + 1]), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(w2, __builtin_bit_cast(bf16x2, xg[4 * d + 2]), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(w3, __builtin_bit_cast(bf16x2, xg[4 * d + 3]), s, false);
+  }
+  return s;
+}
+
+// sum_{i<32} E2M1(code_i) * x_i for x fp32 (32 values at xg).
+__device__ __forceinline__ float group_dot_f32(const u32x4 w,
+                                               const float *__restrict__ xg) {
+  float s = 0.f;
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], 1.0f, 0);
+    const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], 1.0f, 1);
+    const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], 1.0f, 2);
+    const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], 1.0f, 3);
+    s = fmaf(v0.x, xg[8 * d + 0], s);
+    s = fmaf(v0.y, xg[8 * d + 1], s);
+    s = fmaf(v1.x, xg[8 * d + 2], s);
+    s = fmaf(v1.y, xg[8 * d + 3], s);
+    s = fmaf(v2.x, xg[8 * d + 4], s);
+    s = fmaf(v2.y, xg[8 * d + 5], s);
+    s = fmaf(v3.x, xg[8 * d + 6], s);
+    s = fmaf(v3.y, xg[8 * d + 7], s);
+  }
+  return s;
+}
+
+// Same products with the activations in LDS (all lanes read the same
+// address: a broadcast). xs: 16 packed bf16 pairs; hs: 32 fp32 values.
+__device__ __forceinline__ float group_dot_bf16_lds(const u32x4 w,
+                                                    const uint32_t *xs) {
+  const u32x4 *xv = reinterpret_cast<const u32x4 *>(xs);
+  float s = 0.f;
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    // Elements go through a plain array: this compiler turns
+    // __builtin_bit_cast of an ext-vector element into a read of element 0.
+    const u32x4 xq = xv[d];
+    const uint32_t xw[4] = {xq.x, xq.y, xq.z, xq.w};
+    const bf16x2 w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], 1.0f, 0);
+    const bf16x2 w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], 1.0f, 1);
+    const bf16x2 w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], 1.0f, 2);
+    const bf16x2 w3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], 1.0f, 3);
+    s = __builtin_amdgcn_fdot2_f32_bf16(w0, __builtin_bit_cast(bf16x2, xw[0]), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(w1, __builtin_bit_cast(bf16x2, xw[1]), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(w2, __builtin_bit_cast(bf16x2, xw[2]), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(w3, __builtin_bit_cast(bf16x2, xw[3]), s, false);
+  }
+  return s;
+}
+
+__device__ __forceinline__ float group_dot_f32_lds(const u32x4 w,
+                                                   const float *hs) {
+  const u32x4 *hv = reinterpret_cast<const u32x4 *>(hs);
+  float s = 0.f;
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const u32x4 ha = hv[2 * d], hb = hv[2 * d + 1];
+    const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], 1.0f, 0);
+    const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], 1.0f, 1);
+    const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], 1.0f, 2);
+    const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], 1.0f, 3);
+    s = fmaf(v0.x, __uint_as_float(ha.x), s);
+    s = fmaf(v0.y, __uint_as_float(ha.y), s);
+    s = fmaf(v1.x, __uint_as_float(ha.z), s);
+    s = fmaf(v1.y, __uint_as_float(ha.w), s);
+    s = fmaf(v2.x, __uint_as_float(hb.x), s);
+    s = fmaf(v2.y, __uint_as_float(hb.y), s);
+    s = fmaf(v3.x, __uint_as_float(hb.z), s);
+    s = fmaf(v3.y, __uint_as_float(hb.w), s);
+  }
+  return s;
+}
+
+// acc += 2^(e-127) * sub, or nothing for e == 255 (select, not multiply).
+__device__ __forceinline__ float apply_scale(float acc, float sub, uint32_t e) {
+  const float t = acc + ldexpf(sub, (int)e - 127);
+  return e == 255u ? acc : t;
+}
+
+// Global-address-space views, so loads through pointers read from device
+// memory (e.g. an expert table) compile to global_load rather than flat_load.
+typedef __attribute__((address_space(1))) const u32x4 gu4_t;
+typedef __attribute__((address_space(1))) const uint32_t gu32_t;
+
+constexpr int kNW = 16;      // waves per workgroup of the streaming kernels
+constexpr int kMaxTPW = 8;   // tiles per pass of one workgroup
+#ifndef K3_PIPE_DEPTH
+#define K3_PIPE_DEPTH 2
+#endif
+constexpr int kDepth = K3_PIPE_DEPTH;  // quads in flight per wave
+
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+// Streams the tiles [t_begin, t_end) through one workgroup of kNW waves.
+// Weight bytes are read once per call, so they are loaded non-temporally
+// (measured on MI355X: a plain 16-byte-per-lane stream sustains about 6.1
+// TB/s, the same stream with non-temporal loads about 6.9 TB/s).
+//
+// Each tile's groups are cut into kNW contiguous quad slices; slice s of tile
+// t is read by wave (s - t) mod kNW, so the work of a workgroup's tiles is
+// spread evenly over its waves whatever the quad count, and every lane
+// streams its own row's bytes for the slices it owns. A wave walks all its
+// (tile, quad) items back to back through a ring of kDepth register buffers:
+// the loads of item i + kDepth are issued as soon as item i is consumed, so
+// kDepth quads (kDepth KiB x 4 per wave) stay in flight across tile
+// boundaries. In the steady rounds every load is unconditional, so the
+// compiler's wait counts stay exact; no quad is loaded twice. Each
+// slice's partial row sum goes to LDS; after a barrier the kNW partials of a
+// row are added in slice order 0..kNW-1, so the summation order of every
+// output is a function of the matrix shape only (bit-identical reruns on any
+// grid size).
+//
+//   base(t)      -> const uint8_t*   tile t's bytes (wave-uniform)
+//   dot(w, g, t) -> float            unscaled dot product of group g of t
+//   epi(t, lane, sum)                consumes the finished row sums
+template <class Base, class Dot, class Epi>
+__device__ __forceinline__ void run_tiles(int t_begin, int t_end, int G,
+                                          int G4, Base base, Dot dot,
+                                          Epi epi) {
+  __shared__ float part[kMaxTPW * kNW * 64];
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  for (int c0 = t_begin; c0 < t_end; c0 += kMaxTPW) {
+    const int ntl = min(kMaxTPW, t_end - c0);
+    auto slice_of = [&](int tl) { return (wave + c0 + tl) % kNW; };
+    auto slot = [&](int tl) { return (tl * kNW + slice_of(tl)) * 64 + lane; };
+    for (int tl = 0; tl < ntl; ++tl) part[slot(tl)] = 0.f;
+
+    // This wave's items (tile tl, quad q) in order, skipping empty slices.
+    int nitems = 0;
+    for (int tl = 0; tl < ntl; ++tl) {
+      const int s = slice_of(tl);
+      nitems += (s + 1) * G4 / kNW - s * G4 / kNW;
+    }
+    if (nitems > 0) {
+      int ctl = -1, cq = 0, cqe = 0;
+      const uint8_t *cbase = nullptr;
+      auto advance = [&]() {  // to the next item
+        if (++cq < cqe) return;
+        while (++ctl < ntl) {
+          const int s = slice_of(ctl);
+          cq = s * G4 / kNW;
+          cqe = (s + 1) * G4 / kNW;
+          if (cq < cqe) break;
+        }
+        cbase = base(c0 + ctl);
+      };
+      u32x4 w[kDepth][4];
+      uint32_t sc[kDepth];
+      int stl[kDepth], sq[kDepth];
+      auto load = [&](int d) {
+        advance();
+        stl[d] = ctl;
+        sq[d] = cq;
+        const uint8_t *qb = cbase + (size_t)kQuadBytes * cq;
+        gu4_t *nib = (gu4_t *)(qb) + lane;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          w[d][b] = __builtin_nontemporal_load(nib + (size_t)b * 64);
+        sc[d] = __builtin_nontemporal_load((gu32_t *)(qb + 4096) + lane);
+      };
+      float acc = 0.f;
+      int cur = -1;
+      auto consume = [&](int d) {
+        const int tl = stl[d], q = sq[d];
+        if (tl != cur) {
+          if (cur >= 0) part[slot(cur)] = acc;
+          acc = 0.f;
+          cur = tl;
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int g = min(4 * q + b, G - 1);
+          acc = apply_scale(acc, dot(w[d][b], g, c0 + tl), (sc[d] >> (8 * b)) & 255u);
+          // one group's activations live in scalar registers at a time
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      if (nitems >= kDepth) {
+        // Steady rounds: every load is unconditional, so the waits before
+        // each consume count exactly the kDepth-1 quads still in flight.
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) load(d);
+        int rem = nitems - kDepth;  // items not yet loaded
+        for (; rem >= kDepth; rem -= kDepth) {
+#pragma unroll
+          for (int d = 0; d < kDepth; ++d) {
+            consume(d);
+            load(d);
+          }
+        }
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+          consume(d);
+          if (d < rem) load(d);
+        }
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d)
+          if (d < rem) consume(d);
+      } else {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d)
+          if (d < nitems) load(d);
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d)
+          if (d < nitems) consume(d);
+      }
+      part[slot(cur)] = acc;
+    }
+    __syncthreads();
+    for (int tl = wave; tl < ntl; tl += kNW) {
+      float sum = 0.f;
+#pragma unroll
+      for (int s = 0; s < kNW; ++s) sum += part[(tl * kNW + s) * 64 + lane];
+      epi(c0 + tl, lane, sum);
+    }
+    __syncthreads();
+  }
+}
+
+// Contiguous tile range of workgroup b out of `grid` for `total` tiles.
+__device__ __forceinline__ void wg_range(int total, int *t0, int *t1) {
+  const long long b = blockIdx.x, n = gridDim.x;
+  *t0 = (int)(b * total / n);
+  *t1 = (int)((b + 1) * total / n);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu))
+    return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+}  // namespace k3

@@ -1,0 +1,118 @@
+// Internal declarations of the k3moe library (gfx950 / HIP).
+//
+// Tile layout of an MXFP4 matrix (the layout the kernels read; see
+// include/k3moe.h for the byte-level definition): 64-row tiles, each tile a
+// sequence of G4 quad blocks of 4352 bytes: [4 groups][64 lanes][16 B] of
+// packed codes (groups past G are zero padding) then [64 lanes][4 B] of the
+// quad's exponent bytes. One lane owns one row; a wave's load of group g is
+// one contiguous KiB, a wave walks one contiguous stream, and every quad of
+// groups is whole, so the kernels' inner loop has no per-group bounds.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "k3moe.h"
+
+namespace k3 {
+
+constexpr int kTileRows = 64;   // rows per tile = lanes per wave
+constexpr int kGroup = 32;      // weights per exponent byte
+constexpr int kGroupBytes = 16; // packed bytes per group
+constexpr int kQuadBytes = 4352;  // 4 groups x 64 lanes x 16 B + 64 x 4 B
+
+// Byte offsets inside a tile: codes of group g for lane l, and the exponent
+// byte of group g for lane l.
+__host__ __device__ inline size_t code_offset(int g, int lane) {
+  return (size_t)kQuadBytes * (g >> 2) + (size_t)1024 * (g & 3) + 16 * lane;
+}
+__host__ __device__ inline size_t scale_offset(int g, int lane) {
+  return (size_t)kQuadBytes * (g >> 2) + 4096 + 4 * lane + (g & 3);
+}
+
+struct MatLayout {
+  int rows, cols, G, G4, ntiles;
+  size_t tile_bytes;  // G4 quad blocks of 4096 code + 256 exponent bytes
+  __host__ __device__ size_t bytes() const { return (size_t)ntiles * tile_bytes; }
+};
+
+__host__ __device__ inline MatLayout mat_layout(int rows, int cols) {
+  MatLayout m;
+  m.rows = rows;
+  m.cols = cols;
+  m.G = cols / kGroup;
+  m.G4 = (m.G + 3) / 4;
+  m.ntiles = (rows + kTileRows - 1) / kTileRows;
+  m.tile_bytes = (size_t)kQuadBytes * m.G4;
+  return m;
+}
+
+// Expert blob: gate/up region (2*inter virtual rows, 32 gate + 32 up rows per
+// tile) followed by the down region (hidden x inter).
+struct ExpertLayout {
+  MatLayout gu;    // virtual: rows = 64 * ntiles_gu, cols = hidden
+  MatLayout down;  // rows = hidden, cols = inter
+  int inter, hidden;
+  size_t down_offset;
+  __host__ __device__ size_t bytes() const { return down_offset + down.bytes(); }
+};
+
+__host__ __device__ inline ExpertLayout expert_layout(int hidden, int inter) {
+  ExpertLayout e;
+  e.hidden = hidden;
+  e.inter = inter;
+  const int ntiles = (inter + 31) / 32;
+  e.gu = mat_layout(ntiles * kTileRows, hidden);
+  e.down = mat_layout(hidden, inter);
+  e.down_offset = e.gu.bytes();
+  return e;
+}
+
+// Which canonical (matrix, row) a gate/up tile lane holds: lanes 0..31 the
+// gate rows 32t.., lanes 32..63 the up rows 32t...
+__host__ __device__ inline void gu_lane_row(int t, int lane, int *is_up,
+                                            int *row) {
+  *is_up = lane >> 5;
+  *row = 32 * t + (lane & 31);
+}
+
+// ---- host-side helpers (k3_abi.hip) ----
+// Compute units of the current device (cached per device).
+int num_cus();
+void set_error(const char *fmt, ...);
+k3_status device_status(hipError_t e, const char *what);
+
+// ---- launchers (each returns hipSuccess or the launch error) ----
+hipError_t launch_pack(const uint8_t *nib, const uint8_t *sc, int rows,
+                       int cols, uint8_t *tiles, hipStream_t s);
+hipError_t launch_unpack(const uint8_t *tiles, int rows, int cols,
+                         uint8_t *nib, uint8_t *sc, hipStream_t s);
+hipError_t launch_expert_pack(const uint8_t *gn, const uint8_t *gs,
+                              const uint8_t *un, const uint8_t *us,
+                              const uint8_t *dn, const uint8_t *ds, int hidden,
+                              int inter, uint8_t *dst, hipStream_t s);
+hipError_t launch_gemv_f32(const float *x, const uint8_t *tiles, int rows,
+                           int cols, float *y, hipStream_t s);
+// Gate/up + SwiGLU over `nslots` experts: slot j uses expert experts[idx[j]]
+// (or `single` when experts == nullptr); h[j][inter].
+hipError_t launch_gate_up(const uint16_t *x, const uint8_t *const *experts,
+                          const int32_t *idx, const uint8_t *single,
+                          int nslots, int hidden, int inter, float *h,
+                          hipStream_t s);
+// Down projection: yp[j][hidden] = W_down(e_j) h[j].
+hipError_t launch_down(const float *h, const uint8_t *const *experts,
+                       const int32_t *idx, const uint8_t *single, int nslots,
+                       int hidden, int inter, float *yp, hipStream_t s);
+hipError_t launch_combine(const float *yp, const float *w, int k, int hidden,
+                          uint16_t *y, float *y_f32, hipStream_t s);
+hipError_t launch_router(const uint16_t *x, const uint16_t *R, int T,
+                         int hidden, int n, double *logits, hipStream_t s);
+hipError_t launch_topk_f64(const double *logits, const float *bias, int T,
+                           int n, int k, int32_t *idx, float *w,
+                           hipStream_t s);
+hipError_t launch_topk_f32(const float *logits, const float *bias, int T,
+                           int n, int k, int32_t *idx, float *w,
+                           hipStream_t s);
+
+}  // namespace k3
