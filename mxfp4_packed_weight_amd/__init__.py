@@ -35,9 +35,11 @@ SIGNATURES = [
     ("k3_expert_packed_bytes", _sz, [_i, _i]),
     ("k3_expert_pack_host", _i, [_vp] * 6 + [_i, _i, _vp]),
     ("k3_expert_pack", _i, [_vp] * 6 + [_i, _i, _vp, _vp]),
-    ("k3_mxfp4_gemv", _i, [_vp, _vp, _i, _i, _vp, _vp]),
-    ("k3_expert_swiglu", _i, [_vp, _vp, _i, _i, _vp, _vp, _vp]),
-    ("k3_expert_gate_up", _i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
+    ("k3_mxfp4_gemv_workspace_bytes", _sz, [_i]),
+    ("k3_mxfp4_gemv", _i, [_vp, _vp, _i, _i, _vp, _vp, _sz, _vp]),
+    ("k3_expert_workspace_bytes", _sz, [_i, _i]),
+    ("k3_expert_swiglu", _i, [_vp, _vp, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    ("k3_expert_gate_up", _i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _sz, _vp]),
     ("k3_expert_down", _i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
     ("k3_moe_combine", _i, [_vp, _vp, _i, _i, _vp, _vp, _vp]),
     ("k3_router", _i, [_vp, _vp, _i, _i, _i, _vp, _vp]),
@@ -159,18 +161,31 @@ def k3_expert_pack(gate_nib, gate_sc, up_nib, up_sc, down_nib, down_sc, hidden, 
 
 # ---- compute --------------------------------------------------------------
 
-def k3_mxfp4_gemv(x, tiles, rows, cols, y, stream=None):
-    _call("k3_mxfp4_gemv", _dp(x), _dp(tiles), rows, cols, _dp(y), _stream(stream))
+def _nbytes(t):
+    return t.numel() * t.element_size()
 
 
-def k3_expert_swiglu(x, expert, hidden, inter, y, h, stream=None):
-    _call("k3_expert_swiglu", _dp(x), _dp(expert), hidden, inter, _dp(y), _dp(h),
+def k3_mxfp4_gemv_workspace_bytes(cols):
+    return lib().k3_mxfp4_gemv_workspace_bytes(cols)
+
+
+def k3_expert_workspace_bytes(hidden, inter):
+    return lib().k3_expert_workspace_bytes(hidden, inter)
+
+
+def k3_mxfp4_gemv(x, tiles, rows, cols, y, ws, stream=None):
+    _call("k3_mxfp4_gemv", _dp(x), _dp(tiles), rows, cols, _dp(y), _dp(ws), _nbytes(ws),
           _stream(stream))
 
 
-def k3_expert_gate_up(x, experts, idx, k, hidden, inter, h, stream=None):
+def k3_expert_swiglu(x, expert, hidden, inter, y, h, ws, stream=None):
+    _call("k3_expert_swiglu", _dp(x), _dp(expert), hidden, inter, _dp(y), _dp(h), _dp(ws),
+          _nbytes(ws), _stream(stream))
+
+
+def k3_expert_gate_up(x, experts, idx, k, hidden, inter, h, ws, stream=None):
     _call("k3_expert_gate_up", _dp(x), _dp(experts), _dp(idx), k, hidden, inter, _dp(h),
-          _stream(stream))
+          _dp(ws), _nbytes(ws), _stream(stream))
 
 
 def k3_expert_down(h, experts, idx, k, hidden, inter, yp, stream=None):

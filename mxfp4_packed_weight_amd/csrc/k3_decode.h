@@ -130,140 +130,9 @@ typedef __attribute__((address_space(1))) const uint32_t gu32_t;
 
 constexpr int kNW = 16;      // waves per workgroup of the streaming kernels
 constexpr int kMaxTPW = 8;   // tiles per pass of one workgroup
-#ifndef K3_PIPE_DEPTH
-#define K3_PIPE_DEPTH 2
-#endif
-constexpr int kDepth = K3_PIPE_DEPTH;  // quads in flight per wave
 
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-}
-
-// Streams the tiles [t_begin, t_end) through one workgroup of kNW waves.
-// Weight bytes are read once per call, so they are loaded non-temporally
-// (measured on MI355X: a plain 16-byte-per-lane stream sustains about 6.1
-// TB/s, the same stream with non-temporal loads about 6.9 TB/s).
-//
-// Each tile's groups are cut into kNW contiguous quad slices; slice s of tile
-// t is read by wave (s - t) mod kNW, so the work of a workgroup's tiles is
-// spread evenly over its waves whatever the quad count, and every lane
-// streams its own row's bytes for the slices it owns. A wave walks all its
-// (tile, quad) items back to back through a ring of kDepth register buffers:
-// the loads of item i + kDepth are issued as soon as item i is consumed, so
-// kDepth quads (kDepth KiB x 4 per wave) stay in flight across tile
-// boundaries. In the steady rounds every load is unconditional, so the
-// compiler's wait counts stay exact; no quad is loaded twice. Each
-// slice's partial row sum goes to LDS; after a barrier the kNW partials of a
-// row are added in slice order 0..kNW-1, so the summation order of every
-// output is a function of the matrix shape only (bit-identical reruns on any
-// grid size).
-//
-//   base(t)      -> const uint8_t*   tile t's bytes (wave-uniform)
-//   dot(w, g, t) -> float            unscaled dot product of group g of t
-//   epi(t, lane, sum)                consumes the finished row sums
-template <class Base, class Dot, class Epi>
-__device__ __forceinline__ void run_tiles(int t_begin, int t_end, int G,
-                                          int G4, Base base, Dot dot,
-                                          Epi epi) {
-  __shared__ float part[kMaxTPW * kNW * 64];
-  const int lane = threadIdx.x & 63;
-  const int wave = wave_id();
-  for (int c0 = t_begin; c0 < t_end; c0 += kMaxTPW) {
-    const int ntl = min(kMaxTPW, t_end - c0);
-    auto slice_of = [&](int tl) { return (wave + c0 + tl) % kNW; };
-    auto slot = [&](int tl) { return (tl * kNW + slice_of(tl)) * 64 + lane; };
-    for (int tl = 0; tl < ntl; ++tl) part[slot(tl)] = 0.f;
-
-    // This wave's items (tile tl, quad q) in order, skipping empty slices.
-    int nitems = 0;
-    for (int tl = 0; tl < ntl; ++tl) {
-      const int s = slice_of(tl);
-      nitems += (s + 1) * G4 / kNW - s * G4 / kNW;
-    }
-    if (nitems > 0) {
-      int ctl = -1, cq = 0, cqe = 0;
-      const uint8_t *cbase = nullptr;
-      auto advance = [&]() {  // to the next item
-        if (++cq < cqe) return;
-        while (++ctl < ntl) {
-          const int s = slice_of(ctl);
-          cq = s * G4 / kNW;
-          cqe = (s + 1) * G4 / kNW;
-          if (cq < cqe) break;
-        }
-        cbase = base(c0 + ctl);
-      };
-      u32x4 w[kDepth][4];
-      uint32_t sc[kDepth];
-      int stl[kDepth], sq[kDepth];
-      auto load = [&](int d) {
-        advance();
-        stl[d] = ctl;
-        sq[d] = cq;
-        const uint8_t *qb = cbase + (size_t)kQuadBytes * cq;
-        gu4_t *nib = (gu4_t *)(qb) + lane;
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-          w[d][b] = __builtin_nontemporal_load(nib + (size_t)b * 64);
-        sc[d] = __builtin_nontemporal_load((gu32_t *)(qb + 4096) + lane);
-      };
-      float acc = 0.f;
-      int cur = -1;
-      auto consume = [&](int d) {
-        const int tl = stl[d], q = sq[d];
-        if (tl != cur) {
-          if (cur >= 0) part[slot(cur)] = acc;
-          acc = 0.f;
-          cur = tl;
-        }
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int g = min(4 * q + b, G - 1);
-          acc = apply_scale(acc, dot(w[d][b], g, c0 + tl), (sc[d] >> (8 * b)) & 255u);
-          // one group's activations live in scalar registers at a time
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      };
-      if (nitems >= kDepth) {
-        // Steady rounds: every load is unconditional, so the waits before
-        // each consume count exactly the kDepth-1 quads still in flight.
-#pragma unroll
-        for (int d = 0; d < kDepth; ++d) load(d);
-        int rem = nitems - kDepth;  // items not yet loaded
-        for (; rem >= kDepth; rem -= kDepth) {
-#pragma unroll
-          for (int d = 0; d < kDepth; ++d) {
-            consume(d);
-            load(d);
-          }
-        }
-#pragma unroll
-        for (int d = 0; d < kDepth; ++d) {
-          consume(d);
-          if (d < rem) load(d);
-        }
-#pragma unroll
-        for (int d = 0; d < kDepth; ++d)
-          if (d < rem) consume(d);
-      } else {
-#pragma unroll
-        for (int d = 0; d < kDepth; ++d)
-          if (d < nitems) load(d);
-#pragma unroll
-        for (int d = 0; d < kDepth; ++d)
-          if (d < nitems) consume(d);
-      }
-      part[slot(cur)] = acc;
-    }
-    __syncthreads();
-    for (int tl = wave; tl < ntl; tl += kNW) {
-      float sum = 0.f;
-#pragma unroll
-      for (int s = 0; s < kNW; ++s) sum += part[(tl * kNW + s) * 64 + lane];
-      epi(c0 + tl, lane, sum);
-    }
-    __syncthreads();
-  }
 }
 
 // Contiguous tile range of workgroup b out of `grid` for `total` tiles.

@@ -61,7 +61,7 @@ __host__ __device__ inline void pack_scale4(const Src &src, const MatLayout &m,
   for (int b = 0; b < 4; ++b) {
     const int g = 4 * q + b;
     tiles[(size_t)t * m.tile_bytes + scale_offset(g, lane)] =
-        (ok && g < m.G) ? s[(size_t)r * m.G + g] : (uint8_t)255;
+        (ok && g < m.G) ? s[(size_t)r * m.G + g] : (uint8_t)0;
   }
 }
 

@@ -29,9 +29,10 @@ def gpu_gemv(nib, sc, x):
     tiles = up(K.k3_mxfp4_pack_host(nib, sc))
     xd = up(np.asarray(x, np.float32))
     y = empty(rows, torch.float32)
-    K.k3_mxfp4_gemv(xd, tiles, rows, cols, y)
+    ws = empty(K.k3_mxfp4_gemv_workspace_bytes(cols), torch.uint8)
+    K.k3_mxfp4_gemv(xd, tiles, rows, cols, y, ws)
     y1 = y.cpu().numpy().copy()
-    K.k3_mxfp4_gemv(xd, tiles, rows, cols, y)
+    K.k3_mxfp4_gemv(xd, tiles, rows, cols, y, ws)
     y2 = y.cpu().numpy()
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), "rerun not bit-identical"
     return y1
@@ -99,6 +100,22 @@ def test_gemv_shapes_and_exponent_range(rows, cols, elo, ehi):
     assert normwise(y, ref) <= TOL
 
 
+def test_gemv_nan_scale_finite_x():
+    """Exponent 255 with finite activations (the matrix-unit path)."""
+    say("gemv exponent 255, finite activations")
+    rows, cols = 130, 384
+    nib, sc = gen.mxfp4_matrix(8, 66, rows, cols)
+    sc = sc.copy()
+    sc[:, 3] = 255
+    sc[7, :] = 255
+    sc[64:70, 9] = 255
+    x = gen.normal_f32(gen.key(8, 66, gen.KIND_TOKENS), cols)
+    y = gpu_gemv(nib, sc, x)
+    assert y[7] == 0.0
+    ref = oracle.gemv(nib, sc, x.astype(np.float64))
+    assert normwise(y, ref) <= TOL
+
+
 def test_gemv_nan_scale_contains_nonfinite_x():
     say("gemv exponent 255 with NaN/Inf activations")
     rows, cols = 70, 256
@@ -121,9 +138,10 @@ def _expert_on_gpu(E, x_bf16, hidden, inter):
     xd = up(x_bf16)
     y = empty(hidden, torch.float32)
     h = empty(inter, torch.float32)
-    K.k3_expert_swiglu(xd, blob, hidden, inter, y, h)
+    ws = empty(K.k3_expert_workspace_bytes(hidden, inter), torch.uint8)
+    K.k3_expert_swiglu(xd, blob, hidden, inter, y, h, ws)
     y1, h1 = y.cpu().numpy().copy(), h.cpu().numpy().copy()
-    K.k3_expert_swiglu(xd, blob, hidden, inter, y, h)
+    K.k3_expert_swiglu(xd, blob, hidden, inter, y, h, ws)
     assert np.array_equal(y1.view(np.uint32), y.cpu().numpy().view(np.uint32))
     return y1, h1
 
@@ -140,6 +158,23 @@ def test_expert_c2_parity(elo, ehi):
     eh, ey = normwise(h, h_ref), normwise(y, y_ref)
     say(f"expert C2 normwise err h {eh:.3e} y {ey:.3e}")
     assert eh <= TOL and ey <= TOL
+
+
+def test_expert_nonfinite_x_takes_exact_path():
+    """An Inf in x must give the oracle's result: rows reach Inf/NaN exactly
+    where a finite-exponent group meets it."""
+    hidden, inter = 128, 64
+    say("expert with an Inf activation")
+    E = gen.expert(9, 67, 0, hidden, inter, 114, 120)
+    x = gen.normal_bf16(gen.key(9, 67, gen.KIND_TOKENS), hidden)
+    E["gate"][1][:, 1] = 255  # gate group 1 (elements 32..63) skipped
+    E["up"][1][:, 1] = 255
+    x = x.copy()
+    x[40] = 0x7F80  # +Inf in group 1
+    y, h = _expert_on_gpu(E, x, hidden, inter)
+    y_ref, h_ref = oracle.expert_swiglu(E, I.bf16_to_float_bits(x))
+    assert np.all(np.isfinite(h)) and np.all(np.isfinite(h_ref))
+    assert normwise(h, h_ref) <= TOL and normwise(y, y_ref) <= TOL
 
 
 def test_expert_small_ragged():

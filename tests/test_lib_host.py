@@ -60,11 +60,13 @@ def test_pack_roundtrip_and_layout(L, rows, cols):
     G, G4 = cols // 32, (cols // 32 + 3) // 4
     tb = 4352 * G4
 
-    def code_off(t, g, l):
-        return t * tb + 4352 * (g // 4) + 1024 * (g % 4) + 16 * l
+    def code_off(t, g, r):  # r: row inside the tile
+        lane = r % 16 + 16 * (g % 4)
+        return t * tb + 4352 * (g // 4) + 1024 * (r // 16) + 16 * lane
 
-    def scale_off(t, g, l):
-        return t * tb + 4352 * (g // 4) + 4096 + 4 * l + g % 4
+    def scale_off(t, g, r):
+        lane = r % 16 + 16 * (g % 4)
+        return t * tb + 4352 * (g // 4) + 4096 + 4 * lane + r // 16
 
     rng = np.random.default_rng(0)
     for _ in range(50):
@@ -73,14 +75,14 @@ def test_pack_roundtrip_and_layout(L, rows, cols):
         off = code_off(t, g, l)
         assert np.array_equal(tiles[off:off + 16], nib[r, 16 * g:16 * g + 16])
         assert tiles[scale_off(t, g, l)] == sc[r, g]
-    # padding: groups past G are zero codes with exponent 255, rows past `rows` too
+    # padding: groups past G are zero codes with exponent 0, rows past `rows` too
     t_last = (rows - 1) // 64
     for l in range(64):
         r = t_last * 64 + l
         for g in range(4 * G4):
             if r >= rows or g >= G:
                 off = code_off(t_last, g, l)
-                assert tiles[scale_off(t_last, g, l)] == 255
+                assert tiles[scale_off(t_last, g, l)] == 0
                 assert not np.any(tiles[off:off + 16])
 
 
@@ -112,20 +114,28 @@ def _fake(n):
 
 def test_refusals_before_launch(L):
     s = None
-    rc = L.k3_mxfp4_gemv(None, _fake(1), 64, 64, _fake(2), s)
+    big = 1 << 30
+    rc = L.k3_mxfp4_gemv(None, _fake(1), 64, 64, _fake(2), _fake(4), big, s)
     assert rc == K.K3_ERR_ARG and "x is NULL" in K.last_error()
-    rc = L.k3_mxfp4_gemv(ctypes.c_void_p(0x10004), _fake(1), 64, 64, _fake(2), s)
+    rc = L.k3_mxfp4_gemv(ctypes.c_void_p(0x10004), _fake(1), 64, 64, _fake(2), _fake(4), big, s)
     assert rc == K.K3_ERR_ARG and "aligned" in K.last_error()
-    rc = L.k3_mxfp4_gemv(_fake(3), _fake(1), 64, 48, _fake(2), s)
+    rc = L.k3_mxfp4_gemv(_fake(3), _fake(1), 64, 48, _fake(2), _fake(4), big, s)
     assert rc == K.K3_ERR_CONFIG and "cols=48" in K.last_error()
-    rc = L.k3_mxfp4_gemv(_fake(3), _fake(1), 0, 64, _fake(2), s)
+    rc = L.k3_mxfp4_gemv(_fake(3), _fake(1), 0, 64, _fake(2), _fake(4), big, s)
     assert rc == K.K3_ERR_CONFIG
+    rc = L.k3_mxfp4_gemv(_fake(3), _fake(1), 64, 64, _fake(2), _fake(4),
+                         K.k3_mxfp4_gemv_workspace_bytes(64) - 1, s)
+    assert rc == K.K3_ERR_MEMORY
     rc = L.k3_router_topk(_fake(1), None, 1, 896, 17 + 64, _fake(2), _fake(3), s)
     assert rc == K.K3_ERR_CONFIG and "k=81" in K.last_error()
     rc = L.k3_router_topk(_fake(1), None, 1, 8, 9, _fake(2), _fake(3), s)
     assert rc == K.K3_ERR_CONFIG
-    rc = L.k3_expert_swiglu(_fake(1), _fake(2), 7168, 1500, _fake(3), _fake(4), s)
+    rc = L.k3_expert_swiglu(_fake(1), _fake(2), 7168, 1500, _fake(3), _fake(4), _fake(5),
+                            big, s)
     assert rc == K.K3_ERR_CONFIG and "inter=1500" in K.last_error()
+    rc = L.k3_expert_swiglu(_fake(1), _fake(2), 7168, 8192, _fake(3), _fake(4), _fake(5),
+                            big, s)
+    assert rc == K.K3_ERR_CONFIG  # inter above K3_MAX_INTER
     need = K.k3_moe_workspace_bytes(1, 896, 7168, 1536, 16)
     assert need > 0
     rc = L.k3_moe_layer(_fake(1), _fake(2), _fake(3), 896, 7168, 1536, 16, _fake(4), _fake(5),
