@@ -128,14 +128,13 @@ def main():
     K.k3_router(bank, R, T, hidden, n, lg)
     K.k3_router_topk(lg, None, T, n, k, idx, w)
     h = torch.empty((k, inter), dtype=torch.float32, device=dev)
-    ews = torch.empty(K.k3_expert_workspace_bytes(hidden, inter), dtype=torch.uint8, device=dev)
     reps = max(args.steps, 50)
     for i in range(10):
-        K.k3_expert_gate_up(bank[i % T], pool.table, idx[i % T], k, hidden, inter, h, ews)
+        K.k3_expert_gate_up(bank[i % T], pool.table, idx[i % T], k, hidden, inter, h)
     torch.cuda.synchronize()
     ev0.record(stream)
     for i in range(reps):
-        K.k3_expert_gate_up(bank[i % T], pool.table, idx[i % T], k, hidden, inter, h, ews)
+        K.k3_expert_gate_up(bank[i % T], pool.table, idx[i % T], k, hidden, inter, h)
     ev1.record(stream)
     torch.cuda.synchronize()
     gu_us = ev0.elapsed_time(ev1) / reps * 1e3

@@ -124,32 +124,30 @@ k3_status k3_expert_pack(const uint8_t *gate_nib_d, const uint8_t *gate_sc_d,
 
 /* ------------------------------------------------------------------------
  * y[rows] = W[rows][cols] . x[cols] read straight from the packed bytes,
- * never expanded to floats ([SAT] "Reduction one"). Each 32-group is summed
- * and then scaled once by its exponent; exponent 255 contributes nothing.
- * fp32 accumulation in a fixed order: each row is reduced by one workgroup
- * along a fixed tree, so results are bit-identical from run to run (the
- * pages' fixed-order rule, [SAT] "A floating-point contract, not a
- * convention"). x fp32 [cols], tiles from k3_mxfp4_pack, y fp32 [rows],
- * ws of k3_mxfp4_gemv_workspace_bytes(cols) bytes (the activation's split
- * into matrix-unit operands). The product runs on the gfx950 block-scaled
- * FP4 matrix instruction straight from the packed bytes; x is split into five
- * fixed-point E4M3 pieces (per-32 exponents, residual below 2^-24 of each
- * 32-block's largest |x|) as its other operand. Calls whose x holds Inf or
- * NaN take a vector-ALU path that multiplies group by group.
+ * never expanded to floats ([SAT] "Reduction one"). The product runs on the
+ * gfx950 block-scaled FP4 matrix instruction: the packed tiles are its FP4
+ * operand with the group exponents as its scales, and x is split into five
+ * fixed-point E4M3 pieces (per-32 exponents; residual below 2^-24 of each
+ * 32-block's largest |x|) as its other operand, built in LDS by every
+ * workgroup. Exponent 255 contributes nothing. fp32 accumulation in a fixed
+ * order: each row is reduced by one workgroup along a fixed tree, so results
+ * are bit-identical from run to run on one device (the pages' fixed-order
+ * rule, [SAT] "A floating-point contract, not a convention"). Calls whose x
+ * holds Inf or NaN take a vector-ALU path that multiplies group by group.
+ * x fp32 [cols], tiles from k3_mxfp4_pack, y fp32 [rows]; cols <=
+ * K3_MAX_COLS (the fragments of x must fit in LDS). No workspace.
  * ---------------------------------------------------------------------- */
-size_t k3_mxfp4_gemv_workspace_bytes(int cols);
+#define K3_MAX_COLS 16384
 k3_status k3_mxfp4_gemv(const float *x, const uint8_t *tiles, int rows,
-                        int cols, float *y, void *ws, size_t ws_bytes,
-                        k3_stream_t stream);
+                        int cols, float *y, k3_stream_t stream);
 
 /* One routed expert, SwiGLU: g = W_gate x, u = W_up x, h = SiLU(g) * u
  * (fp32, not rounded to bf16), y = W_down h. x bf16 [hidden]; expert from
- * k3_expert_pack; y fp32 [hidden]; h fp32 [inter] receives h; ws of
- * k3_expert_workspace_bytes(hidden, inter) bytes. */
-size_t k3_expert_workspace_bytes(int hidden, int inter);
+ * k3_expert_pack; y fp32 [hidden]; h fp32 [inter] receives h. Same product
+ * as k3_mxfp4_gemv (x and h split into pieces in LDS). */
 k3_status k3_expert_swiglu(const uint16_t *x, const uint8_t *expert,
-                           int hidden, int inter, float *y, float *h, void *ws,
-                           size_t ws_bytes, k3_stream_t stream);
+                           int hidden, int inter, float *y, float *h,
+                           k3_stream_t stream);
 
 /* The two stages of k3_expert_swiglu over k routing slots of one token, and
  * the weighted combine, as separate calls (k3_moe_layer runs exactly these):
@@ -158,12 +156,10 @@ k3_status k3_expert_swiglu(const uint16_t *x, const uint8_t *expert,
  *   k3_moe_combine:     y[i] = sum_{j<k} w[j] * yp[j][i] in rank order (fp32),
  *                       y_f32 (optional) the fp32 value, y bf16 (RNE).
  * with e_j = idx[j] (device int32 [k], each in [0, n_experts)) and experts the
- * device pointer table of k3_moe_layer. 1 <= k <= K3_MAX_TOPK. The gate/up
- * call takes a ws of k3_expert_workspace_bytes(hidden, inter) bytes. */
+ * device pointer table of k3_moe_layer. 1 <= k <= K3_MAX_TOPK. */
 k3_status k3_expert_gate_up(const uint16_t *x, const uint8_t *const *experts,
                             const int32_t *idx, int k, int hidden, int inter,
-                            float *h, void *ws, size_t ws_bytes,
-                            k3_stream_t stream);
+                            float *h, k3_stream_t stream);
 k3_status k3_expert_down(const float *h, const uint8_t *const *experts,
                          const int32_t *idx, int k, int hidden, int inter,
                          float *yp, k3_stream_t stream);

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libk3moe.so")
 _lib = None
 
 K3_OK, K3_ERR_ARG, K3_ERR_CONFIG, K3_ERR_MEMORY, K3_ERR_DEVICE = 0, 1, 2, 3, 4
-K3_MAX_EXPERTS, K3_MAX_TOPK = 4096, 64
+K3_MAX_EXPERTS, K3_MAX_TOPK, K3_MAX_COLS = 4096, 64, 16384
 
 # (name, restype, argtypes) of every exported symbol in include/k3moe.h
 _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -35,11 +35,9 @@ SIGNATURES = [
     ("k3_expert_packed_bytes", _sz, [_i, _i]),
     ("k3_expert_pack_host", _i, [_vp] * 6 + [_i, _i, _vp]),
     ("k3_expert_pack", _i, [_vp] * 6 + [_i, _i, _vp, _vp]),
-    ("k3_mxfp4_gemv_workspace_bytes", _sz, [_i]),
-    ("k3_mxfp4_gemv", _i, [_vp, _vp, _i, _i, _vp, _vp, _sz, _vp]),
-    ("k3_expert_workspace_bytes", _sz, [_i, _i]),
-    ("k3_expert_swiglu", _i, [_vp, _vp, _i, _i, _vp, _vp, _vp, _sz, _vp]),
-    ("k3_expert_gate_up", _i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _sz, _vp]),
+    ("k3_mxfp4_gemv", _i, [_vp, _vp, _i, _i, _vp, _vp]),
+    ("k3_expert_swiglu", _i, [_vp, _vp, _i, _i, _vp, _vp, _vp]),
+    ("k3_expert_gate_up", _i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
     ("k3_expert_down", _i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
     ("k3_moe_combine", _i, [_vp, _vp, _i, _i, _vp, _vp, _vp]),
     ("k3_router", _i, [_vp, _vp, _i, _i, _i, _vp, _vp]),
@@ -165,27 +163,18 @@ def _nbytes(t):
     return t.numel() * t.element_size()
 
 
-def k3_mxfp4_gemv_workspace_bytes(cols):
-    return lib().k3_mxfp4_gemv_workspace_bytes(cols)
+def k3_mxfp4_gemv(x, tiles, rows, cols, y, stream=None):
+    _call("k3_mxfp4_gemv", _dp(x), _dp(tiles), rows, cols, _dp(y), _stream(stream))
 
 
-def k3_expert_workspace_bytes(hidden, inter):
-    return lib().k3_expert_workspace_bytes(hidden, inter)
-
-
-def k3_mxfp4_gemv(x, tiles, rows, cols, y, ws, stream=None):
-    _call("k3_mxfp4_gemv", _dp(x), _dp(tiles), rows, cols, _dp(y), _dp(ws), _nbytes(ws),
+def k3_expert_swiglu(x, expert, hidden, inter, y, h, stream=None):
+    _call("k3_expert_swiglu", _dp(x), _dp(expert), hidden, inter, _dp(y), _dp(h),
           _stream(stream))
 
 
-def k3_expert_swiglu(x, expert, hidden, inter, y, h, ws, stream=None):
-    _call("k3_expert_swiglu", _dp(x), _dp(expert), hidden, inter, _dp(y), _dp(h), _dp(ws),
-          _nbytes(ws), _stream(stream))
-
-
-def k3_expert_gate_up(x, experts, idx, k, hidden, inter, h, ws, stream=None):
+def k3_expert_gate_up(x, experts, idx, k, hidden, inter, h, stream=None):
     _call("k3_expert_gate_up", _dp(x), _dp(experts), _dp(idx), k, hidden, inter, _dp(h),
-          _dp(ws), _nbytes(ws), _stream(stream))
+          _stream(stream))
 
 
 def k3_expert_down(h, experts, idx, k, hidden, inter, yp, stream=None):
@@ -218,11 +207,11 @@ def k3_moe_workspace_bytes(T, n_experts, hidden, inter, k):
 
 def k3_moe_layer(x, router_w, experts, n_experts, hidden, inter, k, y, ws, stream=None):
     _call("k3_moe_layer", _dp(x), _dp(router_w), _dp(experts), n_experts, hidden, inter, k,
-          _dp(y), _dp(ws), ws.numel() * ws.element_size(), _stream(stream))
+          _dp(y), _dp(ws), _nbytes(ws), _stream(stream))
 
 
 def k3_moe_layer_ex(x, router_w, experts, n_experts, hidden, inter, k, y, ws, y_f32=None,
                     idx=None, w=None, logits=None, stream=None):
     _call("k3_moe_layer_ex", _dp(x), _dp(router_w), _dp(experts), n_experts, hidden, inter,
-          k, _dp(y), _dp(y_f32), _dp(idx), _dp(w), _dp(logits), _dp(ws),
-          ws.numel() * ws.element_size(), _stream(stream))
+          k, _dp(y), _dp(y_f32), _dp(idx), _dp(w), _dp(logits), _dp(ws), _nbytes(ws),
+          _stream(stream))

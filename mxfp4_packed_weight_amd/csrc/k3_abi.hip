@@ -28,20 +28,8 @@ constexpr int kMaxDim = 1 << 20;  // rows / cols / hidden / inter / T bound
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Activation fragments of a vector of `len` elements, then its flags.
-struct FragWs {
-  size_t frag, flags, total;
-};
-FragWs frag_ws(int len, int pieces) {
-  FragWs F;
-  F.frag = 0;
-  F.flags = align256(act_frag_bytes(len, pieces));
-  F.total = F.flags + align256(sizeof(int) * (size_t)((len + 127) / 128));
-  return F;
-}
-
 struct WsLayout {
-  size_t logits, idx, w, h, yp, xfrag, total;
+  size_t logits, idx, w, h, yp, total;
 };
 
 WsLayout ws_layout(int T, int n, int hidden, int inter, int k) {
@@ -57,8 +45,6 @@ WsLayout ws_layout(int T, int n, int hidden, int inter, int k) {
   off += align256((size_t)T * k * inter * sizeof(float));
   L.yp = off;
   off += align256((size_t)T * k * hidden * sizeof(float));
-  L.xfrag = off;
-  off += frag_ws(hidden, kPieces).total;
   L.total = off;
   return L;
 }
@@ -267,53 +253,51 @@ static k3_status need_ws(const char *fn, size_t have, size_t need) {
   return K3_OK;
 }
 
-size_t k3_mxfp4_gemv_workspace_bytes(int cols) {
-  if (cols < 32 || cols > kMaxDim || cols % 32) return 0;
-  return frag_ws(cols, kPieces).total;
+static k3_status check_frag_lds(const char *fn, const char *what, int len) {
+  const size_t need = act_frag_bytes(len), have = max_dynamic_lds();
+  K3_NEED(fn, need <= have,
+          "%s: %s=%d needs %zu bytes of LDS for its activation fragments; "
+          "this device allows %zu",
+          fn, what, len, need, have);
+  return K3_OK;
 }
 
 k3_status k3_mxfp4_gemv(const float *x, const uint8_t *tiles, int rows,
-                        int cols, float *y, void *ws, size_t ws_bytes,
-                        k3_stream_t stream) {
+                        int cols, float *y, k3_stream_t stream) {
   const char *fn = "k3_mxfp4_gemv";
   K3_NEED_PTR(fn, x);
   K3_NEED_PTR(fn, tiles);
   K3_NEED_PTR(fn, y);
-  K3_NEED_PTR(fn, ws);
   if (k3_status s = check_mat(fn, rows, cols)) return s;
-  const FragWs F = frag_ws(cols, kPieces);
-  if (k3_status s = need_ws(fn, ws_bytes, F.total)) return s;
-  uint8_t *base = static_cast<uint8_t *>(ws);
-  int *flags = reinterpret_cast<int *>(base + F.flags);
-  K3_LAUNCH(fn, launch_act_frag_f32(x, cols, base + F.frag, flags, stream));
-  K3_LAUNCH(fn, launch_gemv_f32(x, tiles, rows, cols, base + F.frag, flags, y,
-                                stream));
+  K3_NEED(fn, cols <= K3_MAX_COLS, "%s: cols=%d above K3_MAX_COLS=%d", fn, cols,
+          K3_MAX_COLS);
+  if (k3_status s = check_frag_lds(fn, "cols", cols)) return s;
+  K3_LAUNCH(fn, launch_gemv_f32(x, tiles, rows, cols, y, stream));
   return K3_OK;
 }
 
-size_t k3_expert_workspace_bytes(int hidden, int inter) {
-  if (check_expert_dims("k3_expert_workspace_bytes", hidden, inter) != K3_OK)
-    return 0;
-  return frag_ws(hidden, kPieces).total;
+static k3_status check_expert_lds(const char *fn, int k, int hidden, int inter) {
+  if (k3_status s = check_frag_lds(fn, "hidden", hidden)) return s;
+  const int span = down_slots_spanned(k, hidden, inter);
+  K3_NEED(fn, (size_t)span * act_frag_bytes(inter) <= max_dynamic_lds(),
+          "%s: inter=%d with k=%d needs %zu bytes of LDS for the down "
+          "fragments; this device allows %zu",
+          fn, inter, k, (size_t)span * act_frag_bytes(inter), max_dynamic_lds());
+  return K3_OK;
 }
 
 k3_status k3_expert_swiglu(const uint16_t *x, const uint8_t *expert,
-                           int hidden, int inter, float *y, float *h, void *ws,
-                           size_t ws_bytes, k3_stream_t stream) {
+                           int hidden, int inter, float *y, float *h,
+                           k3_stream_t stream) {
   const char *fn = "k3_expert_swiglu";
   K3_NEED_PTR(fn, x);
   K3_NEED_PTR(fn, expert);
   K3_NEED_PTR(fn, y);
   K3_NEED_PTR(fn, h);
-  K3_NEED_PTR(fn, ws);
   if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
-  const FragWs F = frag_ws(hidden, kPieces);
-  if (k3_status s = need_ws(fn, ws_bytes, F.total)) return s;
-  uint8_t *base = static_cast<uint8_t *>(ws);
-  int *flags = reinterpret_cast<int *>(base + F.flags);
-  K3_LAUNCH(fn, launch_act_frag_bf16(x, hidden, base + F.frag, flags, stream));
-  K3_LAUNCH(fn, launch_gate_up(x, nullptr, nullptr, expert, 1, hidden, inter,
-                               base + F.frag, flags, h, stream));
+  if (k3_status s = check_expert_lds(fn, 1, hidden, inter)) return s;
+  K3_LAUNCH(fn, launch_gate_up(x, nullptr, nullptr, expert, 1, hidden, inter, h,
+                               stream));
   K3_LAUNCH(fn, launch_down(h, nullptr, nullptr, expert, 1, hidden, inter, y,
                             stream));
   return K3_OK;
@@ -321,24 +305,18 @@ k3_status k3_expert_swiglu(const uint16_t *x, const uint8_t *expert,
 
 k3_status k3_expert_gate_up(const uint16_t *x, const uint8_t *const *experts,
                             const int32_t *idx, int k, int hidden, int inter,
-                            float *h, void *ws, size_t ws_bytes,
-                            k3_stream_t stream) {
+                            float *h, k3_stream_t stream) {
   const char *fn = "k3_expert_gate_up";
   K3_NEED_PTR(fn, x);
   K3_NEED_PTR(fn, experts);
   K3_NEED_PTR(fn, idx);
   K3_NEED_PTR(fn, h);
-  K3_NEED_PTR(fn, ws);
   K3_NEED(fn, k >= 1 && k <= K3_MAX_TOPK, "%s: k=%d outside [1, %d]", fn, k,
           K3_MAX_TOPK);
   if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
-  const FragWs F = frag_ws(hidden, kPieces);
-  if (k3_status s = need_ws(fn, ws_bytes, F.total)) return s;
-  uint8_t *base = static_cast<uint8_t *>(ws);
-  int *flags = reinterpret_cast<int *>(base + F.flags);
-  K3_LAUNCH(fn, launch_act_frag_bf16(x, hidden, base + F.frag, flags, stream));
-  K3_LAUNCH(fn, launch_gate_up(x, experts, idx, nullptr, k, hidden, inter,
-                               base + F.frag, flags, h, stream));
+  if (k3_status s = check_frag_lds(fn, "hidden", hidden)) return s;
+  K3_LAUNCH(fn, launch_gate_up(x, experts, idx, nullptr, k, hidden, inter, h,
+                               stream));
   return K3_OK;
 }
 
@@ -353,6 +331,7 @@ k3_status k3_expert_down(const float *h, const uint8_t *const *experts,
   K3_NEED(fn, k >= 1 && k <= K3_MAX_TOPK, "%s: k=%d outside [1, %d]", fn, k,
           K3_MAX_TOPK);
   if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
+  if (k3_status s = check_expert_lds(fn, k, hidden, inter)) return s;
   K3_LAUNCH(fn, launch_down(h, experts, idx, nullptr, k, hidden, inter, yp,
                             stream));
   return K3_OK;
@@ -447,22 +426,19 @@ k3_status k3_moe_layer_ex(const uint16_t *x, const uint16_t *router_w,
                 fn);
   if (k3_status s = check_routing(fn, 1, n_experts, k)) return s;
   if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
+  if (k3_status s = check_expert_lds(fn, k, hidden, inter)) return s;
   const WsLayout L = ws_layout(1, n_experts, hidden, inter, k);
   if (k3_status s = need_ws(fn, ws_bytes, L.total)) return s;
   uint8_t *base = static_cast<uint8_t *>(ws);
-  const FragWs F = frag_ws(hidden, kPieces);
-  uint8_t *xfrag = base + L.xfrag + F.frag;
-  int *xflags = reinterpret_cast<int *>(base + L.xfrag + F.flags);
   double *lg = logits ? logits : reinterpret_cast<double *>(base + L.logits);
   int32_t *ix = idx ? idx : reinterpret_cast<int32_t *>(base + L.idx);
   float *wt = w ? w : reinterpret_cast<float *>(base + L.w);
   float *h = reinterpret_cast<float *>(base + L.h);
   float *yp = reinterpret_cast<float *>(base + L.yp);
-  K3_LAUNCH(fn, launch_act_frag_bf16(x, hidden, xfrag, xflags, stream));
   K3_LAUNCH(fn, launch_router(x, router_w, 1, hidden, n_experts, lg, stream));
   K3_LAUNCH(fn, launch_topk_f64(lg, nullptr, 1, n_experts, k, ix, wt, stream));
-  K3_LAUNCH(fn, launch_gate_up(x, experts, ix, nullptr, k, hidden, inter,
-                               xfrag, xflags, h, stream));
+  K3_LAUNCH(fn, launch_gate_up(x, experts, ix, nullptr, k, hidden, inter, h,
+                               stream));
   K3_LAUNCH(fn, launch_down(h, experts, ix, nullptr, k, hidden, inter, yp,
                             stream));
   K3_LAUNCH(fn, launch_combine(yp, wt, k, hidden, y, y_f32, stream));

@@ -128,7 +128,10 @@ __device__ __forceinline__ float apply_scale(float acc, float sub, uint32_t e) {
 typedef __attribute__((address_space(1))) const u32x4 gu4_t;
 typedef __attribute__((address_space(1))) const uint32_t gu32_t;
 
-constexpr int kNW = 16;      // waves per workgroup of the streaming kernels
+#ifndef K3_NW
+#define K3_NW 16
+#endif
+constexpr int kNW = K3_NW;   // waves per workgroup of the streaming kernels
 constexpr int kMaxTPW = 8;   // tiles per pass of one workgroup
 
 __device__ __forceinline__ int wave_id() {

@@ -11,6 +11,8 @@
 // in one order, [SAT] "A floating-point contract, not a convention"). The
 // work is a memory-bound stream of packed bytes ("the wait is for bytes to
 // arrive", [SAT] "Reduction one").
+#include <atomic>
+
 #include "k3_mfma.h"
 
 namespace k3 {
@@ -23,56 +25,11 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
 }
 
-// Any flag set among n ints (wave-uniform).
-__device__ __forceinline__ bool any_flag(const int *__restrict__ flags, int n) {
-  int f = 0;
-  for (int i = 0; i < n; ++i) f |= flags[i];
-  return f != 0;
-}
-
-// This lane's B fragment of K block q from a compact fragment array.
-template <int P>
-__device__ __forceinline__ void load_frag(const uint8_t *frag, int q,
-                                          u32x4 &b0, u32x4 &b1, uint32_t &bsc) {
-  const int lane = threadIdx.x & 63, c = lane & 15, h = lane >> 4;
-  const uint8_t *f = frag + (size_t)frag_bytes(P) * q;
-  if (c < P) {
-    const u32x4 *s = reinterpret_cast<const u32x4 *>(f + 32 * (h * P + c));
-    b0 = s[0];
-    b1 = s[1];
-    bsc = f[128 * P + h * P + c];
-  } else {
-    b0 = u32x4{0u, 0u, 0u, 0u};
-    b1 = b0;
-    bsc = 127u;
-  }
-}
-
-// Fragments of an activation vector: one wave per 128-element block.
-template <int P, typename T>
-__global__ __launch_bounds__(256) void act_frag_kernel(const T *__restrict__ v,
-                                                       int len,
-                                                       uint8_t *__restrict__ frag,
-                                                       int *__restrict__ flags) {
-  const int lane = threadIdx.x & 63;
-  const int kb = blockIdx.x * 4 + wave_id();
-  const int nkb = (len + 127) / 128;
-  if (kb >= nkb) return;
-  auto at = [&](int k) -> float {
-    if (k >= len) return 0.f;
-    if constexpr (sizeof(T) == 2) return bf16_to_f32(v[k]);
-    else return (float)v[k];
-  };
-  const bool bad = make_frag<P>(at(128 * kb + lane), at(128 * kb + 64 + lane),
-                                frag + (size_t)frag_bytes(P) * kb, lane);
-  if (lane == 0) flags[kb] = bad ? 1 : 0;
-}
-
 __global__ __launch_bounds__(kThreads) void gemv_f32_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ tiles, int rows,
-    int cols, const uint8_t *__restrict__ xfrag, const int *__restrict__ flags,
-    float *__restrict__ y) {
-  __shared__ float part[kPartFloats];
+    int cols, float *__restrict__ y) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t xfrag[];
+  __shared__ __attribute__((aligned(16))) float part[kPartFloats];
   const MatLayout m = mat_layout(rows, cols);
   int t0, t1;
   wg_range(m.ntiles, &t0, &t1);
@@ -81,19 +38,22 @@ __global__ __launch_bounds__(kThreads) void gemv_f32_kernel(
     const int row = t * kTileRows + lane;
     if (row < rows) y[row] = s;
   };
-  if (any_flag(flags, m.G4)) {
+  if (t0 >= t1) return;
+  auto at = [&](int fb, int k) {
+    const int i = 128 * fb + k;
+    const float v = x[min(i, cols - 1)];
+    return i < cols ? v : 0.f;
+  };
+  auto dst = [&](int fb) { return xfrag + frag_bytes(kPieces) * fb; };
+  if (!run_tiles_mfma<kPieces>(
+          t0, t1, m.G4, base, [&](int) { return (const uint8_t *)xfrag; },
+          [&]() { return preload_acts(at, m.G4); },
+          [&](const ActPre &st) { return build_frags<kPieces>(st, at, m.G4, dst); },
+          epi, part))
     run_tiles_valu(
         t0, t1, m.G, m.G4, base,
         [&](u32x4 w, int g, int) { return group_dot_f32(w, x + (size_t)32 * g); },
         epi, part);
-  } else {
-    run_tiles_mfma(
-        t0, t1, m.G4, base,
-        [&](int, int q, u32x4 &b0, u32x4 &b1, uint32_t &bsc) {
-          load_frag<kPieces>(xfrag, q, b0, b1, bsc);
-        },
-        epi, part);
-  }
 }
 
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
@@ -106,13 +66,12 @@ __device__ __forceinline__ const uint8_t *expert_base(
 
 // Tiles of the k slots back to back: tile t is gate/up tile t % T of slot
 // t / T (T tiles per expert). h[j][i] = SiLU(gate_i . x) * (up_i . x).
-// xfrag/flags: fragments of x (act_frag_kernel).
 __global__ __launch_bounds__(kThreads) void gate_up_kernel(
     const uint16_t *__restrict__ x, const uint8_t *const *__restrict__ experts,
     const int32_t *__restrict__ idx, const uint8_t *__restrict__ single,
-    int nslots, int hidden, int inter, const uint8_t *__restrict__ xfrag,
-    const int *__restrict__ flags, float *__restrict__ h) {
-  __shared__ float part[kPartFloats];
+    int nslots, int hidden, int inter, float *__restrict__ h) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t xfrag[];
+  __shared__ __attribute__((aligned(16))) float part[kPartFloats];
   const ExpertLayout L = expert_layout(hidden, inter);
   const int T = L.gu.ntiles;
   int t0, t1;
@@ -127,77 +86,69 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(
     gu_lane_row(t % T, lane, &is_up, &row);
     if (lane < 32 && row < inter) h[(size_t)(t / T) * inter + row] = silu(s) * u;
   };
-  if (any_flag(flags, L.gu.G4)) {
+  if (t0 >= t1) return;
+  auto at = [&](int fb, int k) {
+    const int i = 128 * fb + k;
+    const float v = bf16_to_f32(x[min(i, hidden - 1)]);
+    return i < hidden ? v : 0.f;
+  };
+  auto dst = [&](int fb) { return xfrag + frag_bytes(kPieces) * fb; };
+  if (!run_tiles_mfma<kPieces>(
+          t0, t1, L.gu.G4, base, [&](int) { return (const uint8_t *)xfrag; },
+          [&]() { return preload_acts(at, L.gu.G4); },
+          [&](const ActPre &st) { return build_frags<kPieces>(st, at, L.gu.G4, dst); },
+          epi, part)) {
     const uint32_t *xp = reinterpret_cast<const uint32_t *>(x);
     run_tiles_valu(
         t0, t1, L.gu.G, L.gu.G4, base,
         [&](u32x4 w, int g, int) { return group_dot_bf16(w, xp + (size_t)16 * g); },
         epi, part);
-  } else {
-    run_tiles_mfma(
-        t0, t1, L.gu.G4, base,
-        [&](int, int q, u32x4 &b0, u32x4 &b1, uint32_t &bsc) {
-          load_frag<kPieces>(xfrag, q, b0, b1, bsc);
-        },
-        epi, part);
   }
 }
 
 // yp[j][r] = W_down(e_j)[r] . h[j], tiles of the k slots back to back. The
-// workgroup's range is walked slot by slot; for each slot the workgroup
-// first builds the 6-piece fragments of h[j] in LDS (dynamic LDS of
-// ceil(inter/128) fragments).
+// fragments of h[j] for every slot j the workgroup's range touches are built
+// in LDS (dynamic LDS of down_slots_spanned x ceil(inter/128) fragments).
 __global__ __launch_bounds__(kThreads) void down_kernel(
     const float *__restrict__ h, const uint8_t *const *__restrict__ experts,
     const int32_t *__restrict__ idx, const uint8_t *__restrict__ single,
     int nslots, int hidden, int inter, float *__restrict__ yp) {
-  extern __shared__ uint8_t hfrag[];
-  __shared__ float part[kPartFloats];
-  __shared__ int hbad;
+  extern __shared__ __attribute__((aligned(16))) uint8_t hfrag[];
+  __shared__ __attribute__((aligned(16))) float part[kPartFloats];
   const ExpertLayout L = expert_layout(hidden, inter);
   const int T = L.down.ntiles;
   const int nkb = L.down.G4;
-  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int slot_bytes = frag_bytes(kPieces) * nkb;
   int t0, t1;
   wg_range(nslots * T, &t0, &t1);
-  for (int a = t0; a < t1;) {
-    const int j = a / T;
-    const int b = min(t1, (j + 1) * T);
-    const float *hj = h + (size_t)j * inter;
-    __syncthreads();
-    if (threadIdx.x == 0) hbad = 0;
-    __syncthreads();
-    for (int kb = wave; kb < nkb; kb += kNW) {
-      const int k0 = 128 * kb + lane, k1 = k0 + 64;
-      const bool bad = make_frag<kPieces>(
-          k0 < inter ? hj[k0] : 0.f, k1 < inter ? hj[k1] : 0.f,
-          hfrag + (size_t)frag_bytes(kPieces) * kb, lane);
-      if (bad && lane == 0) hbad = 1;
-    }
-    __syncthreads();
-    auto base = [&](int t) {
-      return expert_base(experts, idx, single, j) + L.down_offset +
-             (size_t)(t % T) * L.down.tile_bytes;
-    };
-    auto epi = [&](int t, int ln, float s) {
-      const int row = (t % T) * kTileRows + ln;
-      if (row < hidden) yp[(size_t)j * hidden + row] = s;
-    };
-    if (hbad) {
-      run_tiles_valu(
-          a, b, L.down.G, L.down.G4, base,
-          [&](u32x4 w, int g, int) { return group_dot_f32(w, hj + (size_t)32 * g); },
-          epi, part);
-    } else {
-      run_tiles_mfma(
-          a, b, L.down.G4, base,
-          [&](int, int q, u32x4 &b0, u32x4 &b1, uint32_t &bsc) {
-            load_frag<kPieces>(hfrag, q, b0, b1, bsc);
-          },
-          epi, part);
-    }
-    a = b;
-  }
+  if (t0 >= t1) return;
+  const int j0 = t0 / T;
+  auto base = [&](int t) {
+    return expert_base(experts, idx, single, t / T) + L.down_offset +
+           (size_t)(t % T) * L.down.tile_bytes;
+  };
+  auto frag = [&](int t) { return (const uint8_t *)hfrag + (t / T - j0) * slot_bytes; };
+  auto epi = [&](int t, int ln, float s) {
+    const int row = (t % T) * kTileRows + ln;
+    if (row < hidden) yp[(size_t)(t / T) * hidden + row] = s;
+  };
+  const int nfb = ((t1 - 1) / T - j0 + 1) * nkb;  // blocks of every slot touched
+  auto at = [&](int fb, int k) {
+    const int i = 128 * (fb % nkb) + k;
+    const float v = h[(size_t)(j0 + fb / nkb) * inter + min(i, inter - 1)];
+    return i < inter ? v : 0.f;
+  };
+  auto dst = [&](int fb) { return hfrag + frag_bytes(kPieces) * fb; };
+  if (!run_tiles_mfma<kPieces>(
+          t0, t1, nkb, base, frag, [&]() { return preload_acts(at, nfb); },
+          [&](const ActPre &st) { return build_frags<kPieces>(st, at, nfb, dst); },
+          epi, part))
+    run_tiles_valu(
+        t0, t1, L.down.G, L.down.G4, base,
+        [&](u32x4 w, int g, int t) {
+          return group_dot_f32(w, h + (size_t)(t / T) * inter + (size_t)32 * g);
+        },
+        epi, part);
 }
 
 // y[i] = sum_j w[j] * yp[j][i] in rank order j = 0..k-1, then bf16 (RNE).
@@ -227,46 +178,70 @@ unsigned grid_for_tiles(int total) {
 
 }  // namespace
 
-size_t act_frag_bytes(int len, int pieces) {
-  return (size_t)((len + 127) / 128) * frag_bytes(pieces);
+size_t act_frag_bytes(int len) {
+  return (size_t)((len + 127) / 128) * frag_bytes(kPieces);
 }
 
-hipError_t launch_act_frag_bf16(const uint16_t *v, int len, uint8_t *frag,
-                                int *flags, hipStream_t s) {
-  const int nkb = (len + 127) / 128;
-  hipLaunchKernelGGL((act_frag_kernel<kPieces, uint16_t>),
-                     dim3((nkb + 3) / 4), dim3(256), 0, s, v, len, frag, flags);
-  return hipGetLastError();
+int down_slots_spanned(int nslots, int hidden, int inter) {
+  const ExpertLayout L = expert_layout(hidden, inter);
+  const int T = L.down.ntiles, total = nslots * T;
+  const int grid = (int)grid_for_tiles(total);
+  const int per_wg = (total + grid - 1) / grid;
+  return min(nslots, (per_wg + T - 1) / T + 1);
 }
 
-hipError_t launch_act_frag_f32(const float *v, int len, uint8_t *frag,
-                               int *flags, hipStream_t s) {
-  const int nkb = (len + 127) / 128;
-  hipLaunchKernelGGL((act_frag_kernel<kPieces, float>), dim3((nkb + 3) / 4),
-                     dim3(256), 0, s, v, len, frag, flags);
-  return hipGetLastError();
+namespace {
+// Sets the kernel's dynamic LDS allowance once and refuses sizes beyond the
+// device's LDS (minus the kernel's static arrays).
+hipError_t lds_ok(const void *kernel, size_t dyn, size_t *limit_out) {
+  static std::atomic<int> cap{0};
+  int c = cap.load(std::memory_order_relaxed);
+  if (c <= 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&c, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) ==
+            hipSuccess &&
+        c > 0)
+      cap.store(c, std::memory_order_relaxed);
+    else
+      c = 160 * 1024;  // gfx950's LDS per workgroup; not cached: no device answered
+  }
+  const size_t limit = (size_t)c - sizeof(float) * kPartFloats;
+  if (limit_out) *limit_out = limit;
+  if (dyn > limit) return hipErrorInvalidValue;
+  if (dyn > 48 * 1024)
+    return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)dyn);
+  return hipSuccess;
+}
+}  // namespace
+
+size_t max_dynamic_lds() {
+  size_t limit = 0;
+  (void)lds_ok(nullptr, 0, &limit);
+  return limit;
 }
 
 hipError_t launch_gemv_f32(const float *x, const uint8_t *tiles, int rows,
-                           int cols, const uint8_t *xfrag, const int *flags,
-                           float *y, hipStream_t s) {
+                           int cols, float *y, hipStream_t s) {
   const MatLayout m = mat_layout(rows, cols);
+  const size_t dyn = act_frag_bytes(cols);
+  if (hipError_t e = lds_ok((const void *)gemv_f32_kernel, dyn, nullptr)) return e;
   hipLaunchKernelGGL(gemv_f32_kernel, dim3(grid_for_tiles(m.ntiles)),
-                     dim3(kThreads), 0, s, x, tiles, rows, cols, xfrag, flags,
-                     y);
+                     dim3(kThreads), dyn, s, x, tiles, rows, cols, y);
   return hipGetLastError();
 }
 
 hipError_t launch_gate_up(const uint16_t *x, const uint8_t *const *experts,
                           const int32_t *idx, const uint8_t *single,
-                          int nslots, int hidden, int inter,
-                          const uint8_t *xfrag, const int *flags, float *h,
+                          int nslots, int hidden, int inter, float *h,
                           hipStream_t s) {
   const ExpertLayout L = expert_layout(hidden, inter);
+  const size_t dyn = act_frag_bytes(hidden);
+  if (hipError_t e = lds_ok((const void *)gate_up_kernel, dyn, nullptr)) return e;
   hipLaunchKernelGGL(gate_up_kernel,
                      dim3(grid_for_tiles(nslots * L.gu.ntiles)), dim3(kThreads),
-                     0, s, x, experts, idx, single, nslots, hidden, inter,
-                     xfrag, flags, h);
+                     dyn, s, x, experts, idx, single, nslots, hidden, inter, h);
   return hipGetLastError();
 }
 
@@ -274,10 +249,13 @@ hipError_t launch_down(const float *h, const uint8_t *const *experts,
                        const int32_t *idx, const uint8_t *single, int nslots,
                        int hidden, int inter, float *yp, hipStream_t s) {
   const ExpertLayout L = expert_layout(hidden, inter);
+  const size_t dyn =
+      (size_t)down_slots_spanned(nslots, hidden, inter) * act_frag_bytes(inter);
+  if (hipError_t e = lds_ok((const void *)down_kernel, dyn, nullptr)) return e;
   hipLaunchKernelGGL(down_kernel,
                      dim3(grid_for_tiles(nslots * L.down.ntiles)),
-                     dim3(kThreads), act_frag_bytes(inter, kPieces), s, h,
-                     experts, idx, single, nslots, hidden, inter, yp);
+                     dim3(kThreads), dyn, s, h, experts, idx, single, nslots,
+                     hidden, inter, yp);
   return hipGetLastError();
 }
 

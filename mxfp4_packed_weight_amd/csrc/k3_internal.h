@@ -96,26 +96,22 @@ hipError_t launch_expert_pack(const uint8_t *gn, const uint8_t *gs,
                               const uint8_t *un, const uint8_t *us,
                               const uint8_t *dn, const uint8_t *ds, int hidden,
                               int inter, uint8_t *dst, hipStream_t s);
-// Activation fragments for the FP4 matrix unit (3 pieces for bf16, 6 for
-// fp32) and one non-finite flag per 128-element block.
 // Fixed-point E4M3 pieces an activation vector is split into for the FP4
-// matrix instruction (k3_mfma.h).
+// matrix instruction (k3_mfma.h); the matrix kernels build these fragments
+// in LDS themselves (act_frag_bytes(len) bytes for a vector of len).
 constexpr int kPieces = 5;
-size_t act_frag_bytes(int len, int pieces);
-hipError_t launch_act_frag_bf16(const uint16_t *v, int len, uint8_t *frag,
-                                int *flags, hipStream_t s);
-hipError_t launch_act_frag_f32(const float *v, int len, uint8_t *frag,
-                               int *flags, hipStream_t s);
+size_t act_frag_bytes(int len);
+// Dynamic LDS a matrix kernel may take for fragments on this device.
+size_t max_dynamic_lds();
+// Expert slots one down-kernel workgroup's tile range can touch.
+int down_slots_spanned(int nslots, int hidden, int inter);
 hipError_t launch_gemv_f32(const float *x, const uint8_t *tiles, int rows,
-                           int cols, const uint8_t *xfrag, const int *flags,
-                           float *y, hipStream_t s);
+                           int cols, float *y, hipStream_t s);
 // Gate/up + SwiGLU over `nslots` experts: slot j uses expert experts[idx[j]]
-// (or `single` when experts == nullptr); h[j][inter]. xfrag/flags from
-// launch_act_frag_bf16 of x.
+// (or `single` when experts == nullptr); h[j][inter].
 hipError_t launch_gate_up(const uint16_t *x, const uint8_t *const *experts,
                           const int32_t *idx, const uint8_t *single,
-                          int nslots, int hidden, int inter,
-                          const uint8_t *xfrag, const int *flags, float *h,
+                          int nslots, int hidden, int inter, float *h,
                           hipStream_t s);
 // Down projection: yp[j][hidden] = W_down(e_j) h[j].
 hipError_t launch_down(const float *h, const uint8_t *const *experts,

@@ -111,162 +111,264 @@ __device__ __forceinline__ bool make_frag(float v0, float v1, uint8_t *frag,
   return false;
 }
 
+// ---- fragment building ------------------------------------------------
+// A workgroup builds the fragments of nfb 128-element blocks into LDS; wave
+// w takes blocks w, w + kNW, ... The activations of its first kPreBlocks
+// blocks are loaded ahead, before the first weight loads, so that waiting
+// for them does not wait for weights. at(fb, k) must load unconditionally
+// (clamped address) so the compiler's load counts stay exact.
+constexpr int kPreBlocks = 8;
+struct ActPre {
+  float v[2 * kPreBlocks];
+};
+
+template <class At>
+__device__ __forceinline__ ActPre preload_acts(At at, int nfb) {
+  const int lane = threadIdx.x & 63, w = wave_id();
+  ActPre st;
+#pragma unroll
+  for (int i = 0; i < kPreBlocks; ++i) {
+    const int fb = min(w + kNW * i, nfb - 1);
+    st.v[2 * i] = at(fb, lane);
+    st.v[2 * i + 1] = at(fb, lane + 64);
+  }
+  return st;
+}
+
+// dst(fb) -> uint8_t*  LDS fragment of block fb. True if a value is not finite.
+template <int P, class At, class Dst>
+__device__ __forceinline__ bool build_frags(const ActPre &st, At at, int nfb,
+                                            Dst dst) {
+  const int lane = threadIdx.x & 63, w = wave_id();
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < kPreBlocks; ++i)
+    if (w + kNW * i < nfb)
+      bad |= make_frag<P>(st.v[2 * i], st.v[2 * i + 1], dst(w + kNW * i), lane);
+  for (int fb = w + kNW * kPreBlocks; fb < nfb; fb += kNW)
+    bad |= make_frag<P>(at(fb, lane), at(fb, lane + 64), dst(fb), lane);
+  return bad;
+}
+
 // ---- streaming loop ----------------------------------------------------
 #ifndef K3_MFMA_DEPTH
 #define K3_MFMA_DEPTH 2
 #endif
 constexpr int kMfmaDepth = K3_MFMA_DEPTH;
-constexpr int kPartFloats = kMaxTPW * kNW * 64;  // per-slice row partials
+constexpr int kPartFloats = kMaxTPW * kNW * 64;  // per-wave row partials
+// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left free (gfx9
+// encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int kWaitVmcnt0 = 0x0F70;
 
-// Row sums of the four accumulators: C column sum over the 16 lanes of each
-// DPP row (columns), result in lane 16j+15 for rows 16m + 4j + i.
-__device__ __forceinline__ float row16_sum(float v) {
+// B operand of K block q for this lane from a P-piece fragment array in LDS.
+// Lanes of columns >= P read column 0 (so that every lane issues the same
+// reads) and then take zeros.
+template <int P>
+__device__ __forceinline__ v8i b_operand(const uint8_t *frag, int q,
+                                         uint32_t *bsc) {
+  const int lane = threadIdx.x & 63, c = lane & 15, h = lane >> 4;
+  const bool live = c < P;
+  const int cc = live ? c : 0;
+  const uint8_t *f = frag + frag_bytes(P) * q;
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(f + 32 * (h * P + cc));
+  const u32x4 b0 = src[0], b1 = src[1];
+  *bsc = f[128 * P + h * P + cc];
+  const uint32_t z = live ? 0xffffffffu : 0u;
+  return v8i{(int)(b0.x & z), (int)(b0.y & z), (int)(b0.z & z), (int)(b0.w & z),
+             (int)(b1.x & z), (int)(b1.y & z), (int)(b1.z & z), (int)(b1.w & z)};
+}
+
+// Inclusive prefix sum over the lanes of each 16-lane row, three steps: lane
+// i < 8 ends with the sum of lanes 0..i of its row.
+__device__ __forceinline__ float row_prefix8(float v) {
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, false));
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, false));
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, false));
   return v;
 }
 
-// Streams tiles [t_begin, t_end) through one workgroup of kNW waves with
-// the same slice and summation structure as run_tiles (k3_decode.h).
-//   base(t)           -> const uint8_t*  tile t's bytes (wave-uniform)
-//   bload(t, q, b0, b1, bsc)             this lane's B fragment of K block q
-//   epi(t, lane, sum)                    finished row sums
-// `part` is the caller's LDS array of kPartFloats floats.
-template <class Base, class BLoad, class Epi>
-__device__ __forceinline__ void run_tiles_mfma(int t_begin, int t_end, int G4,
-                                               Base base, BLoad bload, Epi epi,
+// Streams tiles [t_begin, t_end) of one matrix stack through the kNW waves
+// of a workgroup, kMaxTPW tiles at a time. The chunk's (tile, quad) items
+// are split into kNW contiguous runs, one per wave; a wave keeps four 16x16
+// accumulators (one per 16-row sub-block of a quad), adds the P piece
+// columns of each row when its run leaves a tile and stores the 64 row sums
+// to its own LDS slot of that tile. The slots of a tile are then added in
+// wave order, so every row has one summation order fixed by the shape.
+//   base(t)  -> const uint8_t*  tile t's packed bytes (wave-uniform)
+//   frag(t)  -> const uint8_t*  LDS fragments of the activation of tile t
+//   pre()    -> ActPre          loads this wave's activations (runs first)
+//   build(st)-> bool            builds the fragments from them (every wave
+//                               takes part; runs once, after the first
+//                               weight loads are in flight); true if an
+//                               activation is not finite, and then nothing
+//                               is computed
+//   epi(t, lane, sum)           finished row sums of tile t, row = lane
+// `part` is the caller's 16-byte aligned LDS array of kPartFloats floats.
+// Returns false if build() reported a non-finite activation.
+template <int P, class Base, class Frag, class Pre, class Build, class Epi>
+__device__ __forceinline__ bool run_tiles_mfma(int t_begin, int t_end, int G4,
+                                               Base base, Frag frag, Pre pre,
+                                               Build build, Epi epi,
                                                float *part) {
+  static_assert(P >= 1 && P <= 8, "row_prefix8 adds at most 8 columns");
+  if (t_begin >= t_end) return true;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
-  for (int c0 = t_begin; c0 < t_end; c0 += kMaxTPW) {
-    const int ntl = min(kMaxTPW, t_end - c0);
-    auto slice_of = [&](int tl) { return (wave + c0 + tl) % kNW; };
-    auto slot_base = [&](int tl) { return (tl * kNW + slice_of(tl)) * 64; };
-    for (int tl = 0; tl < ntl; ++tl) part[slot_base(tl) + lane] = 0.f;
 
-    int nitems = 0;
-    for (int tl = 0; tl < ntl; ++tl) {
-      const int s = slice_of(tl);
-      nitems += (s + 1) * G4 / kNW - s * G4 / kNW;
-    }
-    if (nitems > 0) {
-      int ctl = -1, cq = 0, cqe = 0;
-      const uint8_t *cbase = nullptr;
-      auto advance = [&]() {
-        if (++cq < cqe) return;
-        while (++ctl < ntl) {
-          const int s = slice_of(ctl);
-          cq = s * G4 / kNW;
-          cqe = (s + 1) * G4 / kNW;
-          if (cq < cqe) break;
-        }
-        cbase = base(c0 + ctl);
-      };
-      u32x4 a[kMfmaDepth][4], b[kMfmaDepth][2];
-      uint32_t asc[kMfmaDepth], bsc[kMfmaDepth];
-      int stl[kMfmaDepth], sq[kMfmaDepth];
-      auto load = [&](int d) {
-        advance();
-        stl[d] = ctl;
-        sq[d] = cq;
-        const uint8_t *qb = cbase + (size_t)kQuadBytes * cq;
-        gu4_t *p = (gu4_t *)(qb) + lane;
+  // chunk state: tiles [c0, c0 + ntl), this wave's items [i0, i0 + nitems)
+  int c0 = t_begin, ntl = 0, nitems = 0;
+  int ltl = 0, lq = 0;  // next item to load (tile-local index, quad)
+  const uint8_t *lbase = nullptr;  // base(c0 + ltl), refreshed per tile
+  u32x4 a[kMfmaDepth][4];
+  uint32_t asc[kMfmaDepth];
+  auto setup = [&](int c) {
+    c0 = c;
+    ntl = min(kMaxTPW, t_end - c0);
+    for (int tl = 0; tl < ntl; ++tl) part[(tl * kNW + wave) * 64 + lane] = 0.f;
+    const int n = ntl * G4;
+    const int i0 = wave * n / kNW;
+    nitems = (wave + 1) * n / kNW - i0;
+    ltl = i0 / G4;
+    lq = i0 % G4;
+    if (nitems > 0) lbase = base(c0 + ltl);
+  };
+  auto load = [&](int d) {
+    const uint8_t *qb = lbase + (size_t)kQuadBytes * lq;
+    const gu4_t *p = (const gu4_t *)(qb) + lane;
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-          a[d][m] = __builtin_nontemporal_load(p + (size_t)m * 64);
-        asc[d] = __builtin_nontemporal_load((gu32_t *)(qb + 4096) + lane);
-        bload(c0 + ctl, cq, b[d][0], b[d][1], bsc[d]);
-      };
-      v4f acc[4];
+    for (int m = 0; m < 4; ++m)
+      a[d][m] = __builtin_nontemporal_load(p + (size_t)m * 64);
+    asc[d] = __builtin_nontemporal_load((const gu32_t *)(qb + 4096) + lane);
+    if (++lq == G4) {
+      lq = 0;
+      ++ltl;
+      if (c0 + ltl < t_end) lbase = base(c0 + ltl);
+    }
+  };
+  auto prologue = [&]() {
+    if (nitems >= kMfmaDepth) {
+#pragma unroll
+      for (int d = 0; d < kMfmaDepth; ++d) load(d);
+    } else {
+#pragma unroll
+      for (int d = 0; d < kMfmaDepth; ++d)
+        if (d < nitems) load(d);
+    }
+  };
+
+  // Consumes the chunk whose prologue is in flight, then writes its rows.
+  auto stream_chunk = [&]() {
+    int ktl = (wave * ntl * G4 / kNW) / G4, kq = (wave * ntl * G4 / kNW) % G4;
+    int cur = ktl;  // tile the accumulators belong to
+    const uint8_t *kfr = nitems > 0 ? frag(c0 + ktl) : nullptr;
+    v4f acc[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
+    auto flush = [&]() {
+      // lane 16j + P-1 ends with rows 16m + 4j + i of tile `cur`
+      v4f r[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[m][i] = row_prefix8(acc[m][i]);
+      if ((lane & 15) == P - 1) {
+        float *dst = part + (cur * kNW + wave) * 64 + 4 * (lane >> 4);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) *reinterpret_cast<v4f *>(dst + 16 * m) = r[m];
+      }
 #pragma unroll
       for (int m = 0; m < 4; ++m) acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
-      int cur = -1;
-      auto flush = [&]() {
-        // lane 16j+15 holds rows 16m + 4j + i of this slice's tile
+    };
+    auto consume = [&](int d) {
+      if (ktl != cur) {
+        flush();
+        cur = ktl;
+      }
+      uint32_t bsc;
+      const v8i bv = b_operand<P>(kfr, kq, &bsc);
+      uint32_t e = asc[d];
+      // groups with exponent byte 255 contribute nothing
+      const uint32_t ff = (~e - 0x01010101u) & e & 0x80808080u;
+      if (__ballot(ff != 0u)) {
 #pragma unroll
         for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float v = row16_sum(acc[m][i]);
-            if ((lane & 15) == 15)
-              part[slot_base(cur) + 16 * m + 4 * (lane >> 4) + i] = v;
+          if (((e >> (8 * m)) & 255u) == 255u) {
+            a[d][m] = u32x4{0u, 0u, 0u, 0u};
+            e &= ~(255u << (8 * m));
           }
-#pragma unroll
-        for (int m = 0; m < 4; ++m) acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
-      };
-      auto consume = [&](int d) {
-        if (stl[d] != cur) {
-          if (cur >= 0) flush();
-          cur = stl[d];
-        }
-        uint32_t e = asc[d];
-        // groups with exponent byte 255 contribute nothing
-        const uint32_t ff = (~e - 0x01010101u) & e & 0x80808080u;
-        if (__ballot(ff != 0u)) {
-#pragma unroll
-          for (int m = 0; m < 4; ++m)
-            if (((e >> (8 * m)) & 255u) == 255u) {
-              a[d][m] = u32x4{0u, 0u, 0u, 0u};
-              e &= ~(255u << (8 * m));
-            }
-        }
-        const u32x4 b0 = b[d][0], b1 = b[d][1];
-        const v8i bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
-                        (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-        // sub-block m takes byte m of the lane's exponent register (op_sel)
+      }
+      // sub-block m takes byte m of the lane's exponent register (op_sel)
 #define K3_MFMA_SUB(M)                                                         \
   {                                                                            \
     const u32x4 am = a[d][M];                                                  \
     const v8i av = {(int)am.x, (int)am.y, (int)am.z, (int)am.w, 0, 0, 0, 0};   \
     acc[M] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                 \
-        av, bv, acc[M], 4, 0, M, (int)e, 0, (int)bsc[d]);                      \
+        av, bv, acc[M], 4, 0, M, (int)e, 0, (int)bsc);                         \
   }
-        K3_MFMA_SUB(0)
-        K3_MFMA_SUB(1)
-        K3_MFMA_SUB(2)
-        K3_MFMA_SUB(3)
+      K3_MFMA_SUB(0)
+      K3_MFMA_SUB(1)
+      K3_MFMA_SUB(2)
+      K3_MFMA_SUB(3)
 #undef K3_MFMA_SUB
-      };
-      if (nitems >= kMfmaDepth) {
-#pragma unroll
-        for (int d = 0; d < kMfmaDepth; ++d) load(d);
-        int rem = nitems - kMfmaDepth;
-        for (; rem >= kMfmaDepth; rem -= kMfmaDepth) {
-#pragma unroll
-          for (int d = 0; d < kMfmaDepth; ++d) {
-            consume(d);
-            load(d);
-          }
-        }
+      if (++kq == G4) {
+        kq = 0;
+        ++ktl;
+        if (c0 + ktl < t_end) kfr = frag(c0 + ktl);
+      }
+    };
+    if (nitems >= kMfmaDepth) {
+      int rem = nitems - kMfmaDepth;  // items not yet loaded
+      for (; rem >= kMfmaDepth; rem -= kMfmaDepth) {
 #pragma unroll
         for (int d = 0; d < kMfmaDepth; ++d) {
           consume(d);
-          if (d < rem) load(d);
+          load(d);
         }
-#pragma unroll
-        for (int d = 0; d < kMfmaDepth; ++d)
-          if (d < rem) consume(d);
-      } else {
-#pragma unroll
-        for (int d = 0; d < kMfmaDepth; ++d)
-          if (d < nitems) load(d);
-#pragma unroll
-        for (int d = 0; d < kMfmaDepth; ++d)
-          if (d < nitems) consume(d);
       }
-      flush();
+#pragma unroll
+      for (int d = 0; d < kMfmaDepth; ++d) {
+        consume(d);
+        if (d < rem) load(d);
+      }
+#pragma unroll
+      for (int d = 0; d < kMfmaDepth; ++d)
+        if (d < rem) consume(d);
+    } else {
+#pragma unroll
+      for (int d = 0; d < kMfmaDepth; ++d)
+        if (d < nitems) consume(d);
     }
+    if (nitems > 0) flush();
     __syncthreads();
     for (int tl = wave; tl < ntl; tl += kNW) {
       float sum = 0.f;
 #pragma unroll
-      for (int s = 0; s < kNW; ++s) sum += part[(tl * kNW + s) * 64 + lane];
+      for (int w = 0; w < kNW; ++w) sum += part[(tl * kNW + w) * 64 + lane];
       epi(c0 + tl, lane, sum);
     }
     __syncthreads();
+  };
+
+  // Activation loads first, then the first chunk's weight loads, then the
+  // fragments (waiting for the activations only), then the stream.
+  {
+    const ActPre st = pre();
+    __builtin_amdgcn_sched_barrier(0);  // keep the activation loads first
+    setup(t_begin);
+    prologue();
+    __builtin_amdgcn_sched_barrier(0);
+    if (__syncthreads_or(build(st) ? 1 : 0)) return false;
   }
+  for (;;) {
+    // Enter the loop with no load pending (the first consume needs these
+    // bytes anyway): the loop's own waits then count only its own loads.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    stream_chunk();
+    if (c0 + kMaxTPW >= t_end) break;
+    setup(c0 + kMaxTPW);
+    prologue();
+  }
+  return true;
 }
 
 // ---- VALU path for non-finite activations ------------------------------

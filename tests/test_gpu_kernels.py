@@ -29,10 +29,9 @@ def gpu_gemv(nib, sc, x):
     tiles = up(K.k3_mxfp4_pack_host(nib, sc))
     xd = up(np.asarray(x, np.float32))
     y = empty(rows, torch.float32)
-    ws = empty(K.k3_mxfp4_gemv_workspace_bytes(cols), torch.uint8)
-    K.k3_mxfp4_gemv(xd, tiles, rows, cols, y, ws)
+    K.k3_mxfp4_gemv(xd, tiles, rows, cols, y)
     y1 = y.cpu().numpy().copy()
-    K.k3_mxfp4_gemv(xd, tiles, rows, cols, y, ws)
+    K.k3_mxfp4_gemv(xd, tiles, rows, cols, y)
     y2 = y.cpu().numpy()
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), "rerun not bit-identical"
     return y1
@@ -138,10 +137,9 @@ def _expert_on_gpu(E, x_bf16, hidden, inter):
     xd = up(x_bf16)
     y = empty(hidden, torch.float32)
     h = empty(inter, torch.float32)
-    ws = empty(K.k3_expert_workspace_bytes(hidden, inter), torch.uint8)
-    K.k3_expert_swiglu(xd, blob, hidden, inter, y, h, ws)
+    K.k3_expert_swiglu(xd, blob, hidden, inter, y, h)
     y1, h1 = y.cpu().numpy().copy(), h.cpu().numpy().copy()
-    K.k3_expert_swiglu(xd, blob, hidden, inter, y, h, ws)
+    K.k3_expert_swiglu(xd, blob, hidden, inter, y, h)
     assert np.array_equal(y1.view(np.uint32), y.cpu().numpy().view(np.uint32))
     return y1, h1
 

@@ -39,8 +39,7 @@ def run_layer(pool, R_d, x, n, hidden, inter, k):
     h = empty((k, inter), torch.float32)
     yp = empty((k, hidden), torch.float32)
     y3 = empty(hidden, torch.float32)
-    ews = empty(K.k3_expert_workspace_bytes(hidden, inter), torch.uint8)
-    K.k3_expert_gate_up(xd, pool.table, idx, k, hidden, inter, h, ews)
+    K.k3_expert_gate_up(xd, pool.table, idx, k, hidden, inter, h)
     K.k3_expert_down(h, pool.table, idx, k, hidden, inter, yp)
     K.k3_moe_combine(yp, w, k, hidden, None, y3)
     assert np.array_equal(y3.cpu().numpy().view(np.uint32), out["y32"].view(np.uint32))

@@ -114,27 +114,23 @@ def _fake(n):
 
 def test_refusals_before_launch(L):
     s = None
-    big = 1 << 30
-    rc = L.k3_mxfp4_gemv(None, _fake(1), 64, 64, _fake(2), _fake(4), big, s)
+    rc = L.k3_mxfp4_gemv(None, _fake(1), 64, 64, _fake(2), s)
     assert rc == K.K3_ERR_ARG and "x is NULL" in K.last_error()
-    rc = L.k3_mxfp4_gemv(ctypes.c_void_p(0x10004), _fake(1), 64, 64, _fake(2), _fake(4), big, s)
+    rc = L.k3_mxfp4_gemv(ctypes.c_void_p(0x10004), _fake(1), 64, 64, _fake(2), s)
     assert rc == K.K3_ERR_ARG and "aligned" in K.last_error()
-    rc = L.k3_mxfp4_gemv(_fake(3), _fake(1), 64, 48, _fake(2), _fake(4), big, s)
+    rc = L.k3_mxfp4_gemv(_fake(3), _fake(1), 64, 48, _fake(2), s)
     assert rc == K.K3_ERR_CONFIG and "cols=48" in K.last_error()
-    rc = L.k3_mxfp4_gemv(_fake(3), _fake(1), 0, 64, _fake(2), _fake(4), big, s)
+    rc = L.k3_mxfp4_gemv(_fake(3), _fake(1), 0, 64, _fake(2), s)
     assert rc == K.K3_ERR_CONFIG
-    rc = L.k3_mxfp4_gemv(_fake(3), _fake(1), 64, 64, _fake(2), _fake(4),
-                         K.k3_mxfp4_gemv_workspace_bytes(64) - 1, s)
-    assert rc == K.K3_ERR_MEMORY
+    rc = L.k3_mxfp4_gemv(_fake(3), _fake(1), 64, K.K3_MAX_COLS + 32, _fake(2), s)
+    assert rc == K.K3_ERR_CONFIG and "K3_MAX_COLS" in K.last_error()
     rc = L.k3_router_topk(_fake(1), None, 1, 896, 17 + 64, _fake(2), _fake(3), s)
     assert rc == K.K3_ERR_CONFIG and "k=81" in K.last_error()
     rc = L.k3_router_topk(_fake(1), None, 1, 8, 9, _fake(2), _fake(3), s)
     assert rc == K.K3_ERR_CONFIG
-    rc = L.k3_expert_swiglu(_fake(1), _fake(2), 7168, 1500, _fake(3), _fake(4), _fake(5),
-                            big, s)
+    rc = L.k3_expert_swiglu(_fake(1), _fake(2), 7168, 1500, _fake(3), _fake(4), s)
     assert rc == K.K3_ERR_CONFIG and "inter=1500" in K.last_error()
-    rc = L.k3_expert_swiglu(_fake(1), _fake(2), 7168, 8192, _fake(3), _fake(4), _fake(5),
-                            big, s)
+    rc = L.k3_expert_swiglu(_fake(1), _fake(2), 7168, 8192, _fake(3), _fake(4), s)
     assert rc == K.K3_ERR_CONFIG  # inter above K3_MAX_INTER
     need = K.k3_moe_workspace_bytes(1, 896, 7168, 1536, 16)
     assert need > 0
