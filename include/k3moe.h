@@ -75,20 +75,17 @@ int k3_abi_version(void);
 /* ------------------------------------------------------------------------
  * Layout. A matrix W[rows][cols] (cols % 32 == 0) is stored as ceil(rows/64)
  * tiles of 64 rows. With G = cols/32 groups and G4 = ceil(G/4), tile t is G4
- * quad blocks of 4352 bytes. For the row r = 16m + i (m = 0..3, i = 0..15)
- * of tile t and the group g = 4q + j (j = 0..3) of quad block q, with
- * lane = i + 16j:
- *   bytes [1024*m + 16*lane, +16)  the 16 canonical bytes (32 codes) of
- *                                  row 64t + r, group g;
- *   byte  4096 + 4*lane + m        the exponent byte of that group.
- * Groups past G and rows past `rows` are zero codes with exponent byte 0.
- * Each 1 KiB sub-block m is the A operand of one gfx950 block-scaled FP4
- * matrix instruction (16 rows x 128 columns, each lane one 32-code group
- * with its exponent as the lane's scale), so the kernels multiply the
- * packed bytes as they are, and a wave's 16-byte loads are contiguous KiBs.
- * Tile size 4352*G4 bytes (no padding when G % 4 == 0). Groups of 32 are 16
- * packed bytes ([SAT] "Reduction one"), which is what makes a group one
- * 128-bit load.
+ * quad blocks of 4352 bytes; quad block q of tile t holds, for l = 0..63:
+ *   bytes [1024*b + 16*l, +16)  the 16 canonical bytes (32 codes) of group
+ *                               g = 4q+b of row 64t + l (zero for g >= G);
+ *   byte  4096 + 4*l + b        the exponent byte of that group (0 for
+ *                               g >= G).
+ * so lane l of a wave reads its row's group g with one 16-byte load, the
+ * wave's 64 loads are one contiguous KiB, and a wave walking a row range
+ * reads one contiguous stream. Rows past `rows` are zero codes with exponent
+ * byte 0. Tile size 4352*G4 bytes (no padding when G % 4 == 0). Groups of 32
+ * are 16 packed bytes ([SAT] "Reduction one"), which is what makes a group
+ * one 128-bit load.
  * ---------------------------------------------------------------------- */
 size_t k3_mxfp4_packed_bytes(int rows, int cols);
 /* Host re-tiling; tiles must hold k3_mxfp4_packed_bytes(rows, cols). */
@@ -124,27 +121,22 @@ k3_status k3_expert_pack(const uint8_t *gate_nib_d, const uint8_t *gate_sc_d,
 
 /* ------------------------------------------------------------------------
  * y[rows] = W[rows][cols] . x[cols] read straight from the packed bytes,
- * never expanded to floats ([SAT] "Reduction one"). The product runs on the
- * gfx950 block-scaled FP4 matrix instruction: the packed tiles are its FP4
- * operand with the group exponents as its scales, and x is split into five
- * fixed-point E4M3 pieces (per-32 exponents; residual below 2^-24 of each
- * 32-block's largest |x|) as its other operand, built in LDS by every
- * workgroup. Exponent 255 contributes nothing. fp32 accumulation in a fixed
- * order: each row is reduced by one workgroup along a fixed tree, so results
- * are bit-identical from run to run on one device (the pages' fixed-order
- * rule, [SAT] "A floating-point contract, not a convention"). Calls whose x
- * holds Inf or NaN take a vector-ALU path that multiplies group by group.
- * x fp32 [cols], tiles from k3_mxfp4_pack, y fp32 [rows]; cols <=
- * K3_MAX_COLS (the fragments of x must fit in LDS). No workspace.
+ * never expanded to floats in memory ([SAT] "Reduction one"): the codes of a
+ * group are converted in registers, multiplied by x with fp32 accumulation,
+ * and the group's exponent is applied once to the group's sum; exponent 255
+ * contributes nothing. fp32 accumulation in a fixed order: each row is
+ * reduced by one workgroup along a fixed tree, so results are bit-identical
+ * from run to run on one device (the pages' fixed-order rule, [SAT] "A
+ * floating-point contract, not a convention"). x fp32 [cols], tiles from
+ * k3_mxfp4_pack, y fp32 [rows]. No workspace.
  * ---------------------------------------------------------------------- */
-#define K3_MAX_COLS 16384
 k3_status k3_mxfp4_gemv(const float *x, const uint8_t *tiles, int rows,
                         int cols, float *y, k3_stream_t stream);
 
 /* One routed expert, SwiGLU: g = W_gate x, u = W_up x, h = SiLU(g) * u
  * (fp32, not rounded to bf16), y = W_down h. x bf16 [hidden]; expert from
  * k3_expert_pack; y fp32 [hidden]; h fp32 [inter] receives h. Same product
- * as k3_mxfp4_gemv (x and h split into pieces in LDS). */
+ * as k3_mxfp4_gemv. */
 k3_status k3_expert_swiglu(const uint16_t *x, const uint8_t *expert,
                            int hidden, int inter, float *y, float *h,
                            k3_stream_t stream);

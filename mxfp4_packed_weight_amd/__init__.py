@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libk3moe.so")
 _lib = None
 
 K3_OK, K3_ERR_ARG, K3_ERR_CONFIG, K3_ERR_MEMORY, K3_ERR_DEVICE = 0, 1, 2, 3, 4
-K3_MAX_EXPERTS, K3_MAX_TOPK, K3_MAX_COLS = 4096, 64, 16384
+K3_MAX_EXPERTS, K3_MAX_TOPK = 4096, 64
 
 # (name, restype, argtypes) of every exported symbol in include/k3moe.h
 _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t

@@ -253,15 +253,6 @@ static k3_status need_ws(const char *fn, size_t have, size_t need) {
   return K3_OK;
 }
 
-static k3_status check_frag_lds(const char *fn, const char *what, int len) {
-  const size_t need = act_frag_bytes(len), have = max_dynamic_lds();
-  K3_NEED(fn, need <= have,
-          "%s: %s=%d needs %zu bytes of LDS for its activation fragments; "
-          "this device allows %zu",
-          fn, what, len, need, have);
-  return K3_OK;
-}
-
 k3_status k3_mxfp4_gemv(const float *x, const uint8_t *tiles, int rows,
                         int cols, float *y, k3_stream_t stream) {
   const char *fn = "k3_mxfp4_gemv";
@@ -269,20 +260,7 @@ k3_status k3_mxfp4_gemv(const float *x, const uint8_t *tiles, int rows,
   K3_NEED_PTR(fn, tiles);
   K3_NEED_PTR(fn, y);
   if (k3_status s = check_mat(fn, rows, cols)) return s;
-  K3_NEED(fn, cols <= K3_MAX_COLS, "%s: cols=%d above K3_MAX_COLS=%d", fn, cols,
-          K3_MAX_COLS);
-  if (k3_status s = check_frag_lds(fn, "cols", cols)) return s;
   K3_LAUNCH(fn, launch_gemv_f32(x, tiles, rows, cols, y, stream));
-  return K3_OK;
-}
-
-static k3_status check_expert_lds(const char *fn, int k, int hidden, int inter) {
-  if (k3_status s = check_frag_lds(fn, "hidden", hidden)) return s;
-  const int span = down_slots_spanned(k, hidden, inter);
-  K3_NEED(fn, (size_t)span * act_frag_bytes(inter) <= max_dynamic_lds(),
-          "%s: inter=%d with k=%d needs %zu bytes of LDS for the down "
-          "fragments; this device allows %zu",
-          fn, inter, k, (size_t)span * act_frag_bytes(inter), max_dynamic_lds());
   return K3_OK;
 }
 
@@ -295,7 +273,6 @@ k3_status k3_expert_swiglu(const uint16_t *x, const uint8_t *expert,
   K3_NEED_PTR(fn, y);
   K3_NEED_PTR(fn, h);
   if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
-  if (k3_status s = check_expert_lds(fn, 1, hidden, inter)) return s;
   K3_LAUNCH(fn, launch_gate_up(x, nullptr, nullptr, expert, 1, hidden, inter, h,
                                stream));
   K3_LAUNCH(fn, launch_down(h, nullptr, nullptr, expert, 1, hidden, inter, y,
@@ -314,7 +291,6 @@ k3_status k3_expert_gate_up(const uint16_t *x, const uint8_t *const *experts,
   K3_NEED(fn, k >= 1 && k <= K3_MAX_TOPK, "%s: k=%d outside [1, %d]", fn, k,
           K3_MAX_TOPK);
   if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
-  if (k3_status s = check_frag_lds(fn, "hidden", hidden)) return s;
   K3_LAUNCH(fn, launch_gate_up(x, experts, idx, nullptr, k, hidden, inter, h,
                                stream));
   return K3_OK;
@@ -331,7 +307,6 @@ k3_status k3_expert_down(const float *h, const uint8_t *const *experts,
   K3_NEED(fn, k >= 1 && k <= K3_MAX_TOPK, "%s: k=%d outside [1, %d]", fn, k,
           K3_MAX_TOPK);
   if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
-  if (k3_status s = check_expert_lds(fn, k, hidden, inter)) return s;
   K3_LAUNCH(fn, launch_down(h, experts, idx, nullptr, k, hidden, inter, yp,
                             stream));
   return K3_OK;
@@ -426,7 +401,6 @@ k3_status k3_moe_layer_ex(const uint16_t *x, const uint16_t *router_w,
                 fn);
   if (k3_status s = check_routing(fn, 1, n_experts, k)) return s;
   if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
-  if (k3_status s = check_expert_lds(fn, k, hidden, inter)) return s;
   const WsLayout L = ws_layout(1, n_experts, hidden, inter, k);
   if (k3_status s = need_ws(fn, ws_bytes, L.total)) return s;
   uint8_t *base = static_cast<uint8_t *>(ws);

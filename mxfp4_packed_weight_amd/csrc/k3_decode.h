@@ -68,55 +68,6 @@ __device__ __forceinline__ float group_dot_f32(const u32x4 w,
   return s;
 }
 
-// Same products with the activations in LDS (all lanes read the same
-// address: a broadcast). xs: 16 packed bf16 pairs; hs: 32 fp32 values.
-__device__ __forceinline__ float group_dot_bf16_lds(const u32x4 w,
-                                                    const uint32_t *xs) {
-  const u32x4 *xv = reinterpret_cast<const u32x4 *>(xs);
-  float s = 0.f;
-  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    // Elements go through a plain array: this compiler turns
-    // __builtin_bit_cast of an ext-vector element into a read of element 0.
-    const u32x4 xq = xv[d];
-    const uint32_t xw[4] = {xq.x, xq.y, xq.z, xq.w};
-    const bf16x2 w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], 1.0f, 0);
-    const bf16x2 w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], 1.0f, 1);
-    const bf16x2 w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], 1.0f, 2);
-    const bf16x2 w3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], 1.0f, 3);
-    s = __builtin_amdgcn_fdot2_f32_bf16(w0, __builtin_bit_cast(bf16x2, xw[0]), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(w1, __builtin_bit_cast(bf16x2, xw[1]), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(w2, __builtin_bit_cast(bf16x2, xw[2]), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(w3, __builtin_bit_cast(bf16x2, xw[3]), s, false);
-  }
-  return s;
-}
-
-__device__ __forceinline__ float group_dot_f32_lds(const u32x4 w,
-                                                   const float *hs) {
-  const u32x4 *hv = reinterpret_cast<const u32x4 *>(hs);
-  float s = 0.f;
-  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const u32x4 ha = hv[2 * d], hb = hv[2 * d + 1];
-    const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], 1.0f, 0);
-    const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], 1.0f, 1);
-    const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], 1.0f, 2);
-    const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], 1.0f, 3);
-    s = fmaf(v0.x, __uint_as_float(ha.x), s);
-    s = fmaf(v0.y, __uint_as_float(ha.y), s);
-    s = fmaf(v1.x, __uint_as_float(ha.z), s);
-    s = fmaf(v1.y, __uint_as_float(ha.w), s);
-    s = fmaf(v2.x, __uint_as_float(hb.x), s);
-    s = fmaf(v2.y, __uint_as_float(hb.y), s);
-    s = fmaf(v3.x, __uint_as_float(hb.z), s);
-    s = fmaf(v3.y, __uint_as_float(hb.w), s);
-  }
-  return s;
-}
-
 // acc += 2^(e-127) * sub, or nothing for e == 255 (select, not multiply).
 __device__ __forceinline__ float apply_scale(float acc, float sub, uint32_t e) {
   const float t = acc + ldexpf(sub, (int)e - 127);

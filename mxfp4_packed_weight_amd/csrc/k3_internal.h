@@ -1,14 +1,12 @@
 // Internal declarations of the k3moe library (gfx950 / HIP).
 //
 // Tile layout of an MXFP4 matrix (the layout the kernels read; see
-// include/k3moe.h for the byte-level definition): 64-row tiles, each a
-// sequence of G4 quad blocks (128 columns = 4 groups of 32). A quad block is
-// four 1 KiB sub-blocks, one per 16 rows, each exactly the A operand of one
-// gfx950 block-scaled FP4 MFMA (16 rows x 128 K): lane l holds the 16 packed
-// bytes of group l/16 of row l%16. The 256 bytes after them hold the four
-// exponent bytes of each lane (byte m for sub-block m), which are the MFMA's
-// A scales. Padding (groups past G, rows past the matrix) is zero codes with
-// exponent byte 0, so it contributes exactly 0 and never a NaN.
+// include/k3moe.h for the byte-level definition): 64-row tiles, each tile a
+// sequence of G4 quad blocks of 4352 bytes: [4 groups][64 lanes][16 B] of
+// packed codes then [64 lanes][4 B] of the quad's exponent bytes. One lane
+// owns one row; a wave's load of group g is one contiguous KiB, a wave walks
+// one contiguous stream, and every quad of groups is whole. Padding (groups
+// past G, rows past the matrix) is zero codes with exponent byte 0.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,15 +22,13 @@ constexpr int kGroup = 32;      // weights per exponent byte
 constexpr int kGroupBytes = 16; // packed bytes per group
 constexpr int kQuadBytes = 4352;  // 4 groups x 64 lanes x 16 B + 64 x 4 B
 
-// Byte offsets inside a tile of the codes and of the exponent byte of group
-// g of tile row r (0..63): sub-block m = r / 16, lane r % 16 + 16 * (g % 4).
+// Byte offsets inside a tile: codes of group g of tile row r (lane r), and
+// the exponent byte of group g of tile row r.
 __host__ __device__ inline size_t code_offset(int g, int r) {
-  const int lane = (r & 15) + 16 * (g & 3);
-  return (size_t)kQuadBytes * (g >> 2) + (size_t)1024 * (r >> 4) + 16 * lane;
+  return (size_t)kQuadBytes * (g >> 2) + (size_t)1024 * (g & 3) + 16 * r;
 }
 __host__ __device__ inline size_t scale_offset(int g, int r) {
-  const int lane = (r & 15) + 16 * (g & 3);
-  return (size_t)kQuadBytes * (g >> 2) + 4096 + 4 * lane + (r >> 4);
+  return (size_t)kQuadBytes * (g >> 2) + 4096 + 4 * r + (g & 3);
 }
 
 struct MatLayout {
@@ -96,15 +92,6 @@ hipError_t launch_expert_pack(const uint8_t *gn, const uint8_t *gs,
                               const uint8_t *un, const uint8_t *us,
                               const uint8_t *dn, const uint8_t *ds, int hidden,
                               int inter, uint8_t *dst, hipStream_t s);
-// Fixed-point E4M3 pieces an activation vector is split into for the FP4
-// matrix instruction (k3_mfma.h); the matrix kernels build these fragments
-// in LDS themselves (act_frag_bytes(len) bytes for a vector of len).
-constexpr int kPieces = 5;
-size_t act_frag_bytes(int len);
-// Dynamic LDS a matrix kernel may take for fragments on this device.
-size_t max_dynamic_lds();
-// Expert slots one down-kernel workgroup's tile range can touch.
-int down_slots_spanned(int nslots, int hidden, int inter);
 hipError_t launch_gemv_f32(const float *x, const uint8_t *tiles, int rows,
                            int cols, float *y, hipStream_t s);
 // Gate/up + SwiGLU over `nslots` experts: slot j uses expert experts[idx[j]]

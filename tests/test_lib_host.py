@@ -60,13 +60,11 @@ def test_pack_roundtrip_and_layout(L, rows, cols):
     G, G4 = cols // 32, (cols // 32 + 3) // 4
     tb = 4352 * G4
 
-    def code_off(t, g, r):  # r: row inside the tile
-        lane = r % 16 + 16 * (g % 4)
-        return t * tb + 4352 * (g // 4) + 1024 * (r // 16) + 16 * lane
+    def code_off(t, g, r):  # r: row inside the tile = the lane that owns it
+        return t * tb + 4352 * (g // 4) + 1024 * (g % 4) + 16 * r
 
     def scale_off(t, g, r):
-        lane = r % 16 + 16 * (g % 4)
-        return t * tb + 4352 * (g // 4) + 4096 + 4 * lane + r // 16
+        return t * tb + 4352 * (g // 4) + 4096 + 4 * r + g % 4
 
     rng = np.random.default_rng(0)
     for _ in range(50):
@@ -122,8 +120,6 @@ def test_refusals_before_launch(L):
     assert rc == K.K3_ERR_CONFIG and "cols=48" in K.last_error()
     rc = L.k3_mxfp4_gemv(_fake(3), _fake(1), 0, 64, _fake(2), s)
     assert rc == K.K3_ERR_CONFIG
-    rc = L.k3_mxfp4_gemv(_fake(3), _fake(1), 64, K.K3_MAX_COLS + 32, _fake(2), s)
-    assert rc == K.K3_ERR_CONFIG and "K3_MAX_COLS" in K.last_error()
     rc = L.k3_router_topk(_fake(1), None, 1, 896, 17 + 64, _fake(2), _fake(3), s)
     assert rc == K.K3_ERR_CONFIG and "k=81" in K.last_error()
     rc = L.k3_router_topk(_fake(1), None, 1, 8, 9, _fake(2), _fake(3), s)
