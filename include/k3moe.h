@@ -211,6 +211,51 @@ k3_status k3_moe_layer_ex(const uint16_t *x, const uint16_t *router_w,
                           double *logits, void *ws, size_t ws_bytes,
                           k3_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Batched decode: T tokens, each routed to k of n_experts experts; every
+ * selected expert's packed bytes are read once for all of its tokens.
+ *
+ * k3_moe_permute: the T*k routing pairs p = t*k + j (expert idx[p], device
+ * int32 [T][k]) sorted by expert, stably in pair order (token, then slot):
+ *   counts[e]   pairs of expert e                     (device int32 [n])
+ *   offsets[e]  start of expert e's run               (device int32 [n])
+ *   pair_token[q], pair_slot[q]  token and slot of the q-th sorted pair
+ *               (device int32 [T*k]).
+ * Entries of idx outside [0, n_experts) are not placed. ws: device scratch
+ * of k3_moe_permute_workspace_bytes(T, k) bytes. 1 <= k <= K3_MAX_TOPK,
+ * T*k <= 2^20.
+ *
+ * k3_moe_layer_from_logits: for each token t, top-k of logits[t] (device
+ * fp64 [T][n_experts]; bias optional as in k3_router_topk), then
+ *   Y[t] = sum_j w[t][j] * SwiGLU_{idx[t][j]}(X[t])  in rank order j,
+ * X bf16 [T][hidden]; Y bf16 [T][hidden] (RNE) and/or Y_f32 fp32
+ * [T][hidden]; idx int32 [T][k] and w fp32 [T][k] optional outputs.
+ * k3_moe_layer_batched: the same with the logits from the router
+ * (k3_router of X against router_w bf16 [n_experts][hidden], no bias).
+ * Both take a workspace of k3_moe_batched_workspace_bytes(T, n_experts,
+ * hidden, inter, k) bytes. Each Y[t] is summed in an order fixed by the
+ * routing of the whole batch, so reruns are bit-identical.
+ * ---------------------------------------------------------------------- */
+size_t k3_moe_permute_workspace_bytes(int T, int k);
+k3_status k3_moe_permute(const int32_t *idx, int T, int k, int n_experts,
+                         int32_t *counts, int32_t *offsets, int32_t *pair_token,
+                         int32_t *pair_slot, void *ws, size_t ws_bytes,
+                         k3_stream_t stream);
+size_t k3_moe_batched_workspace_bytes(int T, int n_experts, int hidden,
+                                      int inter, int k);
+k3_status k3_moe_layer_from_logits(const uint16_t *X, const double *logits,
+                                   const float *bias,
+                                   const uint8_t *const *experts,
+                                   int n_experts, int hidden, int inter, int k,
+                                   int T, uint16_t *Y, float *Y_f32,
+                                   int32_t *idx, float *w, void *ws,
+                                   size_t ws_bytes, k3_stream_t stream);
+k3_status k3_moe_layer_batched(const uint16_t *X, const uint16_t *router_w,
+                               const uint8_t *const *experts, int n_experts,
+                               int hidden, int inter, int k, int T, uint16_t *Y,
+                               float *Y_f32, int32_t *idx, float *w, void *ws,
+                               size_t ws_bytes, k3_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

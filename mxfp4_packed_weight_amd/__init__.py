@@ -47,6 +47,13 @@ SIGNATURES = [
     ("k3_moe_layer", _i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
     ("k3_moe_layer_ex", _i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
                              _vp, _sz, _vp]),
+    ("k3_moe_permute_workspace_bytes", _sz, [_i, _i]),
+    ("k3_moe_permute", _i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    ("k3_moe_batched_workspace_bytes", _sz, [_i, _i, _i, _i, _i]),
+    ("k3_moe_layer_from_logits", _i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp,
+                                      _vp, _vp, _sz, _vp]),
+    ("k3_moe_layer_batched", _i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
+                                  _sz, _vp]),
 ]
 
 
@@ -214,4 +221,34 @@ def k3_moe_layer_ex(x, router_w, experts, n_experts, hidden, inter, k, y, ws, y_
                     idx=None, w=None, logits=None, stream=None):
     _call("k3_moe_layer_ex", _dp(x), _dp(router_w), _dp(experts), n_experts, hidden, inter,
           k, _dp(y), _dp(y_f32), _dp(idx), _dp(w), _dp(logits), _dp(ws), _nbytes(ws),
+          _stream(stream))
+
+
+# ---- batched decode -------------------------------------------------------
+
+def k3_moe_permute_workspace_bytes(T, k):
+    return lib().k3_moe_permute_workspace_bytes(T, k)
+
+
+def k3_moe_permute(idx, T, k, n_experts, counts, offsets, pair_token, pair_slot, ws,
+                   stream=None):
+    _call("k3_moe_permute", _dp(idx), T, k, n_experts, _dp(counts), _dp(offsets),
+          _dp(pair_token), _dp(pair_slot), _dp(ws), _nbytes(ws), _stream(stream))
+
+
+def k3_moe_batched_workspace_bytes(T, n_experts, hidden, inter, k):
+    return lib().k3_moe_batched_workspace_bytes(T, n_experts, hidden, inter, k)
+
+
+def k3_moe_layer_from_logits(X, logits, bias, experts, n_experts, hidden, inter, k, T, Y, ws,
+                             Y_f32=None, idx=None, w=None, stream=None):
+    _call("k3_moe_layer_from_logits", _dp(X), _dp(logits), _dp(bias), _dp(experts), n_experts,
+          hidden, inter, k, T, _dp(Y), _dp(Y_f32), _dp(idx), _dp(w), _dp(ws), _nbytes(ws),
+          _stream(stream))
+
+
+def k3_moe_layer_batched(X, router_w, experts, n_experts, hidden, inter, k, T, Y, ws,
+                         Y_f32=None, idx=None, w=None, stream=None):
+    _call("k3_moe_layer_batched", _dp(X), _dp(router_w), _dp(experts), n_experts, hidden,
+          inter, k, T, _dp(Y), _dp(Y_f32), _dp(idx), _dp(w), _dp(ws), _nbytes(ws),
           _stream(stream))

@@ -25,6 +25,7 @@ namespace {
 thread_local char g_err[512];
 
 constexpr int kMaxDim = 1 << 20;  // rows / cols / hidden / inter / T bound
+constexpr int kMaxPairs = 1 << 20;  // T*k routing pairs of a batched call
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -47,6 +48,75 @@ WsLayout ws_layout(int T, int n, int hidden, int inter, int k) {
   off += align256((size_t)T * k * hidden * sizeof(float));
   L.total = off;
   return L;
+}
+
+// Permutation scratch of T*k pairs (after the caller's counts, offsets,
+// pair_token, pair_slot): pair_pos, item_e, item_off, item_cnt, n_items, n_bad.
+struct PermWs {
+  size_t pair_pos, item_e, item_off, item_cnt, n_items, n_bad, total;
+};
+PermWs perm_ws(size_t off, long long P) {
+  PermWs W;
+  const size_t a = align256(sizeof(int32_t) * (size_t)P);
+  W.pair_pos = off;
+  W.item_e = W.pair_pos + a;
+  W.item_off = W.item_e + a;
+  W.item_cnt = W.item_off + a;
+  W.n_items = W.item_cnt + a;
+  W.n_bad = W.n_items + 256;
+  W.total = W.n_bad + 256;
+  return W;
+}
+
+// Batched layer: logits, idx, w, counts, offsets, pair_token, pair_slot,
+// the permutation scratch, h [P][inter], yp [P][hidden].
+struct BatchWs {
+  size_t logits, idx, w, counts, offsets, pair_token, pair_slot;
+  PermWs perm;
+  size_t h, yp, total;
+};
+BatchWs batch_ws(int T, int n, int hidden, int inter, int k) {
+  BatchWs B;
+  const long long P = (long long)T * k;
+  size_t off = 0;
+  B.logits = off;
+  off += align256((size_t)T * n * sizeof(double));
+  B.idx = off;
+  off += align256((size_t)P * sizeof(int32_t));
+  B.w = off;
+  off += align256((size_t)P * sizeof(float));
+  B.counts = off;
+  off += align256((size_t)n * sizeof(int32_t));
+  B.offsets = off;
+  off += align256((size_t)n * sizeof(int32_t));
+  B.pair_token = off;
+  off += align256((size_t)P * sizeof(int32_t));
+  B.pair_slot = off;
+  off += align256((size_t)P * sizeof(int32_t));
+  B.perm = perm_ws(off, P);
+  off = B.perm.total;
+  B.h = off;
+  off += align256((size_t)P * inter * sizeof(float));
+  B.yp = off;
+  off += align256((size_t)P * hidden * sizeof(float));
+  B.total = off;
+  return B;
+}
+
+PermOut perm_out(uint8_t *base, const PermWs &W, int32_t *counts,
+                 int32_t *offsets, int32_t *pair_token, int32_t *pair_slot) {
+  PermOut o;
+  o.counts = counts;
+  o.offsets = offsets;
+  o.pair_token = pair_token;
+  o.pair_slot = pair_slot;
+  o.pair_pos = reinterpret_cast<int32_t *>(base + W.pair_pos);
+  o.item_e = reinterpret_cast<int32_t *>(base + W.item_e);
+  o.item_off = reinterpret_cast<int32_t *>(base + W.item_off);
+  o.item_cnt = reinterpret_cast<int32_t *>(base + W.item_cnt);
+  o.n_items = reinterpret_cast<int32_t *>(base + W.n_items);
+  o.n_bad = reinterpret_cast<int32_t *>(base + W.n_bad);
+  return o;
 }
 
 k3_status fail(k3_status s, const char *fmt, ...) {
@@ -426,6 +496,125 @@ k3_status k3_moe_layer(const uint16_t *x, const uint16_t *router_w,
   return k3_moe_layer_ex(x, router_w, experts, n_experts, hidden, inter, k, y,
                          nullptr, nullptr, nullptr, nullptr, ws, ws_bytes,
                          stream);
+}
+
+/* ---- batched decode ---------------------------------------------------- */
+
+static k3_status check_batch(const char *fn, int T, int n, int k) {
+  if (k3_status s = check_routing(fn, T, n, k)) return s;
+  K3_NEED(fn, (long long)T * k <= kMaxPairs,
+          "%s: T*k=%lld routing pairs above %d", fn, (long long)T * k, kMaxPairs);
+  return K3_OK;
+}
+
+size_t k3_moe_permute_workspace_bytes(int T, int k) {
+  if (T < 1 || k < 1 || k > K3_MAX_TOPK || (long long)T * k > kMaxPairs) return 0;
+  return perm_ws(0, (long long)T * k).total;
+}
+
+k3_status k3_moe_permute(const int32_t *idx, int T, int k, int n_experts,
+                         int32_t *counts, int32_t *offsets, int32_t *pair_token,
+                         int32_t *pair_slot, void *ws, size_t ws_bytes,
+                         k3_stream_t stream) {
+  const char *fn = "k3_moe_permute";
+  K3_NEED_PTR(fn, idx);
+  K3_NEED_PTR(fn, counts);
+  K3_NEED_PTR(fn, offsets);
+  K3_NEED_PTR(fn, pair_token);
+  K3_NEED_PTR(fn, pair_slot);
+  K3_NEED_PTR(fn, ws);
+  K3_NEED(fn, n_experts >= 1 && n_experts <= K3_MAX_EXPERTS,
+          "%s: n_experts=%d outside [1, %d]", fn, n_experts, K3_MAX_EXPERTS);
+  K3_NEED(fn, T >= 1 && k >= 1 && k <= K3_MAX_TOPK && (long long)T * k <= kMaxPairs,
+          "%s: T=%d k=%d outside T >= 1, 1 <= k <= %d, T*k <= %d", fn, T, k,
+          K3_MAX_TOPK, kMaxPairs);
+  const PermWs W = perm_ws(0, (long long)T * k);
+  if (k3_status s = need_ws(fn, ws_bytes, W.total)) return s;
+  uint8_t *base = static_cast<uint8_t *>(ws);
+  K3_LAUNCH(fn, launch_permute(idx, T, k, n_experts,
+                               perm_out(base, W, counts, offsets, pair_token,
+                                        pair_slot),
+                               stream));
+  return K3_OK;
+}
+
+size_t k3_moe_batched_workspace_bytes(int T, int n_experts, int hidden,
+                                      int inter, int k) {
+  if (check_batch("k3_moe_batched_workspace_bytes", T, n_experts, k) != K3_OK ||
+      check_expert_dims("k3_moe_batched_workspace_bytes", hidden, inter) != K3_OK)
+    return 0;
+  return batch_ws(T, n_experts, hidden, inter, k).total;
+}
+
+static k3_status batched_common(const char *fn, const uint16_t *X,
+                                const uint16_t *router_w, const double *logits,
+                                const float *bias,
+                                const uint8_t *const *experts, int n_experts,
+                                int hidden, int inter, int k, int T,
+                                uint16_t *Y, float *Y_f32, int32_t *idx,
+                                float *w, void *ws, size_t ws_bytes,
+                                k3_stream_t stream) {
+  K3_NEED_PTR(fn, X);
+  K3_NEED_PTR(fn, experts);
+  K3_NEED_PTR(fn, ws);
+  if (!Y && !Y_f32) return fail(K3_ERR_ARG, "%s: Y and Y_f32 are both NULL", fn);
+  if ((Y && !aligned16(Y)) || (Y_f32 && !aligned16(Y_f32)) ||
+      (idx && !aligned16(idx)) || (w && !aligned16(w)) ||
+      (bias && !aligned16(bias)))
+    return fail(K3_ERR_ARG, "%s: an optional argument is not 16-byte aligned",
+                fn);
+  if (k3_status s = check_batch(fn, T, n_experts, k)) return s;
+  if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
+  const BatchWs B = batch_ws(T, n_experts, hidden, inter, k);
+  if (k3_status s = need_ws(fn, ws_bytes, B.total)) return s;
+  uint8_t *base = static_cast<uint8_t *>(ws);
+  double *lg = reinterpret_cast<double *>(base + B.logits);
+  int32_t *ix = idx ? idx : reinterpret_cast<int32_t *>(base + B.idx);
+  float *wt = w ? w : reinterpret_cast<float *>(base + B.w);
+  const PermOut o = perm_out(base, B.perm,
+                             reinterpret_cast<int32_t *>(base + B.counts),
+                             reinterpret_cast<int32_t *>(base + B.offsets),
+                             reinterpret_cast<int32_t *>(base + B.pair_token),
+                             reinterpret_cast<int32_t *>(base + B.pair_slot));
+  float *h = reinterpret_cast<float *>(base + B.h);
+  float *yp = reinterpret_cast<float *>(base + B.yp);
+  if (router_w) {
+    K3_LAUNCH(fn, launch_router(X, router_w, T, hidden, n_experts, lg, stream));
+    logits = lg;
+  }
+  K3_LAUNCH(fn, launch_topk_f64(logits, bias, T, n_experts, k, ix, wt, stream));
+  K3_LAUNCH(fn, launch_permute(ix, T, k, n_experts, o, stream));
+  K3_LAUNCH(fn, launch_gate_up_batched(X, experts, o, hidden, inter, h, stream));
+  K3_LAUNCH(fn, launch_down_batched(h, experts, o, hidden, inter, yp, stream));
+  K3_LAUNCH(fn, launch_combine_batched(yp, wt, o.pair_pos, T, k, hidden, Y,
+                                       Y_f32, stream));
+  return K3_OK;
+}
+
+k3_status k3_moe_layer_from_logits(const uint16_t *X, const double *logits,
+                                   const float *bias,
+                                   const uint8_t *const *experts,
+                                   int n_experts, int hidden, int inter, int k,
+                                   int T, uint16_t *Y, float *Y_f32,
+                                   int32_t *idx, float *w, void *ws,
+                                   size_t ws_bytes, k3_stream_t stream) {
+  const char *fn = "k3_moe_layer_from_logits";
+  K3_NEED_PTR(fn, logits);
+  return batched_common(fn, X, nullptr, logits, bias, experts, n_experts, hidden,
+                        inter, k, T, Y, Y_f32, idx, w, ws, ws_bytes, stream);
+}
+
+k3_status k3_moe_layer_batched(const uint16_t *X, const uint16_t *router_w,
+                               const uint8_t *const *experts, int n_experts,
+                               int hidden, int inter, int k, int T, uint16_t *Y,
+                               float *Y_f32, int32_t *idx, float *w, void *ws,
+                               size_t ws_bytes, k3_stream_t stream) {
+  const char *fn = "k3_moe_layer_batched";
+  K3_NEED_PTR(fn, router_w);
+  K3_NEED(fn, hidden % 8 == 0, "%s: hidden=%d must be a multiple of 8", fn, hidden);
+  return batched_common(fn, X, router_w, nullptr, nullptr, experts, n_experts,
+                        hidden, inter, k, T, Y, Y_f32, idx, w, ws, ws_bytes,
+                        stream);
 }
 
 }  // extern "C"

@@ -1,0 +1,310 @@
+// Batched decode: token->expert permutation, per-expert grouped GEMVs that
+// read each selected expert's packed bytes once for all of its tokens, and
+// the per-token weighted combine.
+//
+// The T*k routing pairs (t, j) are sorted by expert, stably by pair index
+// (token, then slot), so every expert's tokens form one contiguous run. A
+// run is cut into work items of at most kTokBatch tokens; the grouped
+// kernels stream an item's expert tiles exactly like the single-token
+// kernels and multiply every decoded group by each of the item's tokens.
+#include "k3_stream.h"
+
+namespace k3 {
+
+namespace {
+
+constexpr int kThreads = kNW * 64;
+constexpr int kTokBatch = 4;   // tokens per work item (accumulators per lane)
+constexpr int kBatchTPW = 2;   // tiles per chunk of the grouped kernels
+constexpr int kPermThreads = 1024;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+__device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
+
+// Inclusive prefix sum over the block's 1024 threads (wave scans + LDS).
+__device__ int block_scan_incl(int v, int *tmp) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d);
+    if (lane >= d) v += u;
+  }
+  if (lane == 63) tmp[w] = v;
+  __syncthreads();
+  if (w == 0) {
+    int s = lane < kPermThreads / 64 ? tmp[lane] : 0;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int u = __shfl_up(s, d);
+      if (lane >= d) s += u;
+    }
+    if (lane < kPermThreads / 64) tmp[lane] = s;
+  }
+  __syncthreads();
+  const int r = v + (w > 0 ? tmp[w - 1] : 0);
+  __syncthreads();
+  return r;
+}
+
+// One workgroup. Pairs p = t*k + j with expert idx[p]; entries outside
+// [0, n) are not placed (they are counted in *n_bad).
+//   counts[e], offsets[e]        run length and start of expert e
+//   pair_token[q], pair_slot[q]  the q-th pair in (expert, pair index) order
+//   pair_pos[p]                  q of pair p (-1 when not placed)
+//   items: item_e/off/cnt[i]     expert, first q, tokens (<= kTokBatch)
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(
+    const int32_t *__restrict__ idx, int T, int k, int n,
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ pair_token, int32_t *__restrict__ pair_slot,
+    int32_t *__restrict__ pair_pos, int32_t *__restrict__ item_e,
+    int32_t *__restrict__ item_off, int32_t *__restrict__ item_cnt,
+    int32_t *__restrict__ n_items, int32_t *__restrict__ n_bad) {
+  __shared__ int cnt[K3_MAX_EXPERTS];
+  __shared__ int start[K3_MAX_EXPERTS];  // offsets, then running fill base
+  __shared__ int chunk_e[kPermThreads];
+  __shared__ int tmp[kPermThreads / 64];
+  __shared__ int bad;
+  const int tid = threadIdx.x;
+  const int P = T * k;
+  for (int e = tid; e < n; e += kPermThreads) cnt[e] = 0;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += kPermThreads) {
+    const int e = idx[p];
+    if (e >= 0 && e < n)
+      atomicAdd(&cnt[e], 1);
+    else
+      atomicAdd(&bad, 1);
+  }
+  __syncthreads();
+  // exclusive scan of cnt over experts: each thread owns a contiguous span
+  const int per = (n + kPermThreads - 1) / kPermThreads;
+  const int e0 = min(n, tid * per), e1 = min(n, e0 + per);
+  int local = 0;
+  for (int e = e0; e < e1; ++e) local += cnt[e];
+  int run = block_scan_incl(local, tmp) - local;
+  for (int e = e0; e < e1; ++e) {
+    start[e] = run;
+    counts[e] = cnt[e];
+    offsets[e] = run;
+    run += cnt[e];
+  }
+  __syncthreads();
+  // stable placement, kPermThreads pairs at a time: rank = earlier pairs of
+  // the same expert in this chunk + pairs of that expert in earlier chunks
+  for (int c = 0; c < P; c += kPermThreads) {
+    const int p = c + tid;
+    const int e = p < P ? idx[p] : -1;
+    const bool ok = e >= 0 && e < n;
+    chunk_e[tid] = ok ? e : -1;
+    __syncthreads();
+    if (ok) {
+      int r = 0;
+      for (int i = 0; i < tid; ++i) r += chunk_e[i] == e;
+      const int q = start[e] + r;
+      pair_token[q] = p / k;
+      pair_slot[q] = p % k;
+      pair_pos[p] = q;
+    } else if (p < P) {
+      pair_pos[p] = -1;
+    }
+    __syncthreads();
+    // advance each expert's base by its pairs in this chunk (one writer)
+    if (ok) {
+      bool last = true;
+      for (int i = tid + 1; i < kPermThreads; ++i)
+        if (chunk_e[i] == e) {
+          last = false;
+          break;
+        }
+      if (last) {
+        int r = 0;
+        for (int i = 0; i <= tid; ++i) r += chunk_e[i] == e;
+        start[e] += r;
+      }
+    }
+    __syncthreads();
+  }
+  // work items: ceil(cnt/kTokBatch) per expert, in expert order
+  int li = 0;
+  for (int e = e0; e < e1; ++e) li += (cnt[e] + kTokBatch - 1) / kTokBatch;
+  int ibase = block_scan_incl(li, tmp) - li;
+  for (int e = e0; e < e1; ++e) {
+    const int off = offsets[e];
+    for (int s = 0; s < cnt[e]; s += kTokBatch) {
+      item_e[ibase] = e;
+      item_off[ibase] = off + s;
+      item_cnt[ibase] = min(kTokBatch, cnt[e] - s);
+      ++ibase;
+    }
+  }
+  if (tid == kPermThreads - 1) *n_items = ibase;
+  if (tid == 0) *n_bad = bad;
+}
+
+struct Items {
+  const int32_t *e, *off, *cnt, *n;
+};
+
+// Routing data of the tile being multiplied, refreshed when the tile
+// changes: the item's first sorted pair, its token count and one activation
+// row pointer per token (all wave-uniform, read with scalar loads).
+template <typename A>
+struct TileRows {
+  int t = -1, off = 0, cnt = 0;
+  const A *row[kTokBatch];
+};
+
+// h[q][inter] = SiLU(gate . x_tok) * (up . x_tok) for every placed pair q,
+// tok = pair_token[q]; tiles: item i's gate/up tile s is virtual tile
+// i*T + s.
+__global__ __launch_bounds__(kThreads) void gate_up_batched_kernel(
+    const uint16_t *__restrict__ X, const uint8_t *const *__restrict__ experts,
+    Items it, const int32_t *__restrict__ pair_token, int hidden, int inter,
+    float *__restrict__ h) {
+  __shared__ float part[kBatchTPW * kNW * 64 * kTokBatch];
+  const ExpertLayout L = expert_layout(hidden, inter);
+  const int T = L.gu.ntiles;
+  const int total = ldc(it.n) * T;
+  int t0, t1;
+  wg_range(total, &t0, &t1);
+  const uint32_t *Xw = reinterpret_cast<const uint32_t *>(X);
+  const int xrow = hidden / 2;  // uint32 words per token row
+  TileRows<uint32_t> cr;        // consumer side
+  auto rows = [&](int t) {
+    if (t == cr.t) return;
+    cr.t = t;
+    const int i = t / T;
+    cr.off = ldc(it.off + i);
+    cr.cnt = ldc(it.cnt + i);
+#pragma unroll
+    for (int v = 0; v < kTokBatch; ++v) {
+      const int tok = v < cr.cnt ? ldc(pair_token + cr.off + v) : 0;
+      cr.row[v] = Xw + (size_t)tok * xrow;
+    }
+  };
+  run_rows_n<kTokBatch, kBatchTPW>(
+      t0, t1, L.gu.G, L.gu.G4,
+      [&](int t) {
+        return ldc(experts + ldc(it.e + t / T)) + (size_t)(t % T) * L.gu.tile_bytes;
+      },
+      [&](int t) { return ldc(it.cnt + t / T); },
+      [&](u32x4 w, int g, int t, int v) {
+        rows(t);
+        return group_dot_bf16(w, cr.row[v] + (size_t)16 * g);
+      },
+      [&](int t, int v, int lane, float s) {
+        const float u = __shfl_down(s, 32);  // lane l<32: gate row; l+32: up row
+        int is_up, row;
+        gu_lane_row(t % T, lane, &is_up, &row);
+        const int q = ldc(it.off + t / T) + v;
+        if (lane < 32 && row < inter) h[(size_t)q * inter + row] = silu(s) * u;
+      },
+      part);
+}
+
+// yp[q][hidden] = W_down(e) h[q] for every placed pair q of expert e.
+__global__ __launch_bounds__(kThreads) void down_batched_kernel(
+    const float *__restrict__ h, const uint8_t *const *__restrict__ experts,
+    Items it, int hidden, int inter, float *__restrict__ yp) {
+  __shared__ float part[kBatchTPW * kNW * 64 * kTokBatch];
+  const ExpertLayout L = expert_layout(hidden, inter);
+  const int T = L.down.ntiles;
+  const int total = ldc(it.n) * T;
+  int t0, t1;
+  wg_range(total, &t0, &t1);
+  int ct = -1;
+  size_t coff = 0;  // first sorted pair of the consumer's tile
+  run_rows_n<kTokBatch, kBatchTPW>(
+      t0, t1, L.down.G, L.down.G4,
+      [&](int t) {
+        return ldc(experts + ldc(it.e + t / T)) + L.down_offset +
+               (size_t)(t % T) * L.down.tile_bytes;
+      },
+      [&](int t) { return ldc(it.cnt + t / T); },
+      [&](u32x4 w, int g, int t, int v) {
+        if (t != ct) {
+          ct = t;
+          coff = (size_t)ldc(it.off + t / T);
+        }
+        return group_dot_f32(w, h + (coff + v) * inter + (size_t)32 * g);
+      },
+      [&](int t, int v, int lane, float s) {
+        const int row = (t % T) * kTileRows + lane;
+        const size_t q = (size_t)ldc(it.off + t / T) + v;
+        if (row < hidden) yp[q * hidden + row] = s;
+      },
+      part);
+}
+
+// Y[t][i] = sum_j w[t][j] * yp[pair_pos[t*k + j]][i] in rank order j, fp32,
+// then bf16 (RNE).
+__global__ __launch_bounds__(256) void combine_batched_kernel(
+    const float *__restrict__ yp, const float *__restrict__ w,
+    const int32_t *__restrict__ pair_pos, int k, int hidden,
+    uint16_t *__restrict__ Y, float *__restrict__ Y32) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int t = blockIdx.y;
+  if (i >= hidden) return;
+  float acc = 0.f;
+  for (int j0 = 0; j0 < k; j0 += 16) {  // issue a batch of loads, then add
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      v[j] = j0 + j < k
+                 ? yp[(size_t)pair_pos[(size_t)t * k + j0 + j] * hidden + i]
+                 : 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j0 + j < k) acc = fmaf(w[(size_t)t * k + j0 + j], v[j], acc);
+  }
+  if (Y32) Y32[(size_t)t * hidden + i] = acc;
+  if (Y) Y[(size_t)t * hidden + i] = f32_to_bf16_rne(acc);
+}
+
+unsigned persistent_grid() { return (unsigned)num_cus(); }
+
+}  // namespace
+
+int tok_batch() { return kTokBatch; }
+
+hipError_t launch_permute(const int32_t *idx, int T, int k, int n,
+                          const PermOut &o, hipStream_t s) {
+  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, s, idx, T,
+                     k, n, o.counts, o.offsets, o.pair_token, o.pair_slot,
+                     o.pair_pos, o.item_e, o.item_off, o.item_cnt, o.n_items,
+                     o.n_bad);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_up_batched(const uint16_t *X,
+                                  const uint8_t *const *experts,
+                                  const PermOut &o, int hidden, int inter,
+                                  float *h, hipStream_t s) {
+  const Items it{o.item_e, o.item_off, o.item_cnt, o.n_items};
+  hipLaunchKernelGGL(gate_up_batched_kernel, dim3(persistent_grid()),
+                     dim3(kThreads), 0, s, X, experts, it, o.pair_token,
+                     hidden, inter, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_batched(const float *h, const uint8_t *const *experts,
+                               const PermOut &o, int hidden, int inter,
+                               float *yp, hipStream_t s) {
+  const Items it{o.item_e, o.item_off, o.item_cnt, o.n_items};
+  hipLaunchKernelGGL(down_batched_kernel, dim3(persistent_grid()),
+                     dim3(kThreads), 0, s, h, experts, it, hidden, inter, yp);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_batched(const float *yp, const float *w,
+                                  const int32_t *pair_pos, int T, int k,
+                                  int hidden, uint16_t *Y, float *Y32,
+                                  hipStream_t s) {
+  hipLaunchKernelGGL(combine_batched_kernel, dim3((hidden + 255) / 256, T),
+                     dim3(256), 0, s, yp, w, pair_pos, k, hidden, Y, Y32);
+  return hipGetLastError();
+}
+
+}  // namespace k3

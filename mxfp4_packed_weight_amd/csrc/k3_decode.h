@@ -26,9 +26,16 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Activation groups are wave-uniform and never written by the kernels that
+// read them, so they are read through the constant address space: scalar
+// loads into SGPRs that every VALU instruction can take as an operand.
+typedef __attribute__((address_space(4))) const uint32_t cu32_t;
+typedef __attribute__((address_space(4))) const float cf32_t;
+
 // sum_{i<32} E2M1(code_i) * x_i for x bf16 (16 packed pairs at xg).
 __device__ __forceinline__ float group_dot_bf16(const u32x4 w,
-                                                const uint32_t *__restrict__ xg) {
+                                                const uint32_t *xg) {
+  const cu32_t *xc = (const cu32_t *)xg;
   float s = 0.f;
   const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -37,17 +44,17 @@ __device__ __forceinline__ float group_dot_bf16(const u32x4 w,
     const bf16x2 w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], 1.0f, 1);
     const bf16x2 w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], 1.0f, 2);
     const bf16x2 w3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], 1.0f, 3);
-    s = __builtin_amdgcn_fdot2_f32_bf16(w0, __builtin_bit_cast(bf16x2, xg[4 * d + 0]), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(w1, __builtin_bit_cast(bf16x2, xg[4 * d + 1]), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(w2, __builtin_bit_cast(bf16x2, xg[4 * d + 2]), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(w3, __builtin_bit_cast(bf16x2, xg[4 * d + 3]), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(w0, __builtin_bit_cast(bf16x2, xc[4 * d + 0]), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(w1, __builtin_bit_cast(bf16x2, xc[4 * d + 1]), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(w2, __builtin_bit_cast(bf16x2, xc[4 * d + 2]), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(w3, __builtin_bit_cast(bf16x2, xc[4 * d + 3]), s, false);
   }
   return s;
 }
 
 // sum_{i<32} E2M1(code_i) * x_i for x fp32 (32 values at xg).
-__device__ __forceinline__ float group_dot_f32(const u32x4 w,
-                                               const float *__restrict__ xg) {
+__device__ __forceinline__ float group_dot_f32(const u32x4 w, const float *xg) {
+  const cf32_t *xc = (const cf32_t *)xg;
   float s = 0.f;
   const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -56,14 +63,14 @@ __device__ __forceinline__ float group_dot_f32(const u32x4 w,
     const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], 1.0f, 1);
     const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], 1.0f, 2);
     const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], 1.0f, 3);
-    s = fmaf(v0.x, xg[8 * d + 0], s);
-    s = fmaf(v0.y, xg[8 * d + 1], s);
-    s = fmaf(v1.x, xg[8 * d + 2], s);
-    s = fmaf(v1.y, xg[8 * d + 3], s);
-    s = fmaf(v2.x, xg[8 * d + 4], s);
-    s = fmaf(v2.y, xg[8 * d + 5], s);
-    s = fmaf(v3.x, xg[8 * d + 6], s);
-    s = fmaf(v3.y, xg[8 * d + 7], s);
+    s = fmaf(v0.x, xc[8 * d + 0], s);
+    s = fmaf(v0.y, xc[8 * d + 1], s);
+    s = fmaf(v1.x, xc[8 * d + 2], s);
+    s = fmaf(v1.y, xc[8 * d + 3], s);
+    s = fmaf(v2.x, xc[8 * d + 4], s);
+    s = fmaf(v2.y, xc[8 * d + 5], s);
+    s = fmaf(v3.x, xc[8 * d + 6], s);
+    s = fmaf(v3.y, xc[8 * d + 7], s);
   }
   return s;
 }
@@ -78,6 +85,14 @@ __device__ __forceinline__ float apply_scale(float acc, float sub, uint32_t e) {
 // memory (e.g. an expert table) compile to global_load rather than flat_load.
 typedef __attribute__((address_space(1))) const u32x4 gu4_t;
 typedef __attribute__((address_space(1))) const uint32_t gu32_t;
+
+// Wave-uniform read of data the kernel never writes, through the constant
+// address space: a scalar load (counted by lgkmcnt), so it never makes the
+// weight stream's vector-load waits conservative.
+template <typename T>
+__device__ __forceinline__ T ldc(const T *p) {
+  return *(const __attribute__((address_space(4))) T *)p;
+}
 
 #ifndef K3_NW
 #define K3_NW 16

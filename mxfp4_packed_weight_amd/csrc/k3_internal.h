@@ -104,6 +104,27 @@ hipError_t launch_gate_up(const uint16_t *x, const uint8_t *const *experts,
 hipError_t launch_down(const float *h, const uint8_t *const *experts,
                        const int32_t *idx, const uint8_t *single, int nslots,
                        int hidden, int inter, float *yp, hipStream_t s);
+// Batched decode (k3_batched.hip). Permutation outputs, all device arrays:
+// counts/offsets [n], pair_token/pair_slot/pair_pos and the work items
+// item_e/item_off/item_cnt [T*k], n_items and n_bad [1].
+struct PermOut {
+  int32_t *counts, *offsets, *pair_token, *pair_slot, *pair_pos;
+  int32_t *item_e, *item_off, *item_cnt, *n_items, *n_bad;
+};
+int tok_batch();
+hipError_t launch_permute(const int32_t *idx, int T, int k, int n,
+                          const PermOut &o, hipStream_t s);
+hipError_t launch_gate_up_batched(const uint16_t *X,
+                                  const uint8_t *const *experts,
+                                  const PermOut &o, int hidden, int inter,
+                                  float *h, hipStream_t s);
+hipError_t launch_down_batched(const float *h, const uint8_t *const *experts,
+                               const PermOut &o, int hidden, int inter,
+                               float *yp, hipStream_t s);
+hipError_t launch_combine_batched(const float *yp, const float *w,
+                                  const int32_t *pair_pos, int T, int k,
+                                  int hidden, uint16_t *Y, float *Y32,
+                                  hipStream_t s);
 hipError_t launch_combine(const float *yp, const float *w, int k, int hidden,
                           uint16_t *y, float *y_f32, hipStream_t s);
 hipError_t launch_router(const uint16_t *x, const uint16_t *R, int T,

@@ -36,26 +36,30 @@ namespace k3 {
 #define K3_RING_DEPTH 2
 #endif
 constexpr int kRingDepth = K3_RING_DEPTH;
-constexpr int kPartFloats = kMaxTPW * kNW * 64;  // per-wave row partials
+constexpr int kPartFloats = kMaxTPW * kNW * 64;  // per-wave row partials, one vector
 
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left free (gfx9
 // encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-// Streams tiles [t_begin, t_end) of one matrix stack.
-//   base(t)          -> const uint8_t*  tile t's packed bytes (wave-uniform)
-//   dot(w, g, t)     -> float  unscaled dot of this lane's 16 code bytes w
-//                               (group g of its row of tile t) with the
-//                               activations of group g (g < G, uniform)
-//   epi(t, lane, s)  finished sum of row `lane` of tile t
-// `part` is the caller's LDS array of kPartFloats floats.
-template <class Base, class Dot, class Epi>
-__device__ __forceinline__ void run_rows(int t_begin, int t_end, int G, int G4,
-                                         Base base, Dot dot, Epi epi,
-                                         float *part) {
+// Streams tiles [t_begin, t_end) of one matrix stack with NA activation
+// vectors per tile (NA = 1 for one token; the batched kernels multiply each
+// decoded group by up to NA tokens), MaxTPW tiles per chunk.
+//   base(t)               -> const uint8_t*  tile t's packed bytes (uniform)
+//   na(t)                 -> int  vectors tile t uses (1..NA, uniform)
+//   dot(w, g, t, a)       -> float  unscaled dot of this lane's 16 code bytes
+//                            w (group g of its row of tile t) with group g of
+//                            activation vector a (g < G, a < na(t), uniform)
+//   epi(t, a, lane, s)    finished sum of row `lane` of tile t for vector a
+// `part` is the caller's LDS array of MaxTPW * kNW * 64 * NA floats.
+template <int NA, int MaxTPW, class Base, class Na, class Dot, class Epi>
+__device__ __forceinline__ void run_rows_n(int t_begin, int t_end, int G,
+                                           int G4, Base base, Na na, Dot dot,
+                                           Epi epi, float *part) {
   if (t_begin >= t_end) return;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
+  auto slot = [&](int tl, int w, int a) { return ((tl * kNW + w) * NA + a) * 64; };
 
   // chunk state: tiles [c0, c0 + ntl), this wave's items [i0, i0 + nitems)
   int c0 = t_begin, ntl = 0, i0 = 0, nitems = 0;
@@ -65,8 +69,10 @@ __device__ __forceinline__ void run_rows(int t_begin, int t_end, int G, int G4,
   uint32_t asc[kRingDepth];
   auto setup = [&](int c) {
     c0 = c;
-    ntl = min(kMaxTPW, t_end - c0);
-    for (int tl = 0; tl < ntl; ++tl) part[(tl * kNW + wave) * 64 + lane] = 0.f;
+    ntl = min(MaxTPW, t_end - c0);
+    for (int tl = 0; tl < ntl; ++tl)
+#pragma unroll
+      for (int v = 0; v < NA; ++v) part[slot(tl, wave, v) + lane] = 0.f;
     const int n = ntl * G4;
     i0 = wave * n / kNW;
     nitems = (wave + 1) * n / kNW - i0;
@@ -101,23 +107,34 @@ __device__ __forceinline__ void run_rows(int t_begin, int t_end, int G, int G4,
   // Consumes the chunk whose prologue is in flight, then hands out its rows.
   auto stream_chunk = [&]() {
     int ktl = i0 / G4, kq = i0 % G4;  // next item to consume
-    int cur = ktl;                    // tile the accumulator belongs to
-    float acc = 0.f;
+    int cur = ktl;                    // tile the accumulators belong to
+    int cna = nitems > 0 ? na(c0 + ktl) : 0;
+    float acc[NA];
+#pragma unroll
+    for (int v = 0; v < NA; ++v) acc[v] = 0.f;
     auto flush = [&]() {
-      part[(cur * kNW + wave) * 64 + lane] = acc;
-      acc = 0.f;
+#pragma unroll
+      for (int v = 0; v < NA; ++v) {
+        part[slot(cur, wave, v) + lane] = acc[v];
+        acc[v] = 0.f;
+      }
     };
     auto consume = [&](int d) {
       if (ktl != cur) {
         flush();
         cur = ktl;
+        cna = na(c0 + ktl);
       }
       const uint32_t e = asc[d];
       const int g0 = 4 * kq;
 #pragma unroll
       for (int b = 0; b < 4; ++b)
-        if (g0 + b < G)
-          acc = apply_scale(acc, dot(a[d][b], g0 + b, c0 + ktl), (e >> (8 * b)) & 255u);
+        if (g0 + b < G) {
+          const uint32_t eb = (e >> (8 * b)) & 255u;
+#pragma unroll
+          for (int v = 0; v < NA; ++v)
+            if (v < cna) acc[v] = apply_scale(acc[v], dot(a[d][b], g0 + b, c0 + ktl, v), eb);
+        }
       if (++kq == G4) {
         kq = 0;
         ++ktl;
@@ -148,10 +165,15 @@ __device__ __forceinline__ void run_rows(int t_begin, int t_end, int G, int G4,
     if (nitems > 0) flush();
     __syncthreads();
     for (int tl = wave; tl < ntl; tl += kNW) {
-      float sum = 0.f;
+      const int nv = na(c0 + tl);
 #pragma unroll
-      for (int w = 0; w < kNW; ++w) sum += part[(tl * kNW + w) * 64 + lane];
-      epi(c0 + tl, lane, sum);
+      for (int v = 0; v < NA; ++v) {
+        if (v >= nv) break;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) sum += part[slot(tl, w, v) + lane];
+        epi(c0 + tl, v, lane, sum);
+      }
     }
     __syncthreads();
   };
@@ -163,9 +185,21 @@ __device__ __forceinline__ void run_rows(int t_begin, int t_end, int G, int G4,
     // bytes anyway): the loop's own waits then count only its own loads.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     stream_chunk();
-    if (c0 + kMaxTPW >= t_end) break;
-    setup(c0 + kMaxTPW);
+    if (c0 + MaxTPW >= t_end) break;
+    setup(c0 + MaxTPW);
   }
+}
+
+// One activation vector per tile: the single-token kernels.
+//   dot(w, g, t) -> float,  epi(t, lane, s)
+template <class Base, class Dot, class Epi>
+__device__ __forceinline__ void run_rows(int t_begin, int t_end, int G, int G4,
+                                         Base base, Dot dot, Epi epi,
+                                         float *part) {
+  run_rows_n<1, kMaxTPW>(
+      t_begin, t_end, G, G4, base, [](int) { return 1; },
+      [&](u32x4 w, int g, int t, int) { return dot(w, g, t); },
+      [&](int t, int, int lane, float s) { epi(t, lane, s); }, part);
 }
 
 }  // namespace k3
