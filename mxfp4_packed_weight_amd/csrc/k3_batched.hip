@@ -62,9 +62,10 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     int32_t *__restrict__ n_items, int32_t *__restrict__ n_bad) {
   __shared__ int cnt[K3_MAX_EXPERTS];
   __shared__ int start[K3_MAX_EXPERTS];  // offsets, then running fill base
+  __shared__ unsigned long long mask[K3_MAX_EXPERTS];
   __shared__ int chunk_e[kPermThreads];
   __shared__ int tmp[kPermThreads / 64];
-  __shared__ int bad;
+  __shared__ int bad, chunk_slow;
   const int tid = threadIdx.x;
   const int P = T * k;
   for (int e = tid; e < n; e += kPermThreads) cnt[e] = 0;
@@ -91,40 +92,73 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     run += cnt[e];
   }
   __syncthreads();
-  // stable placement, kPermThreads pairs at a time: rank = earlier pairs of
-  // the same expert in this chunk + pairs of that expert in earlier chunks
-  for (int c = 0; c < P; c += kPermThreads) {
-    const int p = c + tid;
-    const int e = p < P ? idx[p] : -1;
-    const bool ok = e >= 0 && e < n;
-    chunk_e[tid] = ok ? e : -1;
+  // Stable placement, 64 tokens at a time. Fast path: bit t of mask[e] says
+  // token t0+t chose e, so a pair's rank among its expert's pairs is start[e]
+  // plus the chosen bits below its token. A token that names an expert twice
+  // (never the case for top-k output) or an entry outside [0, n) sends the
+  // chunk to the exact path, which counts earlier equal entries one by one.
+  for (int t0 = 0; t0 < T; t0 += 64) {
+    const int tn = min(64, T - t0);
+    const int c = t0 * k, cP = tn * k;  // this chunk's pairs [c, c + cP)
+    for (int e = tid; e < n; e += kPermThreads) mask[e] = 0ull;
+    if (tid == 0) chunk_slow = 0;
     __syncthreads();
-    if (ok) {
-      int r = 0;
-      for (int i = 0; i < tid; ++i) r += chunk_e[i] == e;
-      const int q = start[e] + r;
-      pair_token[q] = p / k;
-      pair_slot[q] = p % k;
-      pair_pos[p] = q;
-    } else if (p < P) {
-      pair_pos[p] = -1;
-    }
-    __syncthreads();
-    // advance each expert's base by its pairs in this chunk (one writer)
-    if (ok) {
-      bool last = true;
-      for (int i = tid + 1; i < kPermThreads; ++i)
-        if (chunk_e[i] == e) {
-          last = false;
-          break;
-        }
-      if (last) {
-        int r = 0;
-        for (int i = 0; i <= tid; ++i) r += chunk_e[i] == e;
-        start[e] += r;
+    for (int i = tid; i < cP; i += kPermThreads) {
+      const int e = idx[c + i];
+      if (e >= 0 && e < n) {
+        const unsigned long long bit = 1ull << (i / k);
+        if (atomicOr(&mask[e], bit) & bit) chunk_slow = 1;
+      } else {
+        chunk_slow = 1;
       }
     }
     __syncthreads();
+    if (!chunk_slow) {
+      for (int i = tid; i < cP; i += kPermThreads) {
+        const int p = c + i, e = idx[p], tl = i / k;
+        const int q = start[e] + __popcll(mask[e] & ((1ull << tl) - 1ull));
+        pair_token[q] = p / k;
+        pair_slot[q] = p % k;
+        pair_pos[p] = q;
+      }
+      __syncthreads();
+      for (int e = tid; e < n; e += kPermThreads) start[e] += __popcll(mask[e]);
+      __syncthreads();
+      continue;
+    }
+    for (int b = 0; b < cP; b += kPermThreads) {
+      const int p = c + b + tid;
+      const int e = b + tid < cP ? idx[p] : -1;
+      const bool ok = e >= 0 && e < n;
+      chunk_e[tid] = ok ? e : -1;
+      __syncthreads();
+      if (ok) {
+        int r = 0;
+        for (int i = 0; i < tid; ++i) r += chunk_e[i] == e;
+        const int q = start[e] + r;
+        pair_token[q] = p / k;
+        pair_slot[q] = p % k;
+        pair_pos[p] = q;
+      } else if (b + tid < cP) {
+        pair_pos[p] = -1;
+      }
+      __syncthreads();
+      // advance each expert's base by its pairs here (its last entry writes)
+      if (ok) {
+        bool last = true;
+        for (int i = tid + 1; i < kPermThreads; ++i)
+          if (chunk_e[i] == e) {
+            last = false;
+            break;
+          }
+        if (last) {
+          int r = 0;
+          for (int i = 0; i <= tid; ++i) r += chunk_e[i] == e;
+          start[e] += r;
+        }
+      }
+      __syncthreads();
+    }
   }
   // work items: ceil(cnt/kTokBatch) per expert, in expert order
   int li = 0;
@@ -190,9 +224,12 @@ __global__ __launch_bounds__(kThreads) void gate_up_batched_kernel(
         return ldc(experts + ldc(it.e + t / T)) + (size_t)(t % T) * L.gu.tile_bytes;
       },
       [&](int t) { return ldc(it.cnt + t / T); },
-      [&](u32x4 w, int g, int t, int v) {
+      [&](u32x4 w, int g, int t, int n, float(&sub)[kTokBatch]) {
         rows(t);
-        return group_dot_bf16(w, cr.row[v] + (size_t)16 * g);
+        const GroupBf16 G = decode_bf16(w);
+#pragma unroll
+        for (int v = 0; v < kTokBatch; ++v)
+          sub[v] = v < n ? dot_decoded(G, cr.row[v] + (size_t)16 * g) : 0.f;
       },
       [&](int t, int v, int lane, float s) {
         const float u = __shfl_down(s, 32);  // lane l<32: gate row; l+32: up row
@@ -223,12 +260,15 @@ __global__ __launch_bounds__(kThreads) void down_batched_kernel(
                (size_t)(t % T) * L.down.tile_bytes;
       },
       [&](int t) { return ldc(it.cnt + t / T); },
-      [&](u32x4 w, int g, int t, int v) {
+      [&](u32x4 w, int g, int t, int n, float(&sub)[kTokBatch]) {
         if (t != ct) {
           ct = t;
           coff = (size_t)ldc(it.off + t / T);
         }
-        return group_dot_f32(w, h + (coff + v) * inter + (size_t)32 * g);
+        const GroupF32 G = decode_f32(w);
+#pragma unroll
+        for (int v = 0; v < kTokBatch; ++v)
+          sub[v] = v < n ? dot_decoded(G, h + (coff + v) * inter + (size_t)32 * g) : 0.f;
       },
       [&](int t, int v, int lane, float s) {
         const int row = (t % T) * kTileRows + lane;

@@ -75,6 +75,65 @@ __device__ __forceinline__ float group_dot_f32(const u32x4 w, const float *xg) {
   return s;
 }
 
+// A group's 32 codes decoded once, for multiplying by several activation
+// vectors: 16 bf16 pairs (exact) or 16 fp32 pairs, element 2i+0 first.
+struct GroupBf16 {
+  bf16x2 v[16];
+};
+struct GroupF32 {
+  f32x2 v[16];
+};
+
+__device__ __forceinline__ GroupBf16 decode_bf16(const u32x4 w) {
+  GroupBf16 G;
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    G.v[4 * d + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], 1.0f, 0);
+    G.v[4 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], 1.0f, 1);
+    G.v[4 * d + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], 1.0f, 2);
+    G.v[4 * d + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[d], 1.0f, 3);
+  }
+  return G;
+}
+
+__device__ __forceinline__ GroupF32 decode_f32(const u32x4 w) {
+  GroupF32 G;
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    G.v[4 * d + 0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], 1.0f, 0);
+    G.v[4 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], 1.0f, 1);
+    G.v[4 * d + 2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], 1.0f, 2);
+    G.v[4 * d + 3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[d], 1.0f, 3);
+  }
+  return G;
+}
+
+// sum over the group of decoded weights times bf16 x (16 pairs at xg), in
+// the same order as group_dot_bf16.
+__device__ __forceinline__ float dot_decoded(const GroupBf16 &G,
+                                             const uint32_t *xg) {
+  const cu32_t *xc = (const cu32_t *)xg;
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    s = __builtin_amdgcn_fdot2_f32_bf16(G.v[i], __builtin_bit_cast(bf16x2, xc[i]), s, false);
+  return s;
+}
+
+// Same for fp32 x (32 values at xg), in the order of group_dot_f32.
+__device__ __forceinline__ float dot_decoded(const GroupF32 &G, const float *xg) {
+  const cf32_t *xc = (const cf32_t *)xg;
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    s = fmaf(G.v[i].x, xc[2 * i], s);
+    s = fmaf(G.v[i].y, xc[2 * i + 1], s);
+  }
+  return s;
+}
+
 // acc += 2^(e-127) * sub, or nothing for e == 255 (select, not multiply).
 __device__ __forceinline__ float apply_scale(float acc, float sub, uint32_t e) {
   const float t = acc + ldexpf(sub, (int)e - 127);

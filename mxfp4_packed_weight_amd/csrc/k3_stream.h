@@ -47,9 +47,10 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // decoded group by up to NA tokens), MaxTPW tiles per chunk.
 //   base(t)               -> const uint8_t*  tile t's packed bytes (uniform)
 //   na(t)                 -> int  vectors tile t uses (1..NA, uniform)
-//   dot(w, g, t, a)       -> float  unscaled dot of this lane's 16 code bytes
-//                            w (group g of its row of tile t) with group g of
-//                            activation vector a (g < G, a < na(t), uniform)
+//   dot(w, g, t, n, sub)  sub[a] = unscaled dot of this lane's 16 code
+//                            bytes w (group g of its row of tile t) with
+//                            group g of activation vector a, for a < n =
+//                            na(t) (g < G; g, t, n uniform)
 //   epi(t, a, lane, s)    finished sum of row `lane` of tile t for vector a
 // `part` is the caller's LDS array of MaxTPW * kNW * 64 * NA floats.
 template <int NA, int MaxTPW, class Base, class Na, class Dot, class Epi>
@@ -131,9 +132,11 @@ __device__ __forceinline__ void run_rows_n(int t_begin, int t_end, int G,
       for (int b = 0; b < 4; ++b)
         if (g0 + b < G) {
           const uint32_t eb = (e >> (8 * b)) & 255u;
+          float sub[NA];
+          dot(a[d][b], g0 + b, c0 + ktl, cna, sub);
 #pragma unroll
           for (int v = 0; v < NA; ++v)
-            if (v < cna) acc[v] = apply_scale(acc[v], dot(a[d][b], g0 + b, c0 + ktl, v), eb);
+            if (v < cna) acc[v] = apply_scale(acc[v], sub[v], eb);
         }
       if (++kq == G4) {
         kq = 0;
@@ -198,7 +201,7 @@ __device__ __forceinline__ void run_rows(int t_begin, int t_end, int G, int G4,
                                          float *part) {
   run_rows_n<1, kMaxTPW>(
       t_begin, t_end, G, G4, base, [](int) { return 1; },
-      [&](u32x4 w, int g, int t, int) { return dot(w, g, t); },
+      [&](u32x4 w, int g, int t, int, float(&sub)[1]) { sub[0] = dot(w, g, t); },
       [&](int t, int, int lane, float s) { epi(t, lane, s); }, part);
 }
 
