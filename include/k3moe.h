@@ -256,6 +256,44 @@ k3_status k3_moe_layer_batched(const uint16_t *X, const uint16_t *router_w,
                                float *Y_f32, int32_t *idx, float *w, void *ws,
                                size_t ws_bytes, k3_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Prefill: many tokens per expert, so the expert products are dense
+ * contractions on gfx950's block-scaled FP4 matrix instruction with both
+ * operands MXFP4. The pages' engine has no activation quantiser ([A176]
+ * "What is missing or worth watching"); the rule used here: for each block
+ * of 32 values along K, E = floor(log2 max|v|) - 2 clamped to [-127, 127],
+ * exponent byte E + 127, codes = E2M1 nearest to v / 2^E with ties to the
+ * even code (0, 1, 2, 4), saturating at 6; a code of magnitude 0 is code 0;
+ * an all-zero block has exponent byte 0.
+ *
+ * k3_mxfp4_quantize_{f32,bf16}: v[rows][cols] (device) -> nib[rows][cols/2]
+ * (element 2b in the low nibble of byte b) and sc[rows][cols/32].
+ *
+ * k3_moe_prefill: for T tokens X bf16 [T][hidden] routed by top-k of logits
+ * (fp64 [T][n_experts], optional bias as in k3_router_topk): x is quantised,
+ * every selected expert's gate/up stack is multiplied by its tokens' x, h =
+ * SiLU(gate) * up (fp32) is quantised per 32 along inter, multiplied by the
+ * down matrix, and Y[t] = sum_j w[t][j] * y_{idx[t][j]}(t) in rank order.
+ * Y bf16 / Y_f32 fp32 [T][hidden]; idx int32 [T][k], w fp32 [T][k] optional.
+ * Optional exports of h, indexed by sorted pair q (the order of
+ * k3_moe_permute over idx): h_f32 fp32 [T*k][inter] before quantisation,
+ * h_nib [T*k][inter/2] and h_sc [T*k][inter/32] (given together) after.
+ * Workspace: k3_moe_prefill_workspace_bytes(T, n_experts, hidden, inter, k)
+ * bytes, which include the fp32 partials [T*k][hidden].
+ * ---------------------------------------------------------------------- */
+k3_status k3_mxfp4_quantize_f32(const float *v, int rows, int cols, uint8_t *nib,
+                                uint8_t *sc, k3_stream_t stream);
+k3_status k3_mxfp4_quantize_bf16(const uint16_t *v, int rows, int cols,
+                                 uint8_t *nib, uint8_t *sc, k3_stream_t stream);
+size_t k3_moe_prefill_workspace_bytes(int T, int n_experts, int hidden,
+                                      int inter, int k);
+k3_status k3_moe_prefill(const uint16_t *X, const double *logits,
+                         const float *bias, const uint8_t *const *experts,
+                         int n_experts, int hidden, int inter, int k, int T,
+                         uint16_t *Y, float *Y_f32, int32_t *idx, float *w,
+                         float *h_f32, uint8_t *h_nib, uint8_t *h_sc, void *ws,
+                         size_t ws_bytes, k3_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

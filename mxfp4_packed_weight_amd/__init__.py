@@ -54,6 +54,11 @@ SIGNATURES = [
                                       _vp, _vp, _sz, _vp]),
     ("k3_moe_layer_batched", _i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
                                   _sz, _vp]),
+    ("k3_mxfp4_quantize_f32", _i, [_vp, _i, _i, _vp, _vp, _vp]),
+    ("k3_mxfp4_quantize_bf16", _i, [_vp, _i, _i, _vp, _vp, _vp]),
+    ("k3_moe_prefill_workspace_bytes", _sz, [_i, _i, _i, _i, _i]),
+    ("k3_moe_prefill", _i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
+                            _vp, _vp, _vp, _sz, _vp]),
 ]
 
 
@@ -252,3 +257,24 @@ def k3_moe_layer_batched(X, router_w, experts, n_experts, hidden, inter, k, T, Y
     _call("k3_moe_layer_batched", _dp(X), _dp(router_w), _dp(experts), n_experts, hidden,
           inter, k, T, _dp(Y), _dp(Y_f32), _dp(idx), _dp(w), _dp(ws), _nbytes(ws),
           _stream(stream))
+
+
+# ---- prefill --------------------------------------------------------------
+
+def k3_mxfp4_quantize_f32(v, rows, cols, nib, sc, stream=None):
+    _call("k3_mxfp4_quantize_f32", _dp(v), rows, cols, _dp(nib), _dp(sc), _stream(stream))
+
+
+def k3_mxfp4_quantize_bf16(v, rows, cols, nib, sc, stream=None):
+    _call("k3_mxfp4_quantize_bf16", _dp(v), rows, cols, _dp(nib), _dp(sc), _stream(stream))
+
+
+def k3_moe_prefill_workspace_bytes(T, n_experts, hidden, inter, k):
+    return lib().k3_moe_prefill_workspace_bytes(T, n_experts, hidden, inter, k)
+
+
+def k3_moe_prefill(X, logits, bias, experts, n_experts, hidden, inter, k, T, Y, ws, Y_f32=None,
+                   idx=None, w=None, h_f32=None, h_nib=None, h_sc=None, stream=None):
+    _call("k3_moe_prefill", _dp(X), _dp(logits), _dp(bias), _dp(experts), n_experts, hidden,
+          inter, k, T, _dp(Y), _dp(Y_f32), _dp(idx), _dp(w), _dp(h_f32), _dp(h_nib), _dp(h_sc),
+          _dp(ws), _nbytes(ws), _stream(stream))

@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "k3_internal.h"
@@ -99,6 +100,39 @@ BatchWs batch_ws(int T, int n, int hidden, int inter, int k) {
   off += align256((size_t)P * inter * sizeof(float));
   B.yp = off;
   off += align256((size_t)P * hidden * sizeof(float));
+  B.total = off;
+  return B;
+}
+
+// Prefill: idx, w, counts, offsets, pair_token, pair_slot, permutation
+// scratch, quantised x, quantised h, yp [P][hidden] fp32.
+struct PrefillWs {
+  size_t idx, w, counts, offsets, pair_token, pair_slot;
+  PermWs perm;
+  size_t xq, xsc, hq, hsc, yp, total;
+};
+PrefillWs prefill_ws(int T, int n, int hidden, int inter, int k) {
+  PrefillWs B;
+  const long long P = (long long)T * k;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  B.idx = take((size_t)P * sizeof(int32_t));
+  B.w = take((size_t)P * sizeof(float));
+  B.counts = take((size_t)n * sizeof(int32_t));
+  B.offsets = take((size_t)n * sizeof(int32_t));
+  B.pair_token = take((size_t)P * sizeof(int32_t));
+  B.pair_slot = take((size_t)P * sizeof(int32_t));
+  B.perm = perm_ws(off, P);
+  off = B.perm.total;
+  B.xq = take((size_t)T * hidden / 2);
+  B.xsc = take((size_t)T * hidden / 32);
+  B.hq = take((size_t)P * inter / 2);
+  B.hsc = take((size_t)P * inter / 32);
+  B.yp = take((size_t)P * hidden * sizeof(float));
   B.total = off;
   return B;
 }
@@ -534,7 +568,7 @@ k3_status k3_moe_permute(const int32_t *idx, int T, int k, int n_experts,
   K3_LAUNCH(fn, launch_permute(idx, T, k, n_experts,
                                perm_out(base, W, counts, offsets, pair_token,
                                         pair_slot),
-                               stream));
+                               tok_batch(), stream));
   return K3_OK;
 }
 
@@ -583,7 +617,7 @@ static k3_status batched_common(const char *fn, const uint16_t *X,
     logits = lg;
   }
   K3_LAUNCH(fn, launch_topk_f64(logits, bias, T, n_experts, k, ix, wt, stream));
-  K3_LAUNCH(fn, launch_permute(ix, T, k, n_experts, o, stream));
+  K3_LAUNCH(fn, launch_permute(ix, T, k, n_experts, o, tok_batch(), stream));
   K3_LAUNCH(fn, launch_gate_up_batched(X, experts, o, hidden, inter, h, stream));
   K3_LAUNCH(fn, launch_down_batched(h, experts, o, hidden, inter, yp, stream));
   K3_LAUNCH(fn, launch_combine_batched(yp, wt, o.pair_pos, T, k, hidden, Y,
@@ -615,6 +649,97 @@ k3_status k3_moe_layer_batched(const uint16_t *X, const uint16_t *router_w,
   return batched_common(fn, X, router_w, nullptr, nullptr, experts, n_experts,
                         hidden, inter, k, T, Y, Y_f32, idx, w, ws, ws_bytes,
                         stream);
+}
+
+/* ---- prefill ------------------------------------------------------------ */
+
+static k3_status check_quant(const char *fn, long long rows, int cols) {
+  K3_NEED(fn, rows >= 1 && rows <= (1ll << 31), "%s: rows=%lld outside [1, 2^31]", fn,
+          rows);
+  K3_NEED(fn, cols >= 32 && cols <= kMaxDim && cols % 32 == 0,
+          "%s: cols=%d must be a positive multiple of 32 (<= %d)", fn, cols, kMaxDim);
+  return K3_OK;
+}
+
+k3_status k3_mxfp4_quantize_f32(const float *v, int rows, int cols, uint8_t *nib,
+                                uint8_t *sc, k3_stream_t stream) {
+  const char *fn = "k3_mxfp4_quantize_f32";
+  K3_NEED_PTR(fn, v);
+  K3_NEED_PTR(fn, nib);
+  if (!sc) return fail(K3_ERR_ARG, "%s: sc is NULL", fn);
+  if (k3_status s = check_quant(fn, rows, cols)) return s;
+  K3_LAUNCH(fn, launch_quant_f32(v, rows, cols, nib, sc, stream));
+  return K3_OK;
+}
+
+k3_status k3_mxfp4_quantize_bf16(const uint16_t *v, int rows, int cols,
+                                 uint8_t *nib, uint8_t *sc, k3_stream_t stream) {
+  const char *fn = "k3_mxfp4_quantize_bf16";
+  K3_NEED_PTR(fn, v);
+  K3_NEED_PTR(fn, nib);
+  if (!sc) return fail(K3_ERR_ARG, "%s: sc is NULL", fn);
+  if (k3_status s = check_quant(fn, rows, cols)) return s;
+  K3_LAUNCH(fn, launch_quant_bf16(v, rows, cols, nib, sc, stream));
+  return K3_OK;
+}
+
+size_t k3_moe_prefill_workspace_bytes(int T, int n_experts, int hidden,
+                                      int inter, int k) {
+  if (check_batch("k3_moe_prefill_workspace_bytes", T, n_experts, k) != K3_OK ||
+      check_expert_dims("k3_moe_prefill_workspace_bytes", hidden, inter) != K3_OK)
+    return 0;
+  return prefill_ws(T, n_experts, hidden, inter, k).total;
+}
+
+k3_status k3_moe_prefill(const uint16_t *X, const double *logits,
+                         const float *bias, const uint8_t *const *experts,
+                         int n_experts, int hidden, int inter, int k, int T,
+                         uint16_t *Y, float *Y_f32, int32_t *idx, float *w,
+                         float *h_f32, uint8_t *h_nib, uint8_t *h_sc, void *ws,
+                         size_t ws_bytes, k3_stream_t stream) {
+  const char *fn = "k3_moe_prefill";
+  K3_NEED_PTR(fn, X);
+  K3_NEED_PTR(fn, logits);
+  K3_NEED_PTR(fn, experts);
+  K3_NEED_PTR(fn, ws);
+  if (!Y && !Y_f32) return fail(K3_ERR_ARG, "%s: Y and Y_f32 are both NULL", fn);
+  if ((Y && !aligned16(Y)) || (Y_f32 && !aligned16(Y_f32)) ||
+      (idx && !aligned16(idx)) || (w && !aligned16(w)) ||
+      (bias && !aligned16(bias)) || (h_f32 && !aligned16(h_f32)) ||
+      (h_nib && !aligned16(h_nib)))
+    return fail(K3_ERR_ARG, "%s: an optional argument is not 16-byte aligned",
+                fn);
+  if ((h_nib == nullptr) != (h_sc == nullptr))
+    return fail(K3_ERR_ARG, "%s: h_nib and h_sc must be given together", fn);
+  if (k3_status s = check_batch(fn, T, n_experts, k)) return s;
+  if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
+  const PrefillWs B = prefill_ws(T, n_experts, hidden, inter, k);
+  if (k3_status s = need_ws(fn, ws_bytes, B.total)) return s;
+  uint8_t *base = static_cast<uint8_t *>(ws);
+  int32_t *ix = idx ? idx : reinterpret_cast<int32_t *>(base + B.idx);
+  float *wt = w ? w : reinterpret_cast<float *>(base + B.w);
+  const PermOut o = perm_out(base, B.perm,
+                             reinterpret_cast<int32_t *>(base + B.counts),
+                             reinterpret_cast<int32_t *>(base + B.offsets),
+                             reinterpret_cast<int32_t *>(base + B.pair_token),
+                             reinterpret_cast<int32_t *>(base + B.pair_slot));
+  uint8_t *hq = h_nib ? h_nib : base + B.hq;
+  uint8_t *hsc = h_sc ? h_sc : base + B.hsc;
+  const long long P = (long long)T * k;
+  const int max_items =
+      (int)(std::min<long long>(n_experts, P) + P / prefill_tok_batch() + 1);
+  K3_LAUNCH(fn, launch_topk_f64(logits, bias, T, n_experts, k, ix, wt, stream));
+  K3_LAUNCH(fn, launch_permute(ix, T, k, n_experts, o, prefill_tok_batch(), stream));
+  K3_LAUNCH(fn, launch_quant_bf16(X, T, hidden, base + B.xq, base + B.xsc, stream));
+  K3_LAUNCH(fn, launch_prefill_gate_up(base + B.xq, base + B.xsc, experts, o,
+                                       max_items, hidden, inter, hq, hsc, h_f32,
+                                       stream));
+  float *yp = reinterpret_cast<float *>(base + B.yp);
+  K3_LAUNCH(fn, launch_prefill_down(hq, hsc, experts, o, max_items, hidden,
+                                    inter, yp, stream));
+  K3_LAUNCH(fn, launch_combine_batched(yp, wt, o.pair_pos, T, k, hidden, Y,
+                                       Y_f32, stream));
+  return K3_OK;
 }
 
 }  // extern "C"

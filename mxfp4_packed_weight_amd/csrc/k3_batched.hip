@@ -52,14 +52,14 @@ __device__ int block_scan_incl(int v, int *tmp) {
 //   counts[e], offsets[e]        run length and start of expert e
 //   pair_token[q], pair_slot[q]  the q-th pair in (expert, pair index) order
 //   pair_pos[p]                  q of pair p (-1 when not placed)
-//   items: item_e/off/cnt[i]     expert, first q, tokens (<= kTokBatch)
+//   items: item_e/off/cnt[i]     expert, first q, tokens (<= item_tok)
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     const int32_t *__restrict__ idx, int T, int k, int n,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     int32_t *__restrict__ pair_token, int32_t *__restrict__ pair_slot,
     int32_t *__restrict__ pair_pos, int32_t *__restrict__ item_e,
     int32_t *__restrict__ item_off, int32_t *__restrict__ item_cnt,
-    int32_t *__restrict__ n_items, int32_t *__restrict__ n_bad) {
+    int32_t *__restrict__ n_items, int32_t *__restrict__ n_bad, int item_tok) {
   __shared__ int cnt[K3_MAX_EXPERTS];
   __shared__ int start[K3_MAX_EXPERTS];  // offsets, then running fill base
   __shared__ unsigned long long mask[K3_MAX_EXPERTS];
@@ -160,16 +160,16 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
       __syncthreads();
     }
   }
-  // work items: ceil(cnt/kTokBatch) per expert, in expert order
+  // work items: ceil(cnt/item_tok) per expert, in expert order
   int li = 0;
-  for (int e = e0; e < e1; ++e) li += (cnt[e] + kTokBatch - 1) / kTokBatch;
+  for (int e = e0; e < e1; ++e) li += (cnt[e] + item_tok - 1) / item_tok;
   int ibase = block_scan_incl(li, tmp) - li;
   for (int e = e0; e < e1; ++e) {
     const int off = offsets[e];
-    for (int s = 0; s < cnt[e]; s += kTokBatch) {
+    for (int s = 0; s < cnt[e]; s += item_tok) {
       item_e[ibase] = e;
       item_off[ibase] = off + s;
-      item_cnt[ibase] = min(kTokBatch, cnt[e] - s);
+      item_cnt[ibase] = min(item_tok, cnt[e] - s);
       ++ibase;
     }
   }
@@ -310,11 +310,11 @@ unsigned persistent_grid() { return (unsigned)num_cus(); }
 int tok_batch() { return kTokBatch; }
 
 hipError_t launch_permute(const int32_t *idx, int T, int k, int n,
-                          const PermOut &o, hipStream_t s) {
+                          const PermOut &o, int item_tok, hipStream_t s) {
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, s, idx, T,
                      k, n, o.counts, o.offsets, o.pair_token, o.pair_slot,
                      o.pair_pos, o.item_e, o.item_off, o.item_cnt, o.n_items,
-                     o.n_bad);
+                     o.n_bad, item_tok);
   return hipGetLastError();
 }
 

@@ -113,7 +113,7 @@ struct PermOut {
 };
 int tok_batch();
 hipError_t launch_permute(const int32_t *idx, int T, int k, int n,
-                          const PermOut &o, hipStream_t s);
+                          const PermOut &o, int item_tok, hipStream_t s);
 hipError_t launch_gate_up_batched(const uint16_t *X,
                                   const uint8_t *const *experts,
                                   const PermOut &o, int hidden, int inter,
@@ -125,6 +125,21 @@ hipError_t launch_combine_batched(const float *yp, const float *w,
                                   const int32_t *pair_pos, int T, int k,
                                   int hidden, uint16_t *Y, float *Y32,
                                   hipStream_t s);
+// Prefill (k3_prefill.hip): MXFP4 quantiser and the FP4 x FP4 grouped GEMMs.
+int prefill_tok_batch();
+hipError_t launch_quant_bf16(const uint16_t *v, long long rows, int cols,
+                             uint8_t *nib, uint8_t *sc, hipStream_t s);
+hipError_t launch_quant_f32(const float *v, long long rows, int cols,
+                            uint8_t *nib, uint8_t *sc, hipStream_t s);
+hipError_t launch_prefill_gate_up(const uint8_t *xq, const uint8_t *xsc,
+                                  const uint8_t *const *experts,
+                                  const PermOut &o, int max_items, int hidden,
+                                  int inter, uint8_t *hq, uint8_t *hsc,
+                                  float *h32, hipStream_t s);
+hipError_t launch_prefill_down(const uint8_t *hq, const uint8_t *hsc,
+                               const uint8_t *const *experts, const PermOut &o,
+                               int max_items, int hidden, int inter, float *yp,
+                               hipStream_t s);
 hipError_t launch_combine(const float *yp, const float *w, int k, int hidden,
                           uint16_t *y, float *y_f32, hipStream_t s);
 hipError_t launch_router(const uint16_t *x, const uint16_t *R, int T,

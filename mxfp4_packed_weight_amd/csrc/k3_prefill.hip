@@ -1,0 +1,312 @@
+// Prefill: the grouped GEMMs of many tokens per expert on gfx950's
+// block-scaled FP4 matrix instruction, v_mfma_scale_f32_16x16x128_f8f6f4
+// with both operands FP4 (E2M1 codes and per-32 E8M0 exponents). This is
+// the path's one dense contraction: every expert sees tens of tokens, so
+// its packed weights are multiplied as a matrix, not a vector.
+//
+// Activations are quantised to MXFP4 per 32 along K (x before gate/up, h
+// before down) by the rule of the oracle's quantiser: E = floor(log2 amax)
+// - 2 clamped to [-127, 127], codes = E2M1 nearest to v / 2^E with ties to
+// the even code, saturating at 6; an all-zero block has exponent 0.
+//
+// Operand layouts of the instruction (16 x 16 x 128, both FP4; measured):
+//   A: lane l = row l%16, K elements [32(l/16), +32): 16 bytes, low nibble
+//      even, which is exactly one MXFP4 group of one weight row; its scale
+//      is that group's exponent byte.
+//   B: lane l = column l%16, the same K range of that column: one group of
+//      one token's quantised row, with that group's exponent as its scale.
+//   C: lane l = column l%16, rows 4(l/16) + i, i = 0..3.
+// Every product of two E2M1 values times two powers of two is exact, and
+// within a 32-block they span less than 2^8, below the unit's alignment
+// window, so the block sums are exact and accumulate in fp32.
+#include "k3_stream.h"
+
+namespace k3 {
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kNB = 4;                 // 16-token column blocks per work item
+constexpr int kPfTok = 16 * kNB;       // tokens per prefill work item
+constexpr int kPfDepth = 2;            // quads in flight per wave
+
+// |v| / 2^E (exact) -> E2M1 magnitude code, nearest with ties to the even
+// code (0, 1.0, 2.0, 4.0), saturating at 6.
+__device__ __forceinline__ uint32_t e2m1_mag_code(float a) {
+  if (a <= 0.25f) return 0u;
+  if (a < 0.75f) return 1u;
+  if (a <= 1.25f) return 2u;
+  if (a < 1.75f) return 3u;
+  if (a <= 2.5f) return 4u;
+  if (a < 3.5f) return 5u;
+  if (a <= 5.0f) return 6u;
+  return 7u;
+}
+
+// Exponent byte of a block with largest magnitude amax, and 2^-E.
+__device__ __forceinline__ uint32_t mx_scale(float amax, float *inv) {
+  if (!(amax > 0.f)) {
+    *inv = 0.f;
+    return 0u;
+  }
+  const int ef = (int)((__float_as_uint(amax) >> 23) & 255u);
+  const int E = max(-127, (ef == 0 ? -127 : ef - 127) - 2);
+  *inv = __uint_as_float((uint32_t)(127 - E) << 23);
+  return (uint32_t)(E + 127);
+}
+
+// E2M1 code of v under 2^-E (sign kept only for a nonzero magnitude).
+__device__ __forceinline__ uint32_t e2m1_code(float v, float inv) {
+  const uint32_t m = e2m1_mag_code(fabsf(v) * inv);
+  return (m != 0u && v < 0.f) ? (m | 8u) : m;
+}
+
+// Quantiser: v[rows][cols] -> nib[rows][cols/2] (element 2b in the low
+// nibble of byte b) and sc[rows][cols/32]. Each half-wave owns one block of
+// 32 values, one per lane.
+template <typename T>
+__global__ __launch_bounds__(256) void quant_kernel(const T *__restrict__ v,
+                                                    long long nblocks, int cols,
+                                                    uint8_t *__restrict__ nib,
+                                                    uint8_t *__restrict__ sc) {
+  const long long blk = ((long long)blockIdx.x * 256 + threadIdx.x) >> 5;
+  const int i = threadIdx.x & 31;
+  if (blk >= nblocks) return;  // whole half-waves leave together
+  const int G = cols / 32;
+  const long long r = blk / G, g = blk % G;
+  float x;
+  if constexpr (sizeof(T) == 2)
+    x = __uint_as_float((uint32_t)v[r * cols + g * 32 + i] << 16);
+  else
+    x = (float)v[r * cols + g * 32 + i];
+  float a = fabsf(x);
+#pragma unroll
+  for (int d = 1; d < 32; d <<= 1) a = fmaxf(a, __shfl_xor(a, d, 32));
+  float inv;
+  const uint32_t e = mx_scale(a, &inv);
+  const uint32_t c = e2m1_code(x, inv);
+  const uint32_t hi = __shfl_down(c, 1, 32);
+  if ((i & 1) == 0) nib[r * (cols / 2) + g * 16 + i / 2] = (uint8_t)(c | (hi << 4));
+  if (i == 0) sc[r * G + g] = (uint8_t)e;
+}
+
+__device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
+
+struct PfItems {
+  const int32_t *e, *off, *cnt, *n;
+};
+
+// One wave per (work item, weight tile): C[64 rows][up to 64 tokens] over
+// the whole K of the matrix. kGateUp: the gate/up stack (A = tile s of the
+// expert's gate/up region, B = quantised x rows of the item's tokens);
+// epilogue h = SiLU(gate) * up, quantised per 32 (one group per tile) into
+// hq[pair]; optional fp32 h. Otherwise the down matrix (B = quantised h
+// rows of the item's pairs); epilogue yp[pair][row] fp32.
+template <bool kGateUp>
+__global__ __launch_bounds__(64) void prefill_gemm_kernel(
+    const uint8_t *__restrict__ bq, const uint8_t *__restrict__ bsc,
+    const int32_t *__restrict__ pair_token, const uint8_t *const *__restrict__ experts,
+    PfItems it, int hidden, int inter, uint8_t *__restrict__ hq,
+    uint8_t *__restrict__ hsc, float *__restrict__ h32, float *__restrict__ yp) {
+  const ExpertLayout L = expert_layout(hidden, inter);
+  const MatLayout &M = kGateUp ? L.gu : L.down;
+  const int Tt = M.ntiles;
+  const int u = blockIdx.x;
+  if (u >= ldc(it.n) * Tt) return;
+  const int item = u / Tt, s = u % Tt;
+  const int e = ldc(it.e + item), off = ldc(it.off + item), cnt = ldc(it.cnt + item);
+  const uint8_t *tile = ldc(experts + e) + (kGateUp ? 0 : L.down_offset) +
+                        (size_t)s * M.tile_bytes;
+  const int K = M.cols, G = M.G, G4 = M.G4;
+  const int lane = threadIdx.x & 63, col = lane & 15, kb = lane >> 4;
+
+  // B rows of this lane for each column block (clamped to a valid row)
+  const uint8_t *brow[kNB];
+  const uint8_t *bsrow[kNB];
+  bool bok[kNB];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    const int c = 16 * nb + col;
+    bok[nb] = c < cnt;
+    const int q = off + (bok[nb] ? c : 0);
+    const long long r = kGateUp ? (long long)ldc(pair_token + q) : (long long)q;
+    brow[nb] = bq + r * (K / 2);
+    bsrow[nb] = bsc + r * G;
+  }
+
+  u32x4 a[kPfDepth][4], b[kPfDepth][kNB];
+  uint32_t asc[kPfDepth][4], bs[kPfDepth][kNB];
+  auto load = [&](int d, int q) {
+    const uint8_t *qb = tile + (size_t)kQuadBytes * q;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      a[d][m] = __builtin_nontemporal_load(
+          (const gu4_t *)(qb + 1024 * kb + 16 * (16 * m + col)));
+      asc[d][m] = __builtin_nontemporal_load(
+          (const gu32_t *)(qb + 4096 + 4 * (16 * m + col)));
+    }
+    const int g = min(4 * q + kb, G - 1);  // groups past G are zero below
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      b[d][nb] = *(const gu4_t *)(brow[nb] + 16 * g);
+      bs[d][nb] = *(__attribute__((address_space(1))) const uint8_t *)(bsrow[nb] + g);
+    }
+  };
+  v4f acc[kNB][4];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[nb][m] = v4f{0.f, 0.f, 0.f, 0.f};
+  auto consume = [&](int d, int q) {
+    const bool gin = 4 * q + kb < G;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      uint32_t ea = (asc[d][m] >> (8 * kb)) & 255u;
+      u32x4 am = a[d][m];
+      if (ea == 255u) {  // the group contributes nothing
+        am = u32x4{0u, 0u, 0u, 0u};
+        ea = 127u;
+      }
+      const v8i av = {(int)am.x, (int)am.y, (int)am.z, (int)am.w, 0, 0, 0, 0};
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) {
+        u32x4 bm = b[d][nb];
+        uint32_t eb = bs[d][nb];
+        if (!(bok[nb] && gin)) {
+          bm = u32x4{0u, 0u, 0u, 0u};
+          eb = 127u;
+        }
+        const v8i bv = {(int)bm.x, (int)bm.y, (int)bm.z, (int)bm.w, 0, 0, 0, 0};
+        acc[nb][m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            av, bv, acc[nb][m], 4, 4, 0, (int)ea, 0, (int)eb);
+      }
+    }
+  };
+  // ring over the quads of K (loads unconditional in the steady loop)
+  int q = 0;
+  const int npro = min(kPfDepth, G4);
+  for (int d = 0; d < npro; ++d) load(d, d);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  if (G4 >= kPfDepth) {
+    for (; q + 2 * kPfDepth <= G4; q += kPfDepth) {
+#pragma unroll
+      for (int d = 0; d < kPfDepth; ++d) {
+        consume(d, q + d);
+        load(d, q + kPfDepth + d);
+      }
+    }
+    for (int d = 0; d < kPfDepth; ++d)
+      if (q + d < G4) {
+        consume(d, q + d);
+        if (q + kPfDepth + d < G4) load(d, q + kPfDepth + d);
+      }
+    q += kPfDepth;
+    for (int d = 0; d < kPfDepth; ++d)
+      if (q + d < G4) consume(d, q + d);
+  } else {
+    consume(0, 0);
+  }
+
+  const int j = lane >> 4;  // C rows 4j + i of each 16-row sub-block
+  if constexpr (kGateUp) {
+    // tile rows 0..31 gate, 32..63 up (the same 32 output rows 32s + r)
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      float hv[2][4];
+      float amax = 0.f;
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          hv[m][i] = silu(acc[nb][m][i]) * acc[nb][m + 2][i];
+          amax = fmaxf(amax, fabsf(hv[m][i]));
+        }
+      amax = fmaxf(amax, __shfl_xor(amax, 16));
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      if (!bok[nb]) continue;
+      const size_t p = (size_t)off + 16 * nb + col;
+      float inv;
+      const uint32_t ex = mx_scale(amax, &inv);
+      // rows r = 16m + 4j + i: bytes (16m + 4j)/2 and +1 of the group
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const uint32_t c0 = e2m1_code(hv[m][0], inv), c1 = e2m1_code(hv[m][1], inv);
+        const uint32_t c2 = e2m1_code(hv[m][2], inv), c3 = e2m1_code(hv[m][3], inv);
+        uint8_t *dst = hq + p * (inter / 2) + (size_t)16 * s + 8 * m + 2 * j;
+        dst[0] = (uint8_t)(c0 | (c1 << 4));
+        dst[1] = (uint8_t)(c2 | (c3 << 4));
+        if (h32) {
+          float *hd = h32 + p * inter + (size_t)32 * s + 16 * m + 4 * j;
+          *reinterpret_cast<v4f *>(hd) = v4f{hv[m][0], hv[m][1], hv[m][2], hv[m][3]};
+        }
+      }
+      if (j == 0) hsc[p * (inter / 32) + s] = (uint8_t)ex;
+    }
+  } else {
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      if (!bok[nb]) continue;
+      const size_t p = (size_t)off + 16 * nb + col;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int row = 64 * s + 16 * m + 4 * j;
+        if (row < hidden)
+          *reinterpret_cast<v4f *>(yp + p * hidden + row) = acc[nb][m];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int prefill_tok_batch() { return kPfTok; }
+
+hipError_t launch_quant_bf16(const uint16_t *v, long long rows, int cols,
+                             uint8_t *nib, uint8_t *sc, hipStream_t s) {
+  const long long nblocks = rows * (cols / 32);
+  const long long threads = nblocks * 32;
+  hipLaunchKernelGGL(quant_kernel<uint16_t>, dim3((unsigned)((threads + 255) / 256)),
+                     dim3(256), 0, s, v, nblocks, cols, nib, sc);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_f32(const float *v, long long rows, int cols,
+                            uint8_t *nib, uint8_t *sc, hipStream_t s) {
+  const long long nblocks = rows * (cols / 32);
+  const long long threads = nblocks * 32;
+  hipLaunchKernelGGL(quant_kernel<float>, dim3((unsigned)((threads + 255) / 256)),
+                     dim3(256), 0, s, v, nblocks, cols, nib, sc);
+  return hipGetLastError();
+}
+
+// max_items: an upper bound of the work items the permutation can make.
+hipError_t launch_prefill_gate_up(const uint8_t *xq, const uint8_t *xsc,
+                                  const uint8_t *const *experts,
+                                  const PermOut &o, int max_items, int hidden,
+                                  int inter, uint8_t *hq, uint8_t *hsc,
+                                  float *h32, hipStream_t s) {
+  const ExpertLayout L = expert_layout(hidden, inter);
+  const PfItems it{o.item_e, o.item_off, o.item_cnt, o.n_items};
+  hipLaunchKernelGGL(prefill_gemm_kernel<true>,
+                     dim3((unsigned)((long long)max_items * L.gu.ntiles)), dim3(64),
+                     0, s, xq, xsc, o.pair_token, experts, it, hidden, inter, hq,
+                     hsc, h32, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_down(const uint8_t *hq, const uint8_t *hsc,
+                               const uint8_t *const *experts, const PermOut &o,
+                               int max_items, int hidden, int inter, float *yp,
+                               hipStream_t s) {
+  const ExpertLayout L = expert_layout(hidden, inter);
+  const PfItems it{o.item_e, o.item_off, o.item_cnt, o.n_items};
+  hipLaunchKernelGGL(prefill_gemm_kernel<false>,
+                     dim3((unsigned)((long long)max_items * L.down.ntiles)),
+                     dim3(64), 0, s, hq, hsc, o.pair_token, experts, it, hidden,
+                     inter, nullptr, nullptr, nullptr, yp);
+  return hipGetLastError();
+}
+
+}  // namespace k3
