@@ -81,9 +81,10 @@ def main():
     ap.add_argument("--tokens", type=int, default=512, help="distinct tokens in the bank")
     ap.add_argument("--router-copies", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=("c3", "c4"), default="c3",
+    ap.add_argument("--workload", choices=("c3", "c4", "c5"), default="c3",
                     help="c3: single-token decode layer (the headline line); c4: batched "
-                         "decode, 64 tokens with Zipf(1.1) logits")
+                         "decode, 64 tokens with Zipf(1.1) logits; c5: prefill, 2048 tokens "
+                         "with uniform logits on the FP4 matrix unit")
     ap.add_argument("--calib", action="store_true",
                     help="after the timed region, copy 1 GiB device-to-device three times "
                          "(the known-size kernel the HBM byte counters are scaled by)")
@@ -108,6 +109,8 @@ def main():
 
     if args.workload == "c4":
         return bench_c4(args)
+    if args.workload == "c5":
+        return bench_c5(args)
 
     dev = torch.device("cuda:0")
     n, hidden, inter, k = W.N_EXPERTS, W.HIDDEN, W.INTER, W.TOPK
@@ -284,6 +287,127 @@ def bench_c4(args):
             "kind": "oracle", "tokens_per_s": cb["tokens_per_s"],
             "sample": cb["sample"] + "; the oracle reads every selected expert once per token, "
                       "so a 64-token batch costs it 64 such layers"}
+    print(json.dumps(out))
+
+
+PEAK_FP4_TFLOPS = 10100.0  # dense FP4 matrix peak of MI355X
+
+
+def cpu_baseline_c5(budget_s=15.0):
+    """The oracle's prefill steps, expert by expert, for the experts' real
+    token sets of one C5 batch (quantise x, MXFP4 x MXFP4 gate/up products,
+    SiLU * up, quantise h, down products), until ~budget_s is spent; scaled
+    to all experts by the sampled share of routing pairs."""
+    import oracle
+    from gen import workloads as W
+    threads = min(16, os.cpu_count() or 1)
+    oracle.set_threads(threads)
+    n, hidden, inter, k, T = W.N_EXPERTS, W.HIDDEN, W.INTER, W.TOPK, 2048
+    X = W.tokens_bf16(0, W.C5, T, hidden)
+    L = W.uniform_router_logits(0, T, n, W.C5).astype(np.float64)
+    idx = np.stack([oracle.topk(L[t], k)[0] for t in range(T)])
+    counts, offsets, pt, _ = oracle.permute(idx, n)
+    silu = np.vectorize(oracle.silu)
+    xf = (X.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    spent, pairs, experts = 0.0, 0, 0
+    for e in range(n):
+        if spent >= budget_s:
+            break
+        toks = pt[offsets[e]:offsets[e] + counts[e]]
+        E = W.expert_weights(0, W.C3, e)
+        t0 = time.perf_counter()
+        xn, xs = oracle.mxfp4_quant(xf[toks])
+        g = oracle.mxfp4_matmul(xn, xs, *E["gate"])
+        u = oracle.mxfp4_matmul(xn, xs, *E["up"])
+        with np.errstate(over="ignore"):
+            hn, hs = oracle.mxfp4_quant(silu(g) * u)
+        oracle.mxfp4_matmul(hn, hs, *E["down"])
+        spent += time.perf_counter() - t0
+        pairs += int(counts[e])
+        experts += 1
+    full = spent * (T * k) / pairs
+    return {"value": round(n * BYTES_PER_EXPERT / full / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle", "tokens_per_s": round(T / full, 4),
+            "sample": f"{experts} experts with their {pairs} routed tokens of one C5 batch "
+                      f"through the oracle's quantiser and MXFP4 x MXFP4 products (fp64, "
+                      f"{threads} OpenMP threads), {spent:.1f} s, scaled by "
+                      f"{T * k}/{pairs} pairs to the whole batch"}
+
+
+def bench_c5(args):
+    """Prefill (C5): 2048 tokens, uniform logits, top-16 of 896; x and h
+    quantised to MXFP4, FP4 x FP4 grouped GEMMs on the matrix unit. `value`
+    is the HBM rate of the packed bytes of every expert the batch selects."""
+    import torch
+
+    import mxfp4_packed_weight_amd as K
+    import oracle
+    from gen import device as D
+    from gen import workloads as W
+    dev = torch.device("cuda:0")
+    n, hidden, inter, k, T = W.N_EXPERTS, W.HIDDEN, W.INTER, W.TOPK, 2048
+    nb = 2
+    pool = D.build_expert_pool(0, W.C3, n, device=dev, log=log)
+    Xs = [D.to_device(W.tokens_bf16(0, W.C5, T, batch=b).view(np.int16), dev) for b in range(nb)]
+    Ls = [W.uniform_router_logits(0, T, n, W.C5, batch=b).astype(np.float64) for b in range(nb)]
+    used = []
+    for L in Ls:
+        sel = set()
+        for t in range(T):
+            sel.update(int(e) for e in oracle.topk(L[t], k)[0])
+        used.append(len(sel))
+    Ld = [D.to_device(L, dev) for L in Ls]
+    ws = torch.empty(K.k3_moe_prefill_workspace_bytes(T, n, hidden, inter, k),
+                     dtype=torch.uint8, device=dev)
+    Y = torch.empty((T, hidden), dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        b = i % nb
+        K.k3_moe_prefill(Xs[b], Ld[b], None, pool.table, n, hidden, inter, k, T, Y, ws,
+                         stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    mean_used = sum(used[(args.warmup + i) % nb] for i in range(args.steps)) / args.steps
+    nbytes = mean_used * BYTES_PER_EXPERT
+    value = nbytes / (ms * 1e-3) / 1e9
+    flop = 2.0 * T * k * 3 * hidden * inter
+    tflops = flop / (ms * 1e-3) / 1e12
+    log(f"C5 prefill: {ms:.3f} ms/batch, {value:.1f} GB/s, {tflops:.1f} TFLOP/s")
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp4",
+        "data": "synthetic",
+        "config": {"workload": "prefill MoE layer (C5): 2048 tokens bf16, uniform router "
+                               "logits, top-16 of 896 MXFP4 experts (7168/1536, 15.7 GB "
+                               "resident), x and h quantised to MXFP4 per 32, FP4 x FP4 "
+                               "grouped GEMMs on the matrix unit, rank-order combine",
+                   "tokens_per_step": T, "n_experts": n, "topk": k,
+                   "experts_used": round(mean_used, 2), "expert_bytes_per_step": int(nbytes),
+                   "flop_per_step": flop},
+        "tokens_per_s": round(T * 1e3 / ms, 1),
+        "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "mfma_util": round(tflops / PEAK_FP4_TFLOPS, 5),
+        "roofline": {"kernel": "whole prefill layer (k3_moe_prefill)", "bound": "hbm",
+                     "achieved": round(value, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(value / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": int(nbytes),
+                     "fp4_tflops": round(tflops, 2), "fp4_peak_tflops": PEAK_FP4_TFLOPS},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host (bounded sample)")
+        out["cpu_baseline"] = cpu_baseline_c5()
     print(json.dumps(out))
 
 
