@@ -514,9 +514,14 @@ k3_status k3_moe_layer_ex(const uint16_t *x, const uint16_t *router_w,
   float *h = reinterpret_cast<float *>(base + L.h);
   float *yp = reinterpret_cast<float *>(base + L.yp);
   K3_LAUNCH(fn, launch_router(x, router_w, 1, hidden, n_experts, lg, stream));
-  K3_LAUNCH(fn, launch_topk_f64(lg, nullptr, 1, n_experts, k, ix, wt, stream));
-  K3_LAUNCH(fn, launch_gate_up(x, experts, ix, nullptr, k, hidden, inter, h,
-                               stream));
+  if (n_experts <= kFusedTopkMaxExperts) {  // top-k inside the gate/up launch
+    K3_LAUNCH(fn, launch_gate_up_routed(x, lg, experts, n_experts, k, hidden,
+                                        inter, h, ix, wt, stream));
+  } else {
+    K3_LAUNCH(fn, launch_topk_f64(lg, nullptr, 1, n_experts, k, ix, wt, stream));
+    K3_LAUNCH(fn, launch_gate_up(x, experts, ix, nullptr, k, hidden, inter, h,
+                                 stream));
+  }
   K3_LAUNCH(fn, launch_down(h, experts, ix, nullptr, k, hidden, inter, yp,
                             stream));
   K3_LAUNCH(fn, launch_combine(yp, wt, k, hidden, y, y_f32, stream));

@@ -12,6 +12,7 @@
 // convention"). The work is a memory-bound stream of packed bytes ("the wait
 // is for bytes to arrive", [SAT] "Reduction one").
 #include "k3_stream.h"
+#include "k3_topk.h"
 
 namespace k3 {
 
@@ -103,6 +104,54 @@ __global__ __launch_bounds__(kThreads) void down_kernel(
       part);
 }
 
+// The decode layer's first expert stage with the selection folded in:
+// every workgroup ranks the token's n logits itself (the same selection
+// everywhere, so no grid-wide step is needed), workgroup 0 publishes idx
+// and w, then the tiles of the k selected experts' gate/up stacks are
+// streamed as in gate_up_kernel. One launch fewer than a separate top-k.
+__global__ __launch_bounds__(kThreads) void gate_up_routed_kernel(
+    const uint16_t *__restrict__ x, const double *__restrict__ logits,
+    const uint8_t *const *__restrict__ experts, int n, int k, int hidden,
+    int inter, float *__restrict__ h, int32_t *__restrict__ idx_out,
+    float *__restrict__ w_out) {
+  __shared__ float part[kPartFloats];
+  __shared__ TopkLds tk;
+  __shared__ int sel[K3_MAX_TOPK];
+  if (wave_id() == 0) {
+    int e;
+    float wt;
+    topk_wave<kFusedTopkMaxExperts / 64, double>(logits, nullptr, n, k, tk, &e, &wt);
+    const int lane = threadIdx.x & 63;
+    if (lane < k) {
+      sel[lane] = e;
+      if (blockIdx.x == 0) {
+        idx_out[lane] = e;
+        w_out[lane] = wt;
+      }
+    }
+  }
+  __syncthreads();
+  const ExpertLayout L = expert_layout(hidden, inter);
+  const int T = L.gu.ntiles;
+  const uint32_t *xp = reinterpret_cast<const uint32_t *>(x);
+  int t0, t1;
+  wg_range(k * T, &t0, &t1);
+  run_rows(
+      t0, t1, L.gu.G, L.gu.G4,
+      [&](int t) {
+        const int e = __builtin_amdgcn_readfirstlane(sel[t / T]);
+        return ldc(experts + e) + (size_t)(t % T) * L.gu.tile_bytes;
+      },
+      [&](u32x4 w, int g, int) { return group_dot_bf16(w, xp + (size_t)16 * g); },
+      [&](int t, int lane, float s) {
+        const float u = __shfl_down(s, 32);  // lane l<32: gate row; l+32: up row
+        int is_up, row;
+        gu_lane_row(t % T, lane, &is_up, &row);
+        if (lane < 32 && row < inter) h[(size_t)(t / T) * inter + row] = silu(s) * u;
+      },
+      part);
+}
+
 // y[i] = sum_j w[j] * yp[j][i] in rank order j = 0..k-1, then bf16 (RNE).
 __global__ __launch_bounds__(256) void combine_kernel(
     const float *__restrict__ yp, const float *__restrict__ w, int k,
@@ -160,6 +209,17 @@ hipError_t launch_down(const float *h, const uint8_t *const *experts,
                      dim3(grid_for_tiles(nslots * L.down.ntiles)),
                      dim3(kThreads), 0, s, h, experts, idx, single, nslots,
                      hidden, inter, yp);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_up_routed(const uint16_t *x, const double *logits,
+                                 const uint8_t *const *experts, int n, int k,
+                                 int hidden, int inter, float *h, int32_t *idx,
+                                 float *w, hipStream_t s) {
+  const ExpertLayout L = expert_layout(hidden, inter);
+  hipLaunchKernelGGL(gate_up_routed_kernel, dim3(grid_for_tiles(k * L.gu.ntiles)),
+                     dim3(kThreads), 0, s, x, logits, experts, n, k, hidden,
+                     inter, h, idx, w);
   return hipGetLastError();
 }
 

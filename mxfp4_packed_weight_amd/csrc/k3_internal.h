@@ -140,6 +140,18 @@ hipError_t launch_prefill_down(const uint8_t *hq, const uint8_t *hsc,
                                const uint8_t *const *experts, const PermOut &o,
                                int max_items, int hidden, int inter, float *yp,
                                hipStream_t s);
+// LDS scratch of one wave's top-k (k3_topk.h).
+struct TopkLds {
+  double cand_key[64];
+  int cand_idx[64];
+  double ranked[K3_MAX_TOPK];
+};
+constexpr int kFusedTopkMaxExperts = 16 * 64;  // n handled by the fused path
+// The decode layer's first expert stage with top-k folded in (k3_expert.hip).
+hipError_t launch_gate_up_routed(const uint16_t *x, const double *logits,
+                                 const uint8_t *const *experts, int n, int k,
+                                 int hidden, int inter, float *h, int32_t *idx,
+                                 float *w, hipStream_t s);
 hipError_t launch_combine(const float *yp, const float *w, int k, int hidden,
                           uint16_t *y, float *y_f32, hipStream_t s);
 hipError_t launch_router(const uint16_t *x, const uint16_t *R, int T,

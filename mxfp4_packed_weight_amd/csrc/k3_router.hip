@@ -10,16 +10,15 @@
 // indices identical to an fp64 reference.
 //
 // Selection: one wave per token with the keys in registers; a cheap lower
-// bound keeps ~18 candidates, which are ranked in parallel (see
-// topk_kernel). Ties go to the lower expert index. The routing bias only
+// bound keeps ~18 candidates, which are ranked in parallel (topk_wave,
+// k3_topk.h). Ties go to the lower expert index. The routing bias only
 // changes the keys; the weights always come from the unbiased sigmoid scores
 // ([ZOR] "How is the C engine actually built?", invariant 3), renormalised to
 // sum to one, summed in rank order.
 #include <limits.h>
 #include <math.h>
 
-#include "k3_decode.h"
-#include "k3_internal.h"
+#include "k3_topk.h"
 
 namespace k3 {
 
@@ -44,39 +43,6 @@ __device__ __forceinline__ void dot8_bf16(u32x4 a, u32x4 b, double (&acc)[4]) {
 // DPP reductions over the 64 lanes (row_shr 1,2,4,8, then row_bcast 15 and
 // 31); the result of lane 63 is returned to every lane. Lanes without a DPP
 // source keep their own value.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ int dpp(int v) {
-  return __builtin_amdgcn_update_dpp(v, v, CTRL, ROWS, 0xf, false);
-}
-
-template <int CTRL, int ROWS>
-__device__ __forceinline__ double dpp_d(double v) {
-  const int lo = __double2loint(v), hi = __double2hiint(v);
-  return __hiloint2double(dpp<CTRL, ROWS>(hi), dpp<CTRL, ROWS>(lo));
-}
-
-__device__ __forceinline__ double wave_max(double v) {
-  v = fmax(v, dpp_d<0x111, 0xf>(v));
-  v = fmax(v, dpp_d<0x112, 0xf>(v));
-  v = fmax(v, dpp_d<0x114, 0xf>(v));
-  v = fmax(v, dpp_d<0x118, 0xf>(v));
-  v = fmax(v, dpp_d<0x142, 0xa>(v));
-  v = fmax(v, dpp_d<0x143, 0xc>(v));
-  const int lo = __builtin_amdgcn_readlane(__double2loint(v), 63);
-  const int hi = __builtin_amdgcn_readlane(__double2hiint(v), 63);
-  return __hiloint2double(hi, lo);
-}
-
-__device__ __forceinline__ int wave_min(int v) {
-  v = min(v, dpp<0x111, 0xf>(v));
-  v = min(v, dpp<0x112, 0xf>(v));
-  v = min(v, dpp<0x114, 0xf>(v));
-  v = min(v, dpp<0x118, 0xf>(v));
-  v = min(v, dpp<0x142, 0xa>(v));
-  v = min(v, dpp<0x143, 0xc>(v));
-  return __builtin_amdgcn_readlane(v, 63);
-}
-
 // Sum over the 64 lanes in a fixed DPP tree (lanes without a source add 0).
 template <int CTRL, int ROWS>
 __device__ __forceinline__ double dpp_d0(double v) {
@@ -136,161 +102,22 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(
   if (lane == 0) logits[(size_t)t * n + e] = total;
 }
 
-__device__ __forceinline__ double sigmoid_d(double v) {
-  return 1.0 / (1.0 + exp(-v));
-}
 
-
-__device__ __forceinline__ double readlane_d(double v, int l) {
-  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
-                          __builtin_amdgcn_readlane(__double2loint(v), l));
-}
-
-// Order-preserving map of fp32 bits to uint32 (larger float -> larger int).
-__device__ __forceinline__ uint32_t f32_order(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float f32_unorder(uint32_t o) {
-  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
-}
-
-// Round-based selection over the lane-resident keys (k wave-wide arg-max
-// rounds); the slow path, used when the candidate filter below keeps more
-// than 64 keys. Returns this lane's selection for rank `lane` (< k).
-template <int KPL>
-__device__ __forceinline__ void topk_rounds(const double (&key)[KPL],
-                                            uint64_t avail, int k, int lane,
-                                            int *sel, double *sel_key) {
-  for (int r = 0; r < k; ++r) {
-    double bk = -INFINITY;
-    int bi = -1;
-#pragma unroll
-    for (int i = 0; i < KPL; ++i)
-      if (((avail >> i) & 1) && (bi < 0 || key[i] > bk)) {
-        bk = key[i];
-        bi = i;
-      }
-    const double m = wave_max(bk);
-    int win = wave_min((bi >= 0 && bk == m) ? lane + 64 * bi : INT_MAX);
-    if (win == INT_MAX)
-      win = wave_min(avail ? lane + 64 * (int)__builtin_ctzll(avail) : INT_MAX);
-    if ((win & 63) == lane) avail &= ~(1ull << (win >> 6));
-    if (lane == r) {
-      *sel = win;
-      *sel_key = m;
-    }
-  }
-}
-
-// One wave per token. Expert e's key lives in lane e % 64, slot e / 64.
-//  1. tau = the k-th largest of the 64 lane maxima (rounded down to fp32),
-//     found bit by bit with ballot counts: at least k keys are >= tau, so
-//     the top k are among the keys >= tau (typically ~18 of 896).
-//  2. Those candidates are compacted to one per lane (mbcnt offsets), in
-//     ascending expert index.
-//  3. Each candidate's rank = number of candidates with a higher key, or an
-//     equal key and a lower index; ranks < k are the selection, in order.
-// Exactly the sort-by-(key desc, index asc) selection; no sequential rounds.
-// NaN keys rank below every number.
 template <int KPL, typename LT>
 __global__ __launch_bounds__(64) void topk_kernel(const LT *__restrict__ logits,
                                                   const float *__restrict__ bias,
                                                   int n, int k,
                                                   int32_t *__restrict__ idx,
                                                   float *__restrict__ w) {
-  __shared__ double cand_key[64];
-  __shared__ int cand_idx[64];
-  __shared__ double ranked[K3_MAX_TOPK];
+  __shared__ TopkLds tk;
   const int lane = threadIdx.x;
   const int t = blockIdx.x;
-  const LT *L = logits + (size_t)t * n;
-  LT raw[KPL];
-  float b[KPL];
-#pragma unroll
-  for (int i = 0; i < KPL; ++i) raw[i] = L[min(lane + 64 * i, n - 1)];
-  if (bias) {
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) b[i] = bias[min(lane + 64 * i, n - 1)];
-  }
-  double key[KPL];
-  uint64_t avail = 0;
-  double lmax = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < KPL; ++i) {
-    const double l = (double)raw[i];
-    double kv = bias ? sigmoid_d(l) + (double)b[i] : l;
-    if (kv != kv) kv = -INFINITY;  // NaN ranks below every number
-    key[i] = kv;
-    if (lane + 64 * i < n) {
-      avail |= 1ull << i;
-      lmax = fmax(lmax, kv);
-    }
-  }
-  // 1. k-th largest lane maximum (fp32, rounded down), MSB-first search.
-  const uint32_t um = f32_order(__double2float_rd(lmax));
-  uint32_t pre = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t c = pre | (1u << bit);
-    if (__popcll(__ballot(um >= c)) >= k) pre = c;
-  }
-  const double tau = (double)f32_unorder(pre);
-  // 2. candidates (key >= tau), positions in ascending expert index
-  int base = 0;
-  int my_pos[KPL];
-#pragma unroll
-  for (int i = 0; i < KPL; ++i) {
-    const bool c = ((avail >> i) & 1) && key[i] >= tau;
-    const uint64_t m = __ballot(c);
-    my_pos[i] = c ? base + (int)__builtin_amdgcn_mbcnt_hi(
-                               (uint32_t)(m >> 32),
-                               __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0))
-                  : -1;
-    base += __popcll(m);
-  }
-  const int C = base;
-  int sel = 0;
-  double sel_key = 0.0;
-  if (C <= 64) {
-#pragma unroll
-    for (int i = 0; i < KPL; ++i)
-      if (my_pos[i] >= 0) {
-        cand_key[my_pos[i]] = key[i];
-        cand_idx[my_pos[i]] = lane + 64 * i;
-      }
-    __syncthreads();
-    const double ck = lane < C ? cand_key[lane] : -INFINITY;
-    const int ci = lane < C ? cand_idx[lane] : INT_MAX;
-    int rank = 0;
-    for (int j = 0; j < C; ++j) {
-      const double kj = readlane_d(ck, j);
-      const int ij = __builtin_amdgcn_readlane(ci, j);
-      rank += (kj > ck || (kj == ck && ij < ci)) ? 1 : 0;
-    }
-    __syncthreads();
-    if (lane < C && rank < k) {
-      cand_idx[rank] = ci;  // every lane has read its candidate already
-      cand_key[rank] = ck;
-    }
-    __syncthreads();
-    if (lane < k) {
-      sel = cand_idx[lane];
-      sel_key = cand_key[lane];
-    }
-  } else {
-    topk_rounds<KPL>(key, avail, k, lane, &sel, &sel_key);
-  }
-  // weights from the unbiased scores, renormalised, summed in rank order
-  double logit = sel_key;  // without a bias the key is the logit itself
-  if (bias && lane < k) logit = (double)L[sel];
-  const double s = lane < k ? sigmoid_d(logit) : 0.0;
-  if (lane < k) ranked[lane] = s;
-  __syncthreads();
-  double sum = 0.0;
-  for (int j = 0; j < k; ++j) sum += ranked[j];
+  int sel;
+  float wt;
+  topk_wave<KPL, LT>(logits + (size_t)t * n, bias, n, k, tk, &sel, &wt);
   if (lane < k) {
     idx[(size_t)t * k + lane] = sel;
-    w[(size_t)t * k + lane] = (float)(s / sum);
+    w[(size_t)t * k + lane] = wt;
   }
 }
 
