@@ -152,6 +152,14 @@ k3_status k3_expert_swiglu(const uint16_t *x, const uint8_t *expert,
 k3_status k3_expert_gate_up(const uint16_t *x, const uint8_t *const *experts,
                             const int32_t *idx, int k, int hidden, int inter,
                             float *h, k3_stream_t stream);
+/* The first stage as k3_moe_layer runs it: top-k of one token's logits
+ * (device fp64 [n_experts], no bias, n_experts <= 1024; as k3_router_topk)
+ * inside the gate/up launch, writing idx int32 [k] and w fp32 [k] and
+ * h[j][inter] as k3_expert_gate_up. */
+k3_status k3_expert_gate_up_routed(const uint16_t *x, const double *logits,
+                                   const uint8_t *const *experts, int n_experts,
+                                   int k, int hidden, int inter, float *h,
+                                   int32_t *idx, float *w, k3_stream_t stream);
 k3_status k3_expert_down(const float *h, const uint8_t *const *experts,
                          const int32_t *idx, int k, int hidden, int inter,
                          float *yp, k3_stream_t stream);

@@ -38,6 +38,7 @@ SIGNATURES = [
     ("k3_mxfp4_gemv", _i, [_vp, _vp, _i, _i, _vp, _vp]),
     ("k3_expert_swiglu", _i, [_vp, _vp, _i, _i, _vp, _vp, _vp]),
     ("k3_expert_gate_up", _i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
+    ("k3_expert_gate_up_routed", _i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
     ("k3_expert_down", _i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
     ("k3_moe_combine", _i, [_vp, _vp, _i, _i, _vp, _vp, _vp]),
     ("k3_router", _i, [_vp, _vp, _i, _i, _i, _vp, _vp]),
@@ -187,6 +188,12 @@ def k3_expert_swiglu(x, expert, hidden, inter, y, h, stream=None):
 def k3_expert_gate_up(x, experts, idx, k, hidden, inter, h, stream=None):
     _call("k3_expert_gate_up", _dp(x), _dp(experts), _dp(idx), k, hidden, inter, _dp(h),
           _stream(stream))
+
+
+def k3_expert_gate_up_routed(x, logits, experts, n_experts, k, hidden, inter, h, idx, w,
+                             stream=None):
+    _call("k3_expert_gate_up_routed", _dp(x), _dp(logits), _dp(experts), n_experts, k, hidden,
+          inter, _dp(h), _dp(idx), _dp(w), _stream(stream))
 
 
 def k3_expert_down(h, experts, idx, k, hidden, inter, yp, stream=None):

@@ -400,6 +400,27 @@ k3_status k3_expert_gate_up(const uint16_t *x, const uint8_t *const *experts,
   return K3_OK;
 }
 
+k3_status k3_expert_gate_up_routed(const uint16_t *x, const double *logits,
+                                   const uint8_t *const *experts, int n_experts,
+                                   int k, int hidden, int inter, float *h,
+                                   int32_t *idx, float *w, k3_stream_t stream) {
+  const char *fn = "k3_expert_gate_up_routed";
+  K3_NEED_PTR(fn, x);
+  K3_NEED_PTR(fn, logits);
+  K3_NEED_PTR(fn, experts);
+  K3_NEED_PTR(fn, h);
+  K3_NEED_PTR(fn, idx);
+  K3_NEED_PTR(fn, w);
+  if (k3_status s = check_routing(fn, 1, n_experts, k)) return s;
+  K3_NEED(fn, n_experts <= kFusedTopkMaxExperts,
+          "%s: n_experts=%d above the %d this call ranks in one wave", fn,
+          n_experts, kFusedTopkMaxExperts);
+  if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
+  K3_LAUNCH(fn, launch_gate_up_routed(x, logits, experts, n_experts, k, hidden,
+                                      inter, h, idx, w, stream));
+  return K3_OK;
+}
+
 k3_status k3_expert_down(const float *h, const uint8_t *const *experts,
                          const int32_t *idx, int k, int hidden, int inter,
                          float *yp, k3_stream_t stream) {

@@ -40,6 +40,14 @@ def run_layer(pool, R_d, x, n, hidden, inter, k):
     yp = empty((k, hidden), torch.float32)
     y3 = empty(hidden, torch.float32)
     K.k3_expert_gate_up(xd, pool.table, idx, k, hidden, inter, h)
+    if n <= 1024:  # the layer's own first stage: top-k inside gate/up
+        h2 = empty((k, inter), torch.float32)
+        idx2 = empty(k, torch.int32)
+        w2 = empty(k, torch.float32)
+        K.k3_expert_gate_up_routed(xd, lg, pool.table, n, k, hidden, inter, h2, idx2, w2)
+        assert np.array_equal(idx2.cpu().numpy(), out["idx"])
+        assert np.array_equal(w2.cpu().numpy().view(np.uint32), out["w"].view(np.uint32))
+        assert np.array_equal(h2.cpu().numpy().view(np.uint32), h.cpu().numpy().view(np.uint32))
     K.k3_expert_down(h, pool.table, idx, k, hidden, inter, yp)
     K.k3_moe_combine(yp, w, k, hidden, None, y3)
     assert np.array_equal(y3.cpu().numpy().view(np.uint32), out["y32"].view(np.uint32))
