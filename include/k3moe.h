@@ -205,6 +205,15 @@ k3_status k3_router_topk_f32(const float *logits, const float *bias, int T,
  *             inter, k) bytes
  * k3_moe_layer_ex also writes (any may be NULL) y_f32 [hidden] (the value
  * before the bf16 cast), idx int32 [k], w fp32 [k], logits fp64 [n_experts].
+ *
+ * Four launches: router; gate/up with the top-k folded in; down with the
+ * combine folded in (two launches, down then combine, while the stream is
+ * being captured into a graph). The folded combine marks its workgroups'
+ * progress with a per-call value in the workspace, so the workspace needs
+ * no initialisation, but calls that share one workspace must not overlap.
+ * If its bounded internal wait runs out (about a second; only if the
+ * device cannot run its workgroups), it writes NaN to y_f32 and 0x7FC0
+ * (bf16 NaN) to y instead of hanging.
  * ---------------------------------------------------------------------- */
 size_t k3_moe_workspace_bytes(int T, int n_experts, int hidden, int inter,
                               int k);

@@ -7,8 +7,11 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <unistd.h>
+
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 
 #include "k3_internal.h"
 
@@ -31,7 +34,7 @@ constexpr int kMaxPairs = 1 << 20;  // T*k routing pairs of a batched call
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t logits, idx, w, h, yp, total;
+  size_t logits, idx, w, h, yp, sync, total;
 };
 
 WsLayout ws_layout(int T, int n, int hidden, int inter, int k) {
@@ -47,8 +50,24 @@ WsLayout ws_layout(int T, int n, int hidden, int inter, int k) {
   off += align256((size_t)T * k * inter * sizeof(float));
   L.yp = off;
   off += align256((size_t)T * k * hidden * sizeof(float));
+  L.sync = off;
+  off += align256((size_t)kMaxSyncGrid * sizeof(uint64_t));
   L.total = off;
   return L;
+}
+
+// Per-call values of the layer's arrival slots: unique in the process (a
+// counter) and unlikely to equal leftover memory (a random start).
+uint64_t next_layer_seq() {
+  static std::atomic<uint64_t> seq{[] {
+    uint64_t z = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() ^
+                 ((uint64_t)getpid() << 32);
+    z += 0x9E3779B97F4A7C15ull;  // splitmix64 finaliser
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return (z ^ (z >> 31)) >> 8;
+  }()};
+  return seq.fetch_add(1, std::memory_order_relaxed) * 4;
 }
 
 // Permutation scratch of T*k pairs (after the caller's counts, offsets,
@@ -543,9 +562,20 @@ k3_status k3_moe_layer_ex(const uint16_t *x, const uint16_t *router_w,
     K3_LAUNCH(fn, launch_gate_up(x, experts, ix, nullptr, k, hidden, inter, h,
                                  stream));
   }
-  K3_LAUNCH(fn, launch_down(h, experts, ix, nullptr, k, hidden, inter, yp,
-                            stream));
-  K3_LAUNCH(fn, launch_combine(yp, wt, k, hidden, y, y_f32, stream));
+  // Down and combine in one launch, marked by a per-call value; a graph
+  // being captured would replay one value, so it gets the two launches.
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) == hipSuccess &&
+      cap == hipStreamCaptureStatusNone &&
+      down_combine_grid(k, hidden, inter) <= (unsigned)kMaxSyncGrid) {
+    K3_LAUNCH(fn, launch_down_combine(h, experts, ix, wt, k, hidden, inter, yp,
+                                      reinterpret_cast<uint64_t *>(base + L.sync),
+                                      next_layer_seq(), y, y_f32, stream));
+  } else {
+    K3_LAUNCH(fn, launch_down(h, experts, ix, nullptr, k, hidden, inter, yp,
+                              stream));
+    K3_LAUNCH(fn, launch_combine(yp, wt, k, hidden, y, y_f32, stream));
+  }
   return K3_OK;
 }
 

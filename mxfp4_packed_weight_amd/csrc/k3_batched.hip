@@ -22,8 +22,6 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
 }
 
-__device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
-
 // Inclusive prefix sum over the block's 1024 threads (wave scans + LDS).
 __device__ int block_scan_incl(int v, int *tmp) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;

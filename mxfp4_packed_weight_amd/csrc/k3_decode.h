@@ -170,6 +170,8 @@ __device__ __forceinline__ void wg_range(int total, int *t0, int *t1) {
   *t1 = (int)((b + 1) * total / n);
 }
 
+__device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu))

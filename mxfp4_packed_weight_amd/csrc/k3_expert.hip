@@ -12,6 +12,7 @@
 // convention"). The work is a memory-bound stream of packed bytes ("the wait
 // is for bytes to arrive", [SAT] "Reduction one").
 #include "k3_stream.h"
+#include "k3_sync.h"
 #include "k3_topk.h"
 
 namespace k3 {
@@ -41,8 +42,6 @@ __global__ __launch_bounds__(kThreads) void gemv_f32_kernel(
       },
       part);
 }
-
-__device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
 
 __device__ __forceinline__ const uint8_t *expert_base(
     const uint8_t *const *__restrict__ experts, const int32_t *__restrict__ idx,
@@ -78,7 +77,9 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(
       part);
 }
 
-// yp[j][r] = W_down(e_j)[r] . h[j], tiles of the k slots back to back.
+// yp[j][r] = W_down(e_j)[r] . h[j], tiles of the k slots back to back (a
+// workgroup's tiles share one or two slots, so its activations stay within
+// the scalar cache).
 __global__ __launch_bounds__(kThreads) void down_kernel(
     const float *__restrict__ h, const uint8_t *const *__restrict__ experts,
     const int32_t *__restrict__ idx, const uint8_t *__restrict__ single,
@@ -105,32 +106,23 @@ __global__ __launch_bounds__(kThreads) void down_kernel(
 }
 
 // The decode layer's first expert stage with the selection folded in:
-// every workgroup ranks the token's n logits itself (the same selection
-// everywhere, so no grid-wide step is needed), workgroup 0 publishes idx
-// and w, then the tiles of the k selected experts' gate/up stacks are
-// streamed as in gate_up_kernel. One launch fewer than a separate top-k.
+// every workgroup ranks the token's n logits itself with all of its waves
+// (topk_wg: the same selection everywhere, so no grid-wide step is needed),
+// workgroup 0 publishes idx and w, then the tiles of the k selected
+// experts' gate/up stacks are streamed as in gate_up_kernel. One launch
+// fewer than a separate top-k.
 __global__ __launch_bounds__(kThreads) void gate_up_routed_kernel(
     const uint16_t *__restrict__ x, const double *__restrict__ logits,
     const uint8_t *const *__restrict__ experts, int n, int k, int hidden,
     int inter, float *__restrict__ h, int32_t *__restrict__ idx_out,
     float *__restrict__ w_out) {
   __shared__ float part[kPartFloats];
-  __shared__ TopkLds tk;
-  __shared__ int sel[K3_MAX_TOPK];
-  if (wave_id() == 0) {
-    int e;
-    float wt;
-    topk_wave<kFusedTopkMaxExperts / 64, double>(logits, nullptr, n, k, tk, &e, &wt);
-    const int lane = threadIdx.x & 63;
-    if (lane < k) {
-      sel[lane] = e;
-      if (blockIdx.x == 0) {
-        idx_out[lane] = e;
-        w_out[lane] = wt;
-      }
-    }
+  __shared__ TopkWgLds tk;
+  topk_wg<kNW>(logits, n, k, tk);
+  if (blockIdx.x == 0 && threadIdx.x < k) {
+    idx_out[threadIdx.x] = tk.sel[threadIdx.x];
+    w_out[threadIdx.x] = tk.wt[threadIdx.x];
   }
-  __syncthreads();
   const ExpertLayout L = expert_layout(hidden, inter);
   const int T = L.gu.ntiles;
   const uint32_t *xp = reinterpret_cast<const uint32_t *>(x);
@@ -139,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_routed_kernel(
   run_rows(
       t0, t1, L.gu.G, L.gu.G4,
       [&](int t) {
-        const int e = __builtin_amdgcn_readfirstlane(sel[t / T]);
+        const int e = __builtin_amdgcn_readfirstlane(tk.sel[t / T]);
         return ldc(experts + e) + (size_t)(t % T) * L.gu.tile_bytes;
       },
       [&](u32x4 w, int g, int) { return group_dot_bf16(w, xp + (size_t)16 * g); },
@@ -150,6 +142,73 @@ __global__ __launch_bounds__(kThreads) void gate_up_routed_kernel(
         if (lane < 32 && row < inter) h[(size_t)(t / T) * inter + row] = silu(s) * u;
       },
       part);
+}
+
+// The decode layer's last stage: down projection and weighted combine in
+// one launch. The down tiles are those of down_kernel on the same grid;
+// their partials go out with device-coherent stores, and each workgroup
+// then marks its arrival slot with the call's value `val`. Row tile r's
+// partials are tiles s * T + r (s < k); the workgroup that owns the last
+// one (slot k - 1) waits for the owners of the others and sums them in rank
+// order exactly as combine_kernel, so the bits equal down_kernel followed by
+// combine_kernel. Every workgroup waited for has a lower index and waits
+// for nothing itself, so the waits end even if the grid is not all resident
+// at once; a wait that still runs out (~1 s) makes the call write NaN.
+__global__ __launch_bounds__(kThreads) void down_combine_kernel(
+    const float *__restrict__ h, const uint8_t *const *__restrict__ experts,
+    const int32_t *__restrict__ idx, const float *__restrict__ w, int k,
+    int hidden, int inter, float *yp, uint64_t *slots, uint64_t val,
+    uint16_t *__restrict__ y, float *__restrict__ y_f32) {
+  __shared__ float part[kPartFloats];
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = 0;
+  const ExpertLayout L = expert_layout(hidden, inter);
+  const int T = L.down.ntiles, total = k * T;
+  int t0, t1;
+  wg_range(total, &t0, &t1);
+  run_rows(
+      t0, t1, L.down.G, L.down.G4,
+      [&](int t) {
+        return ldc(experts + ldc(idx + t / T)) + L.down_offset +
+               (size_t)(t % T) * L.down.tile_bytes;
+      },
+      [&](u32x4 wv, int g, int t) {
+        return group_dot_f32(wv, h + (size_t)(t / T) * inter + (size_t)32 * g);
+      },
+      [&](int t, int lane, float s) {
+        const int row = (t % T) * kTileRows + lane;
+        if (row < hidden) st_dev(yp + (size_t)(t / T) * hidden + row, s);
+      },
+      part);
+  arrive(slots, val);
+  const int lane = threadIdx.x & 63;
+  const int last = (k - 1) * T;
+  const int r_lo = max(t0 - last, 0), r_hi = min(t1 - last, T);
+  for (int r = r_lo + wave_id(); r < r_hi; r += kNW) {
+    const int owner = lane < k ? tile_owner(lane * T + r, total, gridDim.x) : 0;
+    if (!wave_wait_owners(slots, owner, k, val) && lane == 0) bad = 1;
+    const int row = r * kTileRows + lane;
+    if (row < hidden) {
+      float acc = 0.f;
+      for (int j0 = 0; j0 < k; j0 += 16) {  // as combine_kernel
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          v[j] = j0 + j < k ? ld_dev(yp + (size_t)(j0 + j) * hidden + row) : 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (j0 + j < k) acc = fmaf(w[j0 + j], v[j], acc);
+      }
+      if (y_f32) y_f32[row] = acc;
+      if (y) y[row] = f32_to_bf16_rne(acc);
+    }
+  }
+  __syncthreads();
+  if (bad)  // the outputs cannot be trusted: say so in them
+    for (int i = threadIdx.x; i < hidden; i += kThreads) {
+      if (y_f32) y_f32[i] = __builtin_nanf("");
+      if (y) y[i] = 0x7FC0;
+    }
 }
 
 // y[i] = sum_j w[j] * yp[j][i] in rank order j = 0..k-1, then bf16 (RNE).
@@ -221,6 +280,23 @@ hipError_t launch_gate_up_routed(const uint16_t *x, const double *logits,
                      dim3(kThreads), 0, s, x, logits, experts, n, k, hidden,
                      inter, h, idx, w);
   return hipGetLastError();
+}
+
+hipError_t launch_down_combine(const float *h, const uint8_t *const *experts,
+                               const int32_t *idx, const float *w, int k,
+                               int hidden, int inter, float *yp,
+                               uint64_t *slots, uint64_t val, uint16_t *y,
+                               float *y_f32, hipStream_t s) {
+  const ExpertLayout L = expert_layout(hidden, inter);
+  hipLaunchKernelGGL(down_combine_kernel,
+                     dim3(grid_for_tiles(k * L.down.ntiles)), dim3(kThreads),
+                     0, s, h, experts, idx, w, k, hidden, inter, yp, slots, val,
+                     y, y_f32);
+  return hipGetLastError();
+}
+
+unsigned down_combine_grid(int k, int hidden, int inter) {
+  return grid_for_tiles(k * expert_layout(hidden, inter).down.ntiles);
 }
 
 hipError_t launch_combine(const float *yp, const float *w, int k, int hidden,

@@ -147,6 +147,17 @@ struct TopkLds {
   double ranked[K3_MAX_TOPK];
 };
 constexpr int kFusedTopkMaxExperts = 16 * 64;  // n handled by the fused path
+// LDS of the workgroup-parallel top-k (one expert per thread, n <= 1024).
+struct TopkWgLds {
+  uint32_t okey[kFusedTopkMaxExperts];  // keys as ordered fp32 (rounded down)
+  int gt[64], ge[64], rank[64], wave_cnt[16];
+  double cand_key[64];
+  int cand_idx[64];
+  double sel_key[K3_MAX_TOPK], ranked[K3_MAX_TOPK];
+  int sel[K3_MAX_TOPK];
+  float wt[K3_MAX_TOPK];
+  TopkLds tk;  // the single-wave fallback
+};
 // The decode layer's first expert stage with top-k folded in (k3_expert.hip).
 hipError_t launch_gate_up_routed(const uint16_t *x, const double *logits,
                                  const uint8_t *const *experts, int n, int k,
@@ -154,6 +165,16 @@ hipError_t launch_gate_up_routed(const uint16_t *x, const double *logits,
                                  float *w, hipStream_t s);
 hipError_t launch_combine(const float *yp, const float *w, int k, int hidden,
                           uint16_t *y, float *y_f32, hipStream_t s);
+// Down + combine in one launch (the decode layer's last stage). slots: one
+// arrival word per workgroup (down_combine_grid of them, at most
+// kMaxSyncGrid); val: this call's value, never reused in the process.
+constexpr int kMaxSyncGrid = 1024;
+unsigned down_combine_grid(int k, int hidden, int inter);
+hipError_t launch_down_combine(const float *h, const uint8_t *const *experts,
+                               const int32_t *idx, const float *w, int k,
+                               int hidden, int inter, float *yp,
+                               uint64_t *slots, uint64_t val, uint16_t *y,
+                               float *y_f32, hipStream_t s);
 hipError_t launch_router(const uint16_t *x, const uint16_t *R, int T,
                          int hidden, int n, double *logits, hipStream_t s);
 hipError_t launch_topk_f64(const double *logits, const float *bias, int T,

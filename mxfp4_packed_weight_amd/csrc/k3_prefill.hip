@@ -92,8 +92,6 @@ __global__ __launch_bounds__(256) void quant_kernel(const T *__restrict__ v,
   if (i == 0) sc[r * G + g] = (uint8_t)e;
 }
 
-__device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
-
 struct PfItems {
   const int32_t *e, *off, *cnt, *n;
 };

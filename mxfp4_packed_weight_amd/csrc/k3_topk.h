@@ -5,15 +5,17 @@
 //  1. tau = the k-th largest of the 64 lane maxima (rounded down to fp32),
 //     found bit by bit with ballot counts: at least k keys are >= tau, so
 //     the top k are among the keys >= tau (typically ~18 of 896).
-//  2. Those candidates are compacted to one per lane (mbcnt offsets), in
-//     ascending expert index.
+//  2. Those candidates are packed into LDS (per-lane counts, a prefix sum
+//     from ballots of the count bits).
 //  3. Each candidate's rank = number of candidates with a higher key, or an
 //     equal key and a lower index; ranks < k are the selection, in order.
-// Exactly the sort-by-(key desc, index asc) selection; no sequential rounds.
-// NaN keys rank below every number. The routing bias only changes the keys;
-// the weights always come from the unbiased sigmoid scores ([ZOR] "How is the
-// C engine actually built?", invariant 3), renormalised to sum to one,
-// summed in rank order.
+// Exactly the sort-by-(key desc, index asc) selection. topk_wg does the
+// same with a whole workgroup, one expert per thread, for the decode layer,
+// where every workgroup waits for the selection. NaN keys rank below every
+// number. The
+// routing bias only changes the keys; the weights always come from the
+// unbiased sigmoid scores ([ZOR] "How is the C engine actually built?",
+// invariant 3), renormalised to sum to one, summed in rank order.
 #pragma once
 
 #include <limits.h>
@@ -111,18 +113,18 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Top-k of one token's n logits by one wave (any wave of a workgroup). On
-// return lanes < k of the wave hold the j-th selection in *sel and its
-// renormalised weight in *wt (rank order). `tk` is that wave's LDS scratch.
-template <int KPL, typename LT>
-__device__ __forceinline__ void topk_wave(const LT *__restrict__ L, const float *__restrict__ bias,
-                          int n, int k, TopkLds &tk, int *sel_out,
-                          float *wt_out) {
+// Top-k of one token's n logits held in registers by one wave: raw[i] is the
+// logit of expert lane + 64 i (entries at or past n are ignored). On return
+// lanes < k hold the j-th selection in *sel_out and its renormalised weight
+// in *wt_out (rank order). `tk` is the wave's LDS scratch; with a bias,
+// logit_of(e) returns expert e's logit (the weights use unbiased scores).
+template <int KPL, typename LT, class LogitOf>
+__device__ __forceinline__ void topk_core(const LT (&raw)[KPL],
+                                          const float *__restrict__ bias, int n,
+                                          int k, TopkLds &tk, LogitOf logit_of,
+                                          int *sel_out, float *wt_out) {
   const int lane = threadIdx.x & 63;
-  LT raw[KPL];
   float b[KPL];
-#pragma unroll
-  for (int i = 0; i < KPL; ++i) raw[i] = L[min(lane + 64 * i, n - 1)];
   if (bias) {
 #pragma unroll
     for (int i = 0; i < KPL; ++i) b[i] = bias[min(lane + 64 * i, n - 1)];
@@ -141,7 +143,7 @@ __device__ __forceinline__ void topk_wave(const LT *__restrict__ L, const float 
       lmax = fmax(lmax, kv);
     }
   }
-  // 1. k-th largest lane maximum (fp32, rounded down), MSB-first search.
+  // 1. tau = k-th largest lane maximum (fp32, rounded down), MSB first.
   const uint32_t um = f32_order(__double2float_rd(lmax));
   uint32_t pre = 0;
   for (int bit = 31; bit >= 0; --bit) {
@@ -149,28 +151,32 @@ __device__ __forceinline__ void topk_wave(const LT *__restrict__ L, const float 
     if (__popcll(__ballot(um >= c)) >= k) pre = c;
   }
   const double tau = (double)f32_unorder(pre);
-  // 2. candidates (key >= tau), positions in ascending expert index
-  int base = 0;
-  int my_pos[KPL];
+  // 2. candidates (key >= tau): per-lane count, exclusive prefix over lanes
+  //    from one ballot per count bit, then packed into LDS.
+  uint64_t cmask = 0;
 #pragma unroll
-  for (int i = 0; i < KPL; ++i) {
-    const bool c = ((avail >> i) & 1) && key[i] >= tau;
-    const uint64_t m = __ballot(c);
-    my_pos[i] = c ? base + (int)__builtin_amdgcn_mbcnt_hi(
-                               (uint32_t)(m >> 32),
-                               __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0))
-                  : -1;
-    base += __popcll(m);
+  for (int i = 0; i < KPL; ++i)
+    if (((avail >> i) & 1) && key[i] >= tau) cmask |= 1ull << i;
+  const int cnt = __popcll(cmask);
+  int base = 0, C = 0;
+#pragma unroll
+  for (int bit = 0; bit < 7; ++bit) {  // cnt <= KPL <= 64
+    const uint64_t m = __ballot((cnt >> bit) & 1);
+    base += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0))
+            << bit;
+    C += __popcll(m) << bit;
   }
-  const int C = base;
   int sel = 0;
   double sel_key = 0.0;
   if (C <= 64) {
+    int at = base;
 #pragma unroll
     for (int i = 0; i < KPL; ++i)
-      if (my_pos[i] >= 0) {
-        tk.cand_key[my_pos[i]] = key[i];
-        tk.cand_idx[my_pos[i]] = lane + 64 * i;
+      if ((cmask >> i) & 1) {
+        tk.cand_key[at] = key[i];
+        tk.cand_idx[at] = lane + 64 * i;
+        ++at;
       }
     wave_lds_sync();
     const double ck = lane < C ? tk.cand_key[lane] : -INFINITY;
@@ -196,7 +202,7 @@ __device__ __forceinline__ void topk_wave(const LT *__restrict__ L, const float 
   }
   // weights from the unbiased scores, renormalised, summed in rank order
   double logit = sel_key;  // without a bias the key is the logit itself
-  if (bias && lane < k) logit = (double)L[sel];
+  if (bias && lane < k) logit = logit_of(sel);
   const double s = lane < k ? sigmoid_d(logit) : 0.0;
   if (lane < k) tk.ranked[lane] = s;
   wave_lds_sync();
@@ -204,6 +210,136 @@ __device__ __forceinline__ void topk_wave(const LT *__restrict__ L, const float 
   for (int j = 0; j < k; ++j) sum += tk.ranked[j];
   *sel_out = sel;
   *wt_out = (float)(s / sum);
+}
+
+// The same with the logits read from memory (L[e], e < n).
+template <int KPL, typename LT>
+__device__ __forceinline__ void topk_wave(const LT *__restrict__ L,
+                                          const float *__restrict__ bias, int n,
+                                          int k, TopkLds &tk, int *sel_out,
+                                          float *wt_out) {
+  const int lane = threadIdx.x & 63;
+  LT raw[KPL];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) raw[i] = L[min(lane + 64 * i, n - 1)];
+  topk_core<KPL, LT>(raw, bias, n, k, tk, [&](int e) { return (double)L[e]; },
+                     sel_out, wt_out);
+}
+
+// Top-k of one token's n <= blockDim logits by a whole workgroup (16 waves),
+// one expert per thread: the selection and weights of topk_core, with the
+// three steps spread over the waves so that no single wave walks the keys.
+//   1. tau: the k-th largest of the 64 column maxima (column = e % 64):
+//      each wave computes the maxima, compares every column with 4 others
+//      and adds its counts into LDS; the column with fewer than k above it
+//      and at least k at or above it holds tau.
+//   2. candidates (key >= tau) are packed per wave with ballots, wave
+//      offsets from LDS.
+//   3. each wave ranks every candidate against 4 others; the counts add up
+//      in LDS to the exact (key desc, index asc) rank.
+// More than 64 candidates (many equal keys) take topk_core on wave 0.
+// Result in s.sel / s.wt (rank order, lanes < k) after a barrier.
+template <int NWAVES>
+__device__ void topk_wg(const double *__restrict__ L, int n, int k, TopkWgLds &s) {
+  static_assert(NWAVES * 4 >= 64, "each wave compares against 4 columns");
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  double key = -INFINITY;
+  if (t < n) {
+    key = L[t];
+    if (key != key) key = -INFINITY;  // NaN ranks below every number
+  }
+  s.okey[t] = f32_order(__double2float_rd(key));
+  if (t < 64) {
+    s.gt[t] = 0;
+    s.ge[t] = 0;
+    s.rank[t] = 0;
+  }
+  __syncthreads();
+  // 1. column maxima (each wave, redundantly), then 4 comparisons per lane.
+  uint32_t um = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVES; ++i) um = max(um, s.okey[lane + 64 * i]);
+  {
+    int gt = 0, ge = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t v = __builtin_amdgcn_readlane(um, 4 * w + j);
+      gt += v > um ? 1 : 0;
+      ge += v >= um ? 1 : 0;
+    }
+    atomicAdd(&s.gt[lane], gt);
+    atomicAdd(&s.ge[lane], ge);
+  }
+  __syncthreads();
+  const uint64_t holds = __ballot(s.gt[lane] < k && s.ge[lane] >= k);
+  const double tau = (double)f32_unorder(
+      __builtin_amdgcn_readlane(um, (int)__builtin_ctzll(holds)));
+  // 2. candidates, packed in wave order.
+  const bool cand = t < n && key >= tau;
+  const uint64_t m = __ballot(cand);
+  if (lane == 0) s.wave_cnt[w] = __popcll(m);
+  __syncthreads();
+  int base = 0, C = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVES; ++i) {
+    const int c = s.wave_cnt[i];
+    base += i < w ? c : 0;
+    C += c;
+  }
+  if (C <= 64) {
+    if (cand) {
+      const int at = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                (uint32_t)(m >> 32),
+                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+      s.cand_key[at] = key;
+      s.cand_idx[at] = t;
+    }
+    __syncthreads();
+    // 3. candidate `lane` against candidates 4w .. 4w + 3.
+    if (lane < C) {
+      const double ck = s.cand_key[lane];
+      const int ci = s.cand_idx[lane];
+      int r = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int q = 4 * w + j;
+        if (q < C) {
+          const double kq = s.cand_key[q];
+          const int iq = s.cand_idx[q];
+          r += (kq > ck || (kq == ck && iq < ci)) ? 1 : 0;
+        }
+      }
+      if (r) atomicAdd(&s.rank[lane], r);
+    }
+    __syncthreads();
+    if (w == 0) {
+      if (lane < C) {
+        const int r = s.rank[lane];
+        if (r < k) {
+          s.sel[r] = s.cand_idx[lane];
+          s.sel_key[r] = s.cand_key[lane];
+        }
+      }
+      wave_lds_sync();
+      // weights from the scores, renormalised, summed in rank order (as
+      // topk_core without a bias: the key is the logit)
+      const double sc = lane < k ? sigmoid_d(s.sel_key[lane]) : 0.0;
+      if (lane < k) s.ranked[lane] = sc;
+      wave_lds_sync();
+      double sum = 0.0;
+      for (int j = 0; j < k; ++j) sum += s.ranked[j];
+      if (lane < k) s.wt[lane] = (float)(sc / sum);
+    }
+  } else if (w == 0) {
+    int e;
+    float wt;
+    topk_wave<kFusedTopkMaxExperts / 64, double>(L, nullptr, n, k, s.tk, &e, &wt);
+    if (lane < k) {
+      s.sel[lane] = e;
+      s.wt[lane] = wt;
+    }
+  }
+  __syncthreads();
 }
 
 }  // namespace k3

@@ -4,7 +4,13 @@ size (15.7 GB of packed experts resident), plus small layers covering k = 1,
 k = n and ragged expert shapes. y (fp32 before the cast): normwise <= 1e-5;
 top-k indices bit-exact; weights within 1e-6; the bf16 cast bit-exact
 against round-to-nearest-even of the GPU's own fp32 y; reruns
-bit-identical; the stage-by-stage calls give the same bits as the layer."""
+bit-identical; the stage-by-stage calls give the same bits as the layer.
+
+The layer's last launch folds the combine into the down projection (its
+workgroups hand partials over through arrival slots marked with a per-call
+value); the stage-by-stage calls run down and combine as two launches. Both
+must give identical bits, also on workspaces that start as random bytes and
+over runs of calls with changing tokens on one workspace."""
 import numpy as np
 import pytest
 
@@ -52,6 +58,45 @@ def run_layer(pool, R_d, x, n, hidden, inter, k):
     K.k3_moe_combine(yp, w, k, hidden, None, y3)
     assert np.array_equal(y3.cpu().numpy().view(np.uint32), out["y32"].view(np.uint32))
     return out
+
+
+def layer_outputs(pool, R_d, xd, n, hidden, inter, k, ws):
+    import torch
+    y = empty(hidden, torch.int16)
+    y32 = empty(hidden, torch.float32)
+    idx = empty(k, torch.int32)
+    w = empty(k, torch.float32)
+    lg = empty(n, torch.float64)
+    K.k3_moe_layer_ex(xd, R_d, pool.table, n, hidden, inter, k, y, ws, y_f32=y32, idx=idx, w=w,
+                      logits=lg)
+    return dict(y=y.cpu().numpy().view(np.uint16), y32=y32.cpu().numpy(),
+                idx=idx.cpu().numpy(), w=w.cpu().numpy(), logits=lg.cpu().numpy())
+
+
+def stage_outputs(pool, R_d, xd, n, hidden, inter, k):
+    """The layer as separate public calls: router, routed gate/up, down,
+    combine (two launches where the layer folds them into one)."""
+    import torch
+    lg = empty(n, torch.float64)
+    h = empty((k, inter), torch.float32)
+    idx = empty(k, torch.int32)
+    w = empty(k, torch.float32)
+    yp = empty((k, hidden), torch.float32)
+    y = empty(hidden, torch.int16)
+    y32 = empty(hidden, torch.float32)
+    K.k3_router(xd, R_d, 1, hidden, n, lg)
+    K.k3_expert_gate_up_routed(xd, lg, pool.table, n, k, hidden, inter, h, idx, w)
+    K.k3_expert_down(h, pool.table, idx, k, hidden, inter, yp)
+    K.k3_moe_combine(yp, w, k, hidden, y, y32)
+    return dict(y=y.cpu().numpy().view(np.uint16), y32=y32.cpu().numpy(),
+                idx=idx.cpu().numpy(), w=w.cpu().numpy(), logits=lg.cpu().numpy())
+
+
+def assert_same(a, b):
+    for key in ("y", "idx"):
+        assert np.array_equal(a[key], b[key]), key
+    for key in ("y32", "w", "logits"):
+        assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key
 
 
 def check_against_oracle(out, x, R, seed, cfg, n, hidden, inter, k, elo, ehi):
@@ -104,3 +149,42 @@ def test_decode_layer_small(n, hidden, inter, k):
     x = gen.normal_bf16(gen.key(seed, cfg, gen.KIND_TOKENS), hidden)
     out = run_layer(pool, up(R), x, n, hidden, inter, k)
     check_against_oracle(out, x, R, seed, cfg, n, hidden, inter, k, 114, 120)
+
+
+def test_layer_over_many_tokens_on_one_workspace():
+    """Twenty calls in a row on one workspace that starts as random bytes,
+    a new token each time (every call must wait on its own arrival values,
+    not on a previous call's); each compared bit for bit with the
+    stage-by-stage calls, and the first and last with the oracle."""
+    import torch
+    cfg, seed, n, hidden, inter, k = 74, 8, 48, 384, 224, 8
+    say("layer: 20 tokens on one random-filled workspace")
+    pool = D.build_expert_pool(seed, cfg, n, hidden, inter, 114, 120, workers=2)
+    R = gen.normal_bf16(gen.key(seed, cfg, gen.KIND_ROUTER), n * hidden, 0, 0.02).reshape(
+        n, hidden)
+    R_d = up(R)
+    nb = K.k3_moe_workspace_bytes(1, n, hidden, inter, k)
+    ws = up(np.random.default_rng(1).integers(0, 256, nb, dtype=np.uint8))
+    X = W.tokens_bf16(seed, cfg, 20, hidden)
+    for t in range(20):
+        xd = up(X[t])
+        out = layer_outputs(pool, R_d, xd, n, hidden, inter, k, ws)
+        assert_same(out, stage_outputs(pool, R_d, xd, n, hidden, inter, k))
+        if t in (0, 19):
+            check_against_oracle(out, X[t], R, seed, cfg, n, hidden, inter, k, 114, 120)
+
+
+def test_layer_c3_tokens_in_a_row(c3_pool):
+    """Eight C3 tokens back to back on one workspace, each bit-identical to the
+    stage-by-stage calls (the full-size grid: 768 gate/up and 1792 down
+    tiles)."""
+    import torch
+    pool, R, R_d = c3_pool
+    n, hidden, inter, k = W.N_EXPERTS, W.HIDDEN, W.INTER, W.TOPK
+    ws = empty(K.k3_moe_workspace_bytes(1, n, hidden, inter, k), torch.uint8)
+    X = W.tokens_bf16(0, W.C3, 8, hidden, batch=5)
+    say("layer: 8 C3 tokens in a row")
+    for t in range(8):
+        xd = up(X[t])
+        out = layer_outputs(pool, R_d, xd, n, hidden, inter, k, ws)
+        assert_same(out, stage_outputs(pool, R_d, xd, n, hidden, inter, k))
