@@ -31,7 +31,6 @@ sys.path.insert(0, ROOT)
 METRIC = "effective HBM GB/s of MXFP4 expert weights (% of 8 TB/s); MoE-layer tokens/s"
 PEAK_HBM_GBS = 8000.0
 BYTES_PER_EXPERT = 17547264            # 3 x 7168 x 1536 weights at 0.53125 B
-GATE_UP_BYTES_PER_EXPERT = 11698176    # 2 x 1536 x 7168 x 0.53125
 ROUTER_BYTES = 896 * 7168 * 2
 
 
@@ -143,21 +142,20 @@ def main():
     value = expert_bytes / (ms_per_step * 1e-3) / 1e9
     log(f"layer: {ms_per_step * 1e3:.2f} us/step, {value:.1f} GB/s expert weights")
 
-    # Dominant kernel: the layer's first stage (top-k of the token's logits
-    # inside the gate/up + SwiGLU stream over the 16 selected experts), the
-    # same kernel the layer launches, timed on fresh tokens' logits with HIP
-    # events on the same stream.
+    # Dominant kernel: the layer's expert launch (top-k of the token's
+    # logits, gate/up + SwiGLU, down and combine over the 16 selected
+    # experts), the same kernel the layer launches after its router, timed
+    # alone on fresh tokens' logits with HIP events on the same stream.
     T = args.tokens
     lg = torch.empty((T, n), dtype=torch.float64, device=dev)
     K.k3_router(bank, R, T, hidden, n, lg)
-    h = torch.empty((k, inter), dtype=torch.float32, device=dev)
-    idx = torch.empty(k, dtype=torch.int32, device=dev)
-    w = torch.empty(k, dtype=torch.float32, device=dev)
+    wsx = torch.empty(K.k3_moe_batched_workspace_bytes(1, n, hidden, inter, k),
+                      dtype=torch.uint8, device=dev)
     reps = max(args.steps, 50)
 
     def stage(i):
-        K.k3_expert_gate_up_routed(bank[i % T], lg[i % T], pool.table, n, k, hidden, inter, h,
-                                   idx, w, stream=stream)
+        K.k3_moe_layer_from_logits(bank[i % T], lg[i % T], None, pool.table, n, hidden, inter,
+                                   k, 1, y, wsx, stream=stream)
 
     for i in range(10):
         stage(i)
@@ -167,13 +165,14 @@ def main():
         stage(i)
     ev1.record(stream)
     torch.cuda.synchronize()
-    gu_us = ev0.elapsed_time(ev1) / reps * 1e3
-    gu_bytes = k * GATE_UP_BYTES_PER_EXPERT
-    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
-    log(f"top-k + gate/up stage: {gu_us:.2f} us/launch, {achieved:.1f} GB/s")
+    ex_us = ev0.elapsed_time(ev1) / reps * 1e3
+    ex_bytes = k * BYTES_PER_EXPERT
+    achieved = ex_bytes / (ex_us * 1e-6) / 1e9
+    log(f"expert launch (top-k, gate/up, down, combine): {ex_us:.2f} us/launch, "
+        f"{achieved:.1f} GB/s")
 
     traffic = None
-    tpath = os.path.join(ROOT, "profiles", "gate_up_c3_traffic.json")
+    tpath = os.path.join(ROOT, "profiles", TRAFFIC_JSON)
     if os.path.exists(tpath):
         with open(tpath) as f:
             tr = json.load(f)
@@ -202,11 +201,12 @@ def main():
         "tokens_per_s": round(1e3 / ms_per_step, 1),
         "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "all_bytes_GBs": round((expert_bytes + ROUTER_BYTES) / (ms_per_step * 1e-3) / 1e9, 2),
-        "roofline": {"kernel": "gate_up_routed_kernel (top-k + gate/up, k3_expert_gate_up_routed)",
+        "roofline": {"kernel": "moe_experts_kernel (top-k, gate/up, down, combine; "
+                               "k3_moe_layer_from_logits with T = 1)",
                      "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "launch_us": round(gu_us, 3), "algorithmic_bytes_per_launch": gu_bytes},
+                     "launch_us": round(ex_us, 3), "algorithmic_bytes_per_launch": ex_bytes},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -418,7 +418,8 @@ def bench_c5(args):
 
 
 CALIB_BYTES = 1 << 30
-GATE_UP_KERNEL = "gate_up_routed_kernel"
+DOMINANT_KERNEL = "moe_experts_kernel"
+TRAFFIC_JSON = "experts_c3_traffic.json"
 
 
 def _pmc_rows(path, counter):
@@ -436,26 +437,26 @@ def _pmc_rows(path, counter):
 
 
 def traffic_summary(fetch_csv, write_csv):
-    """HBM bytes per gate/up launch from FETCH_SIZE and WRITE_SIZE (KiB per
+    """HBM bytes per expert launch from FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch), each scaled by what the counter reads for the 1 GiB calibration
     copy (CALIB_BYTES read and CALIB_BYTES written)."""
-    out = {"kernel": GATE_UP_KERNEL, "kernel_source_hash": _kernel_hash(),
+    out = {"kernel": DOMINANT_KERNEL, "kernel_source_hash": _kernel_hash(),
            "calibration": f"device-to-device copy of {CALIB_BYTES} bytes",
-           "algorithmic_bytes_per_launch": 16 * GATE_UP_BYTES_PER_EXPERT}
+           "algorithmic_bytes_per_launch": 16 * BYTES_PER_EXPERT}
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _pmc_rows(path, name)
-        gu = [v for k, g, v in rows if GATE_UP_KERNEL in k]
+        gu = [v for k, g, v in rows if DOMINANT_KERNEL in k]
         calib = [v for k, g, v in rows if "copy" in k.lower()]
         calib = sorted(calib)[-3:]  # the three largest copies are the calibration
         if not gu or not calib:
-            raise SystemExit(f"{path}: no {GATE_UP_KERNEL} or calibration dispatches")
+            raise SystemExit(f"{path}: no {DOMINANT_KERNEL} or calibration dispatches")
         factor = (sum(calib) / len(calib)) * 1024.0 / CALIB_BYTES
-        out[name] = {"gate_up_kib_mean": sum(gu) / len(gu), "dispatches": len(gu),
+        out[name] = {"kernel_kib_mean": sum(gu) / len(gu), "dispatches": len(gu),
                      "calib_kib_mean": sum(calib) / len(calib), "scale": factor,
                      "bytes_per_launch": sum(gu) / len(gu) * 1024.0 / factor}
     out["bytes_per_launch"] = out["FETCH_SIZE"]["bytes_per_launch"] + \
         out["WRITE_SIZE"]["bytes_per_launch"]
-    path = os.path.join(ROOT, "profiles", "gate_up_c3_traffic.json")
+    path = os.path.join(ROOT, "profiles", TRAFFIC_JSON)
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
@@ -464,7 +465,7 @@ def traffic_summary(fetch_csv, write_csv):
 def _kernel_hash():
     import hashlib
     hsh = hashlib.sha256()
-    for f in ("k3_decode.h", "k3_stream.h", "k3_topk.h", "k3_expert.hip"):
+    for f in ("k3_decode.h", "k3_stream.h", "k3_topk.h", "k3_sync.h", "k3_expert.hip"):
         with open(os.path.join(ROOT, "mxfp4_packed_weight_amd", "csrc", f), "rb") as fh:
             hsh.update(fh.read())
     return hsh.hexdigest()[:16]

@@ -206,14 +206,17 @@ k3_status k3_router_topk_f32(const float *logits, const float *bias, int T,
  * k3_moe_layer_ex also writes (any may be NULL) y_f32 [hidden] (the value
  * before the bf16 cast), idx int32 [k], w fp32 [k], logits fp64 [n_experts].
  *
- * Four launches: router; gate/up with the top-k folded in; down with the
- * combine folded in (two launches, down then combine, while the stream is
- * being captured into a graph). The folded combine marks its workgroups'
- * progress with a per-call value in the workspace, so the workspace needs
- * no initialisation, but calls that share one workspace must not overlap.
- * If its bounded internal wait runs out (about a second; only if the
- * device cannot run its workgroups), it writes NaN to y_f32 and 0x7FC0
- * (bf16 NaN) to y instead of hanging.
+ * Two launches: the router, then the expert work (top-k, gate/up + SwiGLU,
+ * down, combine) in one grid of one workgroup per compute unit whose stages
+ * hand over through the workspace, marked with a per-call value (so the
+ * workspace needs no initialisation, but calls that share one workspace
+ * must not overlap). Its bits equal those of the stage-by-stage calls below
+ * (k3_expert_gate_up_routed, k3_expert_down, k3_moe_combine), which are
+ * what the layer runs while the stream is being captured into a graph or
+ * for n_experts > 1024. Its internal waits are bounded: if the device
+ * cannot run its whole grid at once for about a second (another kernel
+ * holding compute units), it writes NaN to y_f32 and 0x7FC0 (bf16 NaN) to y
+ * instead of hanging.
  * ---------------------------------------------------------------------- */
 size_t k3_moe_workspace_bytes(int T, int n_experts, int hidden, int inter,
                               int k);
@@ -251,7 +254,9 @@ k3_status k3_moe_layer_ex(const uint16_t *x, const uint16_t *router_w,
  * (k3_router of X against router_w bf16 [n_experts][hidden], no bias).
  * Both take a workspace of k3_moe_batched_workspace_bytes(T, n_experts,
  * hidden, inter, k) bytes. Each Y[t] is summed in an order fixed by the
- * routing of the whole batch, so reruns are bit-identical.
+ * routing of the whole batch, so reruns are bit-identical. One token
+ * (T == 1) without a bias takes the single-token layer's expert launch (as
+ * k3_moe_layer after its router; same workspace rules).
  * ---------------------------------------------------------------------- */
 size_t k3_moe_permute_workspace_bytes(int T, int k);
 k3_status k3_moe_permute(const int32_t *idx, int T, int k, int n_experts,

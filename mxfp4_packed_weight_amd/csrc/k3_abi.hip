@@ -51,7 +51,7 @@ WsLayout ws_layout(int T, int n, int hidden, int inter, int k) {
   L.yp = off;
   off += align256((size_t)T * k * hidden * sizeof(float));
   L.sync = off;
-  off += align256((size_t)kMaxSyncGrid * sizeof(uint64_t));
+  off += align256((size_t)2 * kMaxSyncGrid * sizeof(uint64_t));
   L.total = off;
   return L;
 }
@@ -93,7 +93,7 @@ PermWs perm_ws(size_t off, long long P) {
 struct BatchWs {
   size_t logits, idx, w, counts, offsets, pair_token, pair_slot;
   PermWs perm;
-  size_t h, yp, total;
+  size_t h, yp, sync, total;
 };
 BatchWs batch_ws(int T, int n, int hidden, int inter, int k) {
   BatchWs B;
@@ -119,6 +119,8 @@ BatchWs batch_ws(int T, int n, int hidden, int inter, int k) {
   off += align256((size_t)P * inter * sizeof(float));
   B.yp = off;
   off += align256((size_t)P * hidden * sizeof(float));
+  B.sync = off;  // the single-token path's arrival slots (T == 1)
+  off += align256((size_t)2 * kMaxSyncGrid * sizeof(uint64_t));
   B.total = off;
   return B;
 }
@@ -554,6 +556,20 @@ k3_status k3_moe_layer_ex(const uint16_t *x, const uint16_t *router_w,
   float *h = reinterpret_cast<float *>(base + L.h);
   float *yp = reinterpret_cast<float *>(base + L.yp);
   K3_LAUNCH(fn, launch_router(x, router_w, 1, hidden, n_experts, lg, stream));
+  // The expert work in one launch, its stages marked by a per-call value; a
+  // graph being captured would replay one value, so it gets the separate
+  // launches (as does a selection over more than 1024 experts).
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (n_experts <= kFusedTopkMaxExperts &&
+      moe_experts_grid() <= (unsigned)kMaxSyncGrid &&
+      hipStreamIsCapturing(stream, &cap) == hipSuccess &&
+      cap == hipStreamCaptureStatusNone) {
+    K3_LAUNCH(fn, launch_moe_experts(x, lg, experts, n_experts, k, hidden,
+                                     inter, h, yp,
+                                     reinterpret_cast<uint64_t *>(base + L.sync),
+                                     next_layer_seq(), ix, wt, y, y_f32, stream));
+    return K3_OK;
+  }
   if (n_experts <= kFusedTopkMaxExperts) {  // top-k inside the gate/up launch
     K3_LAUNCH(fn, launch_gate_up_routed(x, lg, experts, n_experts, k, hidden,
                                         inter, h, ix, wt, stream));
@@ -562,20 +578,9 @@ k3_status k3_moe_layer_ex(const uint16_t *x, const uint16_t *router_w,
     K3_LAUNCH(fn, launch_gate_up(x, experts, ix, nullptr, k, hidden, inter, h,
                                  stream));
   }
-  // Down and combine in one launch, marked by a per-call value; a graph
-  // being captured would replay one value, so it gets the two launches.
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(stream, &cap) == hipSuccess &&
-      cap == hipStreamCaptureStatusNone &&
-      down_combine_grid(k, hidden, inter) <= (unsigned)kMaxSyncGrid) {
-    K3_LAUNCH(fn, launch_down_combine(h, experts, ix, wt, k, hidden, inter, yp,
-                                      reinterpret_cast<uint64_t *>(base + L.sync),
-                                      next_layer_seq(), y, y_f32, stream));
-  } else {
-    K3_LAUNCH(fn, launch_down(h, experts, ix, nullptr, k, hidden, inter, yp,
-                              stream));
-    K3_LAUNCH(fn, launch_combine(yp, wt, k, hidden, y, y_f32, stream));
-  }
+  K3_LAUNCH(fn, launch_down(h, experts, ix, nullptr, k, hidden, inter, yp,
+                            stream));
+  K3_LAUNCH(fn, launch_combine(yp, wt, k, hidden, y, y_f32, stream));
   return K3_OK;
 }
 
@@ -671,6 +676,19 @@ static k3_status batched_common(const char *fn, const uint16_t *X,
   if (router_w) {
     K3_LAUNCH(fn, launch_router(X, router_w, T, hidden, n_experts, lg, stream));
     logits = lg;
+  }
+  // One token without a routing bias: the single-token decode layer's expert
+  // launch (top-k, gate/up, down, combine; as k3_moe_layer after its router).
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (T == 1 && !bias && n_experts <= kFusedTopkMaxExperts &&
+      moe_experts_grid() <= (unsigned)kMaxSyncGrid &&
+      hipStreamIsCapturing(stream, &cap) == hipSuccess &&
+      cap == hipStreamCaptureStatusNone) {
+    K3_LAUNCH(fn, launch_moe_experts(X, logits, experts, n_experts, k, hidden,
+                                     inter, h, yp,
+                                     reinterpret_cast<uint64_t *>(base + B.sync),
+                                     next_layer_seq(), ix, wt, Y, Y_f32, stream));
+    return K3_OK;
   }
   K3_LAUNCH(fn, launch_topk_f64(logits, bias, T, n_experts, k, ix, wt, stream));
   K3_LAUNCH(fn, launch_permute(ix, T, k, n_experts, o, tok_batch(), stream));

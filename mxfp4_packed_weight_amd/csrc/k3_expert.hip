@@ -144,49 +144,98 @@ __global__ __launch_bounds__(kThreads) void gate_up_routed_kernel(
       part);
 }
 
-// The decode layer's last stage: down projection and weighted combine in
-// one launch. The down tiles are those of down_kernel on the same grid;
-// their partials go out with device-coherent stores, and each workgroup
-// then marks its arrival slot with the call's value `val`. Row tile r's
-// partials are tiles s * T + r (s < k); the workgroup that owns the last
-// one (slot k - 1) waits for the owners of the others and sums them in rank
-// order exactly as combine_kernel, so the bits equal down_kernel followed by
-// combine_kernel. Every workgroup waited for has a lower index and waits
-// for nothing itself, so the waits end even if the grid is not all resident
-// at once; a wait that still runs out (~1 s) makes the call write NaN.
-__global__ __launch_bounds__(kThreads) void down_combine_kernel(
-    const float *__restrict__ h, const uint8_t *const *__restrict__ experts,
-    const int32_t *__restrict__ idx, const float *__restrict__ w, int k,
-    int hidden, int inter, float *yp, uint64_t *slots, uint64_t val,
+// The decode layer's expert work in one launch, after the router: top-k
+// (topk_wg), gate/up + SwiGLU, down, and the weighted combine. The grid is
+// one workgroup per compute unit; each stage cuts its tiles over the grid as
+// the separate kernels do (gate_up_routed_kernel, down_kernel, then
+// combine_kernel), so the bits equal those launches'. Between stages:
+//   - h goes out with device-coherent stores and each workgroup marks its
+//     stage-0 arrival slot with the call's value `val`; a workgroup's down
+//     stage issues its first quads' loads and then waits only for the
+//     workgroups that produced the h slots it needs (its own expert's
+//     gate/up workgroups), so the down weights are already on their way;
+//   - the down partials go out the same way (stage-1 slots); the owner of a
+//     row tile's last partial waits for the owners of the others and sums
+//     the k partials in rank order.
+// This saves the boundary between the gate/up and down launches, the down
+// launch's ramp and the combine launch. Waits are bounded: if the device
+// cannot run the whole grid at once for about a second (another kernel
+// holding compute units), the call writes NaN rather than hang.
+__global__ __launch_bounds__(kThreads) void moe_experts_kernel(
+    const uint16_t *__restrict__ x, const double *__restrict__ logits,
+    const uint8_t *const *__restrict__ experts, int n, int k, int hidden,
+    int inter, float *h, float *yp, uint64_t *slots, uint64_t val,
+    int32_t *__restrict__ idx_out, float *__restrict__ w_out,
     uint16_t *__restrict__ y, float *__restrict__ y_f32) {
   __shared__ float part[kPartFloats];
+  __shared__ TopkWgLds tk;
   __shared__ int bad;
   if (threadIdx.x == 0) bad = 0;
+  topk_wg<kNW>(logits, n, k, tk);
+  if (blockIdx.x == 0 && threadIdx.x < k) {
+    idx_out[threadIdx.x] = tk.sel[threadIdx.x];
+    w_out[threadIdx.x] = tk.wt[threadIdx.x];
+  }
+  const int G = gridDim.x, lane = threadIdx.x & 63;
   const ExpertLayout L = expert_layout(hidden, inter);
-  const int T = L.down.ntiles, total = k * T;
+  const uint32_t *xp = reinterpret_cast<const uint32_t *>(x);
+  const int Tg = L.gu.ntiles, total_gu = k * Tg;
+  {
+    int t0, t1;
+    wg_range(total_gu, &t0, &t1);
+    run_rows(
+        t0, t1, L.gu.G, L.gu.G4,
+        [&](int t) {
+          const int e = __builtin_amdgcn_readfirstlane(tk.sel[t / Tg]);
+          return ldc(experts + e) + (size_t)(t % Tg) * L.gu.tile_bytes;
+        },
+        [&](u32x4 w, int g, int) { return group_dot_bf16(w, xp + (size_t)16 * g); },
+        [&](int t, int ln, float s) {
+          const float u = __shfl_down(s, 32);  // lane l<32: gate row; l+32: up row
+          int is_up, row;
+          gu_lane_row(t % Tg, ln, &is_up, &row);
+          if (ln < 32 && row < inter)
+            st_dev(h + (size_t)(t / Tg) * inter + row, silu(s) * u);
+        },
+        part);
+  }
+  arrive(slots, val);
+
+  const int Td = L.down.ntiles, total = k * Td;
   int t0, t1;
   wg_range(total, &t0, &t1);
+  const float *hb = h;
   run_rows(
       t0, t1, L.down.G, L.down.G4,
       [&](int t) {
-        return ldc(experts + ldc(idx + t / T)) + L.down_offset +
-               (size_t)(t % T) * L.down.tile_bytes;
+        const int e = __builtin_amdgcn_readfirstlane(tk.sel[t / Td]);
+        return ldc(experts + e) + L.down_offset + (size_t)(t % Td) * L.down.tile_bytes;
       },
-      [&](u32x4 wv, int g, int t) {
-        return group_dot_f32(wv, h + (size_t)(t / T) * inter + (size_t)32 * g);
+      [&](u32x4 w, int g, int t) {
+        return group_dot_f32(w, hb + (size_t)(t / Td) * inter + (size_t)32 * g);
       },
-      [&](int t, int lane, float s) {
-        const int row = (t % T) * kTileRows + lane;
-        if (row < hidden) st_dev(yp + (size_t)(t / T) * hidden + row, s);
+      [&](int t, int ln, float s) {
+        const int row = (t % Td) * kTileRows + ln;
+        if (row < hidden) st_dev(yp + (size_t)(t / Td) * hidden + row, s);
       },
-      part);
-  arrive(slots, val);
-  const int lane = threadIdx.x & 63;
-  const int last = (k - 1) * T;
-  const int r_lo = max(t0 - last, 0), r_hi = min(t1 - last, T);
+      part,
+      [&]() {  // the gate/up workgroups of this workgroup's down slots
+        if (t0 < t1 && wave_id() == 0) {
+          const int c_lo = tile_owner(t0 / Td * Tg, total_gu, G);
+          const int c_hi = tile_owner(((t1 - 1) / Td + 1) * Tg - 1, total_gu, G);
+          if (!wave_wait_range(slots, c_lo, c_hi - c_lo + 1, val) && lane == 0) bad = 1;
+        }
+        __syncthreads();
+        hb = after_wait(hb);
+      });
+  uint64_t *done = slots + kMaxSyncGrid;
+  arrive(done, val);
+
+  const int last = (k - 1) * Td;
+  const int r_lo = max(t0 - last, 0), r_hi = min(t1 - last, Td);
   for (int r = r_lo + wave_id(); r < r_hi; r += kNW) {
-    const int owner = lane < k ? tile_owner(lane * T + r, total, gridDim.x) : 0;
-    if (!wave_wait_owners(slots, owner, k, val) && lane == 0) bad = 1;
+    const int owner = lane < k ? tile_owner(lane * Td + r, total, G) : 0;
+    if (!wave_wait_owners(done, owner, k, val) && lane == 0) bad = 1;
     const int row = r * kTileRows + lane;
     if (row < hidden) {
       float acc = 0.f;
@@ -197,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void down_combine_kernel(
           v[j] = j0 + j < k ? ld_dev(yp + (size_t)(j0 + j) * hidden + row) : 0.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          if (j0 + j < k) acc = fmaf(w[j0 + j], v[j], acc);
+          if (j0 + j < k) acc = fmaf(tk.wt[j0 + j], v[j], acc);
       }
       if (y_f32) y_f32[row] = acc;
       if (y) y[row] = f32_to_bf16_rne(acc);
@@ -282,21 +331,19 @@ hipError_t launch_gate_up_routed(const uint16_t *x, const double *logits,
   return hipGetLastError();
 }
 
-hipError_t launch_down_combine(const float *h, const uint8_t *const *experts,
-                               const int32_t *idx, const float *w, int k,
-                               int hidden, int inter, float *yp,
-                               uint64_t *slots, uint64_t val, uint16_t *y,
-                               float *y_f32, hipStream_t s) {
-  const ExpertLayout L = expert_layout(hidden, inter);
-  hipLaunchKernelGGL(down_combine_kernel,
-                     dim3(grid_for_tiles(k * L.down.ntiles)), dim3(kThreads),
-                     0, s, h, experts, idx, w, k, hidden, inter, yp, slots, val,
-                     y, y_f32);
-  return hipGetLastError();
-}
+unsigned moe_experts_grid() { return (unsigned)num_cus(); }
 
-unsigned down_combine_grid(int k, int hidden, int inter) {
-  return grid_for_tiles(k * expert_layout(hidden, inter).down.ntiles);
+hipError_t launch_moe_experts(const uint16_t *x, const double *logits,
+                              const uint8_t *const *experts, int n, int k,
+                              int hidden, int inter, float *h, float *yp,
+                              uint64_t *slots, uint64_t val, int32_t *idx,
+                              float *w, uint16_t *y, float *y_f32,
+                              hipStream_t s) {
+  // one workgroup per compute unit: the whole grid fits at once
+  hipLaunchKernelGGL(moe_experts_kernel, dim3(moe_experts_grid()),
+                     dim3(kThreads), 0, s, x, logits, experts, n, k, hidden,
+                     inter, h, yp, slots, val, idx, w, y, y_f32);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(const float *yp, const float *w, int k, int hidden,

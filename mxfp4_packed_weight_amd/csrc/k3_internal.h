@@ -165,16 +165,18 @@ hipError_t launch_gate_up_routed(const uint16_t *x, const double *logits,
                                  float *w, hipStream_t s);
 hipError_t launch_combine(const float *yp, const float *w, int k, int hidden,
                           uint16_t *y, float *y_f32, hipStream_t s);
-// Down + combine in one launch (the decode layer's last stage). slots: one
-// arrival word per workgroup (down_combine_grid of them, at most
-// kMaxSyncGrid); val: this call's value, never reused in the process.
+// The decode layer's expert work in one launch (k3_expert.hip): top-k of
+// the logits, gate/up, down, combine. slots: 2 * kMaxSyncGrid arrival words
+// (moe_experts_grid() <= kMaxSyncGrid workgroups); val: this call's value,
+// never reused in the process.
 constexpr int kMaxSyncGrid = 1024;
-unsigned down_combine_grid(int k, int hidden, int inter);
-hipError_t launch_down_combine(const float *h, const uint8_t *const *experts,
-                               const int32_t *idx, const float *w, int k,
-                               int hidden, int inter, float *yp,
-                               uint64_t *slots, uint64_t val, uint16_t *y,
-                               float *y_f32, hipStream_t s);
+unsigned moe_experts_grid();
+hipError_t launch_moe_experts(const uint16_t *x, const double *logits,
+                              const uint8_t *const *experts, int n, int k,
+                              int hidden, int inter, float *h, float *yp,
+                              uint64_t *slots, uint64_t val, int32_t *idx,
+                              float *w, uint16_t *y, float *y_f32,
+                              hipStream_t s);
 hipError_t launch_router(const uint16_t *x, const uint16_t *R, int T,
                          int hidden, int n, double *logits, hipStream_t s);
 hipError_t launch_topk_f64(const double *logits, const float *bias, int T,

@@ -52,12 +52,28 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 //                            group g of activation vector a, for a < n =
 //                            na(t) (g < G; g, t, n uniform)
 //   epi(t, a, lane, s)    finished sum of row `lane` of tile t for vector a
+//   pre()                 called once by every wave before any loaded quad
+//                         is used: by waves 1.. after their first quads'
+//                         loads are issued (a caller can wait there for its
+//                         activations while the weights are on their way),
+//                         by wave 0 before its own loads, since wave 0 is
+//                         the one that polls and a poll completes only after
+//                         the wave's earlier loads
 // `part` is the caller's LDS array of MaxTPW * kNW * 64 * NA floats.
-template <int NA, int MaxTPW, class Base, class Na, class Dot, class Epi>
+struct NoPre {
+  __device__ void operator()() const {}
+};
+
+template <int NA, int MaxTPW, class Base, class Na, class Dot, class Epi,
+          class Pre = NoPre>
 __device__ __forceinline__ void run_rows_n(int t_begin, int t_end, int G,
                                            int G4, Base base, Na na, Dot dot,
-                                           Epi epi, float *part) {
-  if (t_begin >= t_end) return;
+                                           Epi epi, float *part,
+                                           Pre pre = Pre()) {
+  if (t_begin >= t_end) {
+    pre();
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   auto slot = [&](int tl, int w, int a) { return ((tl * kNW + w) * NA + a) * 64; };
@@ -182,8 +198,10 @@ __device__ __forceinline__ void run_rows_n(int t_begin, int t_end, int G,
   };
 
   setup(t_begin);
-  for (;;) {
+  for (bool first = true;; first = false) {
+    if (first && wave == 0) pre();
     prologue();
+    if (first && wave != 0) pre();
     // Enter the loop with no load pending (the first consume needs these
     // bytes anyway): the loop's own waits then count only its own loads.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -195,14 +213,14 @@ __device__ __forceinline__ void run_rows_n(int t_begin, int t_end, int G,
 
 // One activation vector per tile: the single-token kernels.
 //   dot(w, g, t) -> float,  epi(t, lane, s)
-template <class Base, class Dot, class Epi>
+template <class Base, class Dot, class Epi, class Pre = NoPre>
 __device__ __forceinline__ void run_rows(int t_begin, int t_end, int G, int G4,
                                          Base base, Dot dot, Epi epi,
-                                         float *part) {
+                                         float *part, Pre pre = Pre()) {
   run_rows_n<1, kMaxTPW>(
       t_begin, t_end, G, G4, base, [](int) { return 1; },
       [&](u32x4 w, int g, int t, int, float(&sub)[1]) { sub[0] = dot(w, g, t); },
-      [&](int t, int, int lane, float s) { epi(t, lane, s); }, part);
+      [&](int t, int, int lane, float s) { epi(t, lane, s); }, part, pre);
 }
 
 }  // namespace k3

@@ -36,6 +36,39 @@ __device__ __forceinline__ void arrive(uint64_t *slots, uint64_t val) {
   if (threadIdx.x == 0) st_dev(slots + blockIdx.x, val);
 }
 
+// Hides where a pointer came from, so that no load through it (scalar
+// activation loads in particular, which the compiler may otherwise hoist)
+// is scheduled above the wait that precedes this call.
+template <typename T>
+__device__ __forceinline__ T *after_wait(T *p) {
+  asm volatile("" : "+s"(p) : : "memory");
+  return p;
+}
+
+// One wave: waits until slots[i] == val for all i in [first, first + count).
+// False if the poll limit runs out.
+__device__ __forceinline__ bool wave_wait_range(const uint64_t *slots,
+                                                int first, int count,
+                                                uint64_t val) {
+  const int lane = threadIdx.x & 63;
+  for (int it = 0; it < kSpinLimit; ++it) {
+    bool ok = true;
+    for (int i0 = 0; i0 < count; i0 += 256) {  // four loads in flight per lane
+      uint64_t v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = i0 + lane + 64 * q;
+        v[q] = i < count ? ld_dev(slots + first + i) : val;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ok &= v[q] == val;
+    }
+    if (__ballot(!ok) == 0) return true;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return false;
+}
+
 // One wave: waits until slots[owner] == val for every lane < count (each
 // lane names its own owner). False if the poll limit runs out.
 __device__ __forceinline__ bool wave_wait_owners(const uint64_t *slots,
