@@ -13,9 +13,26 @@ namespace k3 {
 
 namespace {
 
-constexpr int kThreads = kNW * 64;
+// Grouped kernels: small workgroups, several per compute unit. Their
+// activations reach the waves through scalar loads that miss the scalar
+// cache (each item brings new tokens), so a wave stalls on them; small
+// workgroups let the stalled waves' neighbours run instead of holding a
+// 16-wave barrier, and about 10 workgroups per CU keep ~40 waves' loads
+// queued. Measured at 64 tokens (Zipf routing): 1.9x faster down and 1.3x
+// faster gate/up than one 16-wave workgroup per CU.
+#ifndef K3_BATCH_NW
+#define K3_BATCH_NW 4
+#endif
+#ifndef K3_BATCH_WG_PER_CU
+#define K3_BATCH_WG_PER_CU 10
+#endif
+constexpr int kBatchNW = K3_BATCH_NW;  // waves per workgroup, grouped kernels
+constexpr int kThreads = kBatchNW * 64;
 constexpr int kTokBatch = 4;   // tokens per work item (accumulators per lane)
-constexpr int kBatchTPW = 2;   // tiles per chunk of the grouped kernels
+#ifndef K3_BATCH_TPW
+#define K3_BATCH_TPW 2
+#endif
+constexpr int kBatchTPW = K3_BATCH_TPW;  // tiles per chunk of the grouped kernels
 constexpr int kPermThreads = 1024;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -195,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_batched_kernel(
     const uint16_t *__restrict__ X, const uint8_t *const *__restrict__ experts,
     Items it, const int32_t *__restrict__ pair_token, int hidden, int inter,
     float *__restrict__ h) {
-  __shared__ float part[kBatchTPW * kNW * 64 * kTokBatch];
+  __shared__ float part[kBatchTPW * kBatchNW * 64 * kTokBatch];
   const ExpertLayout L = expert_layout(hidden, inter);
   const int T = L.gu.ntiles;
   const int total = ldc(it.n) * T;
@@ -216,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_batched_kernel(
       cr.row[v] = Xw + (size_t)tok * xrow;
     }
   };
-  run_rows_n<kTokBatch, kBatchTPW>(
+  run_rows_n<kTokBatch, kBatchTPW, kBatchNW>(
       t0, t1, L.gu.G, L.gu.G4,
       [&](int t) {
         return ldc(experts + ldc(it.e + t / T)) + (size_t)(t % T) * L.gu.tile_bytes;
@@ -243,15 +260,15 @@ __global__ __launch_bounds__(kThreads) void gate_up_batched_kernel(
 __global__ __launch_bounds__(kThreads) void down_batched_kernel(
     const float *__restrict__ h, const uint8_t *const *__restrict__ experts,
     Items it, int hidden, int inter, float *__restrict__ yp) {
-  __shared__ float part[kBatchTPW * kNW * 64 * kTokBatch];
+  __shared__ float part[kBatchTPW * kBatchNW * 64 * kTokBatch];
   const ExpertLayout L = expert_layout(hidden, inter);
   const int T = L.down.ntiles;
   const int total = ldc(it.n) * T;
   int t0, t1;
   wg_range(total, &t0, &t1);
   int ct = -1;
-  size_t coff = 0;  // first sorted pair of the consumer's tile
-  run_rows_n<kTokBatch, kBatchTPW>(
+  const float *hrow[kTokBatch];  // activation rows of the consumer's tile
+  run_rows_n<kTokBatch, kBatchTPW, kBatchNW>(
       t0, t1, L.down.G, L.down.G4,
       [&](int t) {
         return ldc(experts + ldc(it.e + t / T)) + L.down_offset +
@@ -261,12 +278,14 @@ __global__ __launch_bounds__(kThreads) void down_batched_kernel(
       [&](u32x4 w, int g, int t, int n, float(&sub)[kTokBatch]) {
         if (t != ct) {
           ct = t;
-          coff = (size_t)ldc(it.off + t / T);
+          const size_t coff = (size_t)ldc(it.off + t / T);
+#pragma unroll
+          for (int v = 0; v < kTokBatch; ++v) hrow[v] = h + (coff + v) * inter;
         }
         const GroupF32 G = decode_f32(w);
 #pragma unroll
         for (int v = 0; v < kTokBatch; ++v)
-          sub[v] = v < n ? dot_decoded(G, h + (coff + v) * inter + (size_t)32 * g) : 0.f;
+          sub[v] = v < n ? dot_decoded(G, hrow[v] + (size_t)32 * g) : 0.f;
       },
       [&](int t, int v, int lane, float s) {
         const int row = (t % T) * kTileRows + lane;
@@ -301,7 +320,7 @@ __global__ __launch_bounds__(256) void combine_batched_kernel(
   if (Y) Y[(size_t)t * hidden + i] = f32_to_bf16_rne(acc);
 }
 
-unsigned persistent_grid() { return (unsigned)num_cus(); }
+unsigned persistent_grid() { return (unsigned)(num_cus() * K3_BATCH_WG_PER_CU); }
 
 }  // namespace
 

@@ -59,13 +59,14 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 //                         by wave 0 before its own loads, since wave 0 is
 //                         the one that polls and a poll completes only after
 //                         the wave's earlier loads
-// `part` is the caller's LDS array of MaxTPW * kNW * 64 * NA floats.
+// NWV waves per workgroup; `part` is the caller's LDS array of
+// MaxTPW * NWV * 64 * NA floats.
 struct NoPre {
   __device__ void operator()() const {}
 };
 
-template <int NA, int MaxTPW, class Base, class Na, class Dot, class Epi,
-          class Pre = NoPre>
+template <int NA, int MaxTPW, int NWV = kNW, class Base, class Na, class Dot,
+          class Epi, class Pre = NoPre>
 __device__ __forceinline__ void run_rows_n(int t_begin, int t_end, int G,
                                            int G4, Base base, Na na, Dot dot,
                                            Epi epi, float *part,
@@ -76,7 +77,7 @@ __device__ __forceinline__ void run_rows_n(int t_begin, int t_end, int G,
   }
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
-  auto slot = [&](int tl, int w, int a) { return ((tl * kNW + w) * NA + a) * 64; };
+  auto slot = [&](int tl, int w, int a) { return ((tl * NWV + w) * NA + a) * 64; };
 
   // chunk state: tiles [c0, c0 + ntl), this wave's items [i0, i0 + nitems)
   int c0 = t_begin, ntl = 0, i0 = 0, nitems = 0;
@@ -91,8 +92,8 @@ __device__ __forceinline__ void run_rows_n(int t_begin, int t_end, int G,
 #pragma unroll
       for (int v = 0; v < NA; ++v) part[slot(tl, wave, v) + lane] = 0.f;
     const int n = ntl * G4;
-    i0 = wave * n / kNW;
-    nitems = (wave + 1) * n / kNW - i0;
+    i0 = wave * n / NWV;
+    nitems = (wave + 1) * n / NWV - i0;
     ltl = i0 / G4;
     lq = i0 % G4;
     if (nitems > 0) lbase = base(c0 + ltl);
@@ -183,14 +184,14 @@ __device__ __forceinline__ void run_rows_n(int t_begin, int t_end, int G,
     }
     if (nitems > 0) flush();
     __syncthreads();
-    for (int tl = wave; tl < ntl; tl += kNW) {
+    for (int tl = wave; tl < ntl; tl += NWV) {
       const int nv = na(c0 + tl);
 #pragma unroll
       for (int v = 0; v < NA; ++v) {
         if (v >= nv) break;
         float sum = 0.f;
 #pragma unroll
-        for (int w = 0; w < kNW; ++w) sum += part[slot(tl, w, v) + lane];
+        for (int w = 0; w < NWV; ++w) sum += part[slot(tl, w, v) + lane];
         epi(c0 + tl, v, lane, sum);
       }
     }
