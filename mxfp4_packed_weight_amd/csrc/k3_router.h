@@ -1,13 +1,13 @@
-// One router row's logit by one wave: bf16 x . bf16 R[e] with every product
-// and sum in fp64. Shared by the router kernel and the fused decode layer so
-// that both produce the same bits.
+// One router row's logit: bf16 x . bf16 R[e] with every product and sum in
+// fp64, split over kRouterSplit waves.
 //
-// Each lane issues the loads of all its 16-byte chunks of the row (chunk
-// c = lane + 64 i) before computing, so a whole row is in flight at once;
-// products go into four chains per lane ((0 + 1) + (2 + 3) at the end) and
-// the lane sums are combined by a fixed DPP tree. A product of two bf16
-// values is exact in fp64, so a logit is within ~1e-16 of a sequential fp64
-// sum, which keeps the top-k indices identical to an fp64 reference.
+// Each lane issues the loads of all its 16-byte chunks of the row before
+// computing, so a whole row is in flight at once; products go into four
+// chains per lane ((0 + 1) + (2 + 3) at the end), the lane sums are combined
+// by a fixed DPP tree and the waves' partials in a fixed order. A product of
+// two bf16 values is exact in fp64, so a logit is within ~1e-16 of a
+// sequential fp64 sum, which keeps the top-k indices identical to an fp64
+// reference.
 #pragma once
 
 #include "k3_decode.h"
@@ -53,33 +53,40 @@ __device__ __forceinline__ double wave_sum(double v) {
 }
 
 constexpr int kRouterCPL = 16;  // 16-byte chunks per lane in flight
+constexpr int kRouterSplit = 4;  // waves per router row
 
-// x from global memory (XLds = false, x at xg) or from this workgroup's LDS
-// copy (XLds = true, x at xl); R row at Rrow; hidden a multiple of 8.
+// This wave's share of one router row's logit: wave `part` of kRouterSplit
+// takes chunks c = 64 (kRouterSplit i + part) + lane, x from global memory
+// (XLds = false, at xg) or from the workgroup's LDS copy (XLds = true, at
+// xl); R row at Rrow; hidden a multiple of 8. Returns the wave's fp64 sum
+// (four chains per lane, then the DPP tree), the same in every lane; the
+// kRouterSplit partials are added as (p0 + p1) + (p2 + p3).
 template <bool XLds>
-__device__ __forceinline__ double router_row(const uint16_t *__restrict__ Rrow,
-                                             const uint16_t *__restrict__ xg,
-                                             const u32x4 *xl, int hidden) {
+__device__ __forceinline__ double router_row_part(const uint16_t *__restrict__ Rrow,
+                                                  const uint16_t *__restrict__ xg,
+                                                  const u32x4 *xl, int hidden,
+                                                  int part) {
   const int lane = threadIdx.x & 63;
   gu4_t *Rr = (gu4_t *)Rrow;
   gu4_t *xr = (gu4_t *)xg;
   const int nchunk = hidden / 8;
+  constexpr int kStride = 64 * kRouterSplit;
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int c0 = 0; c0 < nchunk; c0 += 64 * kRouterCPL) {
+  for (int c0 = 64 * part; c0 < nchunk; c0 += kStride * kRouterCPL) {
     // Every lane loads (at a clamped index) so that all loads issue before
     // the first use; lanes past the row's end then use zeros.
     u32x4 rv[kRouterCPL], xv[kRouterCPL];
 #pragma unroll
     for (int i = 0; i < kRouterCPL; ++i) {
-      if (c0 + 64 * i >= nchunk) break;  // wave-uniform
-      const int c = min(c0 + lane + 64 * i, nchunk - 1);
+      if (c0 + kStride * i >= nchunk) break;  // wave-uniform
+      const int c = min(c0 + lane + kStride * i, nchunk - 1);
       rv[i] = Rr[c];
       if (!XLds) xv[i] = xr[c];
     }
 #pragma unroll
     for (int i = 0; i < kRouterCPL; ++i) {
-      if (c0 + 64 * i >= nchunk) break;
-      const int c = c0 + lane + 64 * i;
+      if (c0 + kStride * i >= nchunk) break;
+      const int c = c0 + lane + kStride * i;
       const bool ok = c < nchunk;
       if (XLds) xv[i] = xl[min(c, nchunk - 1)];
       const u32x4 z = {0u, 0u, 0u, 0u};

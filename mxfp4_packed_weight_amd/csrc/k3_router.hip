@@ -1,8 +1,8 @@
 // Router: bf16 logits GEMV in fp64 and sigmoid top-k selection.
 //
-// Logits: one wave per (token, expert) row (router_row, k3_router.h: all of
-// a row's loads in flight at once, fp64 products and sums in a fixed order,
-// reproducible bit for bit).
+// Logits: four waves per (token, expert) row (router_row_part, k3_router.h:
+// all of a row's loads in flight at once, fp64 products and sums in a fixed
+// order, reproducible bit for bit).
 //
 // Selection: one wave per token with the keys in registers; a cheap lower
 // bound keeps ~18 candidates, which are ranked in parallel (topk_wave,
@@ -20,17 +20,23 @@ namespace k3 {
 
 namespace {
 
-constexpr int kRouterWaves = 4;
-
-__global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(
+// One workgroup of kRouterSplit waves per (row, token); tokens beyond the
+// grid's y extent are taken in strides of it.
+static_assert(kRouterSplit == 4, "the partials are added as (p0 + p1) + (p2 + p3)");
+__global__ __launch_bounds__(kRouterSplit * 64) void router_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ R, int hidden,
-    int n, double *__restrict__ logits) {
-  const int e = blockIdx.x * kRouterWaves + wave_id();
-  const int t = blockIdx.y;
-  if (e >= n) return;  // whole wave; no barrier below
-  const double total = router_row<false>(R + (size_t)e * hidden,
-                                         x + (size_t)t * hidden, nullptr, hidden);
-  if ((threadIdx.x & 63) == 0) logits[(size_t)t * n + e] = total;
+    int n, int T, double *__restrict__ logits) {
+  __shared__ double partial[kRouterSplit];
+  const int e = blockIdx.x, w = wave_id();
+  for (int t = blockIdx.y; t < T; t += gridDim.y) {
+    const double p = router_row_part<false>(R + (size_t)e * hidden,
+                                            x + (size_t)t * hidden, nullptr, hidden, w);
+    if ((threadIdx.x & 63) == 0) partial[w] = p;
+    __syncthreads();
+    if (threadIdx.x == 0)
+      logits[(size_t)t * n + e] = (partial[0] + partial[1]) + (partial[2] + partial[3]);
+    __syncthreads();
+  }
 }
 
 
@@ -77,9 +83,8 @@ hipError_t launch_topk(const LT *logits, const float *bias, int T, int n,
 
 hipError_t launch_router(const uint16_t *x, const uint16_t *R, int T,
                          int hidden, int n, double *logits, hipStream_t s) {
-  hipLaunchKernelGGL(router_kernel,
-                     dim3((n + kRouterWaves - 1) / kRouterWaves, T),
-                     dim3(kRouterWaves * 64), 0, s, x, R, hidden, n, logits);
+  hipLaunchKernelGGL(router_kernel, dim3(n, T < 65535 ? T : 65535),
+                     dim3(kRouterSplit * 64), 0, s, x, R, hidden, n, T, logits);
   return hipGetLastError();
 }
 
