@@ -28,7 +28,10 @@ namespace {
 #endif
 constexpr int kBatchNW = K3_BATCH_NW;  // waves per workgroup, grouped kernels
 constexpr int kThreads = kBatchNW * 64;
-constexpr int kTokBatch = 4;   // tokens per work item (accumulators per lane)
+#ifndef K3_TOK_BATCH
+#define K3_TOK_BATCH 4
+#endif
+constexpr int kTokBatch = K3_TOK_BATCH;  // tokens per work item (accumulators per lane)
 #ifndef K3_BATCH_TPW
 #define K3_BATCH_TPW 2
 #endif

@@ -174,3 +174,40 @@ def test_batched_c4_full_size(c4_pool):
                        lambda e: W.expert_weights(0, W.C3, e, hidden, inter),
                        k, hidden, inter, [0, 31, 63])
     say(f"C4 sampled tokens: max normwise {err:.3e}")
+
+
+def test_one_token_from_logits_takes_the_decode_launch(c4_pool):
+    """T = 1 without a bias runs the single-token decode layer's expert
+    launch (the launch the decode layer makes after its router, and the one
+    the benchmark times): bit-identical to k3_moe_layer_ex on the same token
+    and router, and within 1e-5 of the oracle, over several tokens on one
+    workspace."""
+    import torch
+    n, hidden, inter, k = W.N_EXPERTS, W.HIDDEN, W.INTER, W.TOPK
+    R = W.router_bf16(0, W.C3)
+    R_d = up(R)
+    X = W.tokens_bf16(0, W.C3, 4, hidden, batch=9)
+    wsb = empty(K.k3_moe_batched_workspace_bytes(1, n, hidden, inter, k), torch.uint8)
+    wsl = empty(K.k3_moe_workspace_bytes(1, n, hidden, inter, k), torch.uint8)
+    say("one token from logits vs the decode layer")
+    for t in range(4):
+        xd = up(X[t:t + 1])
+        lg = empty((1, n), torch.float64)
+        K.k3_router(xd, R_d, 1, hidden, n, lg)
+        Y = empty((1, hidden), torch.int16)
+        Y32 = empty((1, hidden), torch.float32)
+        idx = empty((1, k), torch.int32)
+        w = empty((1, k), torch.float32)
+        K.k3_moe_layer_from_logits(xd, lg, None, c4_pool.table, n, hidden, inter, k, 1, Y, wsb,
+                                   Y_f32=Y32, idx=idx, w=w)
+        y = empty(hidden, torch.int16)
+        y32 = empty(hidden, torch.float32)
+        K.k3_moe_layer_ex(xd, R_d, c4_pool.table, n, hidden, inter, k, y, wsl, y_f32=y32)
+        assert np.array_equal(Y32.cpu().numpy()[0].view(np.uint32), y32.cpu().numpy().view(np.uint32))
+        assert np.array_equal(Y.cpu().numpy()[0], y.cpu().numpy())
+        if t == 0:
+            out = dict(idx=idx.cpu().numpy(), w=w.cpu().numpy(), Y32=Y32.cpu().numpy())
+            err = check_tokens(out, X[t:t + 1], lg.cpu().numpy(),
+                               lambda e: W.expert_weights(0, W.C3, e, hidden, inter),
+                               k, hidden, inter, [0])
+            say(f"one token from logits: normwise {err:.3e}")
