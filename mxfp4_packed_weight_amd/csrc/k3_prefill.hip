@@ -159,6 +159,18 @@ __global__ __launch_bounds__(64) void prefill_gemm_kernel(
     for (int m = 0; m < 4; ++m) acc[nb][m] = v4f{0.f, 0.f, 0.f, 0.f};
   auto consume = [&](int d, int q) {
     const bool gin = 4 * q + kb < G;
+    // B operands once per quad: a column past the item or a group past K
+    // contributes nothing (zero codes, unit scale)
+    v8i bv[kNB];
+    int eb[kNB];
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      const bool use = bok[nb] && gin;
+      const u32x4 bm = b[d][nb];
+      bv[nb] = v8i{use ? (int)bm.x : 0, use ? (int)bm.y : 0, use ? (int)bm.z : 0,
+                   use ? (int)bm.w : 0, 0, 0, 0, 0};
+      eb[nb] = use ? (int)bs[d][nb] : 127;
+    }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       uint32_t ea = (asc[d][m] >> (8 * kb)) & 255u;
@@ -169,17 +181,9 @@ __global__ __launch_bounds__(64) void prefill_gemm_kernel(
       }
       const v8i av = {(int)am.x, (int)am.y, (int)am.z, (int)am.w, 0, 0, 0, 0};
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) {
-        u32x4 bm = b[d][nb];
-        uint32_t eb = bs[d][nb];
-        if (!(bok[nb] && gin)) {
-          bm = u32x4{0u, 0u, 0u, 0u};
-          eb = 127u;
-        }
-        const v8i bv = {(int)bm.x, (int)bm.y, (int)bm.z, (int)bm.w, 0, 0, 0, 0};
+      for (int nb = 0; nb < kNB; ++nb)
         acc[nb][m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            av, bv, acc[nb][m], 4, 4, 0, (int)ea, 0, (int)eb);
-      }
+            av, bv[nb], acc[nb][m], 4, 4, 0, (int)ea, 0, eb[nb]);
     }
   };
   // ring over the quads of K (loads unconditional in the steady loop)
