@@ -188,3 +188,46 @@ def test_layer_c3_tokens_in_a_row(c3_pool):
         xd = up(X[t])
         out = layer_outputs(pool, R_d, xd, n, hidden, inter, k, ws)
         assert_same(out, stage_outputs(pool, R_d, xd, n, hidden, inter, k))
+
+
+def test_layer_in_a_captured_graph():
+    """Captured into a HIP graph, the layer takes the separate launches (its
+    single expert launch marks stages with a per-call value a replay would
+    repeat). Replays with new tokens copied into the captured input must
+    match eager calls bit for bit and the oracle within 1e-5; eager work
+    and synchronisation run between the replays."""
+    import torch
+    cfg, seed, n, hidden, inter, k = 75, 9, 32, 256, 160, 6
+    say("layer in a captured graph: 4 replays")
+    pool = D.build_expert_pool(seed, cfg, n, hidden, inter, 114, 120, workers=2)
+    R = gen.normal_bf16(gen.key(seed, cfg, gen.KIND_ROUTER), n * hidden, 0, 0.02).reshape(
+        n, hidden)
+    R_d = up(R)
+    X = W.tokens_bf16(seed, cfg, 4, hidden)
+    ws = empty(K.k3_moe_workspace_bytes(1, n, hidden, inter, k), torch.uint8)
+    xin = empty(hidden, torch.int16)
+    y = empty(hidden, torch.int16)
+    y32 = empty(hidden, torch.float32)
+    s = torch.cuda.Stream()
+    xin.copy_(up(X[0]))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        K.k3_moe_layer_ex(xin, R_d, pool.table, n, hidden, inter, k, y, ws, y_f32=y32,
+                          stream=s)
+    ws_e = empty(K.k3_moe_workspace_bytes(1, n, hidden, inter, k), torch.uint8)
+    for t in range(4):
+        xin.copy_(up(X[t]))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = y32.cpu().numpy().copy()
+        eager = layer_outputs(pool, R_d, up(X[t]), n, hidden, inter, k, ws_e)
+        # the eager layer runs the single expert launch; the replay the
+        # separate ones, whose bits the stage-by-stage calls give
+        stages = stage_outputs(pool, R_d, up(X[t]), n, hidden, inter, k)
+        assert np.array_equal(got.view(np.uint32), stages["y32"].view(np.uint32)), t
+        assert np.array_equal(got.view(np.uint32), eager["y32"].view(np.uint32)), t
+        experts = {e: W.expert_weights(seed, cfg, e, hidden, inter, 114, 120) for e in range(n)}
+        y_ref, _, _ = oracle.moe_layer(X[t], R, experts, k, hidden, inter)
+        assert normwise(got, y_ref) <= TOL
