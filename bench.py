@@ -80,10 +80,14 @@ def main():
     ap.add_argument("--tokens", type=int, default=512, help="distinct tokens in the bank")
     ap.add_argument("--router-copies", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=("c3", "c4", "c5"), default="c3",
+    ap.add_argument("--workload", choices=("c3", "c4", "c5", "c3-cached"), default="c3",
                     help="c3: single-token decode layer (the headline line); c4: batched "
                          "decode, 64 tokens with Zipf(1.1) logits; c5: prefill, 2048 tokens "
-                         "with uniform logits on the FP4 matrix unit")
+                         "with uniform logits on the FP4 matrix unit; c3-cached: the c3 "
+                         "layer with experts streamed from pinned host memory through an "
+                         "HBM cache of --cache-slots slots")
+    ap.add_argument("--cache-slots", type=int, default=128,
+                    help="HBM slots of the expert cache (c3-cached)")
     ap.add_argument("--calib", action="store_true",
                     help="after the timed region, copy 1 GiB device-to-device three times "
                          "(the known-size kernel the HBM byte counters are scaled by)")
@@ -110,6 +114,8 @@ def main():
         return bench_c4(args)
     if args.workload == "c5":
         return bench_c5(args)
+    if args.workload == "c3-cached":
+        return bench_c3_cached(args)
 
     dev = torch.device("cuda:0")
     n, hidden, inter, k = W.N_EXPERTS, W.HIDDEN, W.INTER, W.TOPK
@@ -293,6 +299,79 @@ def bench_c4(args):
             "kind": "oracle", "tokens_per_s": cb["tokens_per_s"],
             "sample": cb["sample"] + "; the oracle reads every selected expert once per token, "
                       "so a 64-token batch costs it 64 such layers"}
+    print(json.dumps(out))
+
+
+PEAK_H2D_GBS = 64.0  # PCIe 5.0 x16, one direction (the host link of one MI355X)
+
+
+def bench_c3_cached(args):
+    """The C3 decode layer with the 896 experts in pinned host memory and an
+    HBM cache of --cache-slots slots (LRU, k3_moe_layer_cached). One step is
+    one token: router and top-k, the selection to the host, the copies of
+    the missed experts, the expert launch. `value` is tokens/s; the host
+    link's rate (bytes copied over the whole time) is the roofline, since a
+    missed expert's 17.5 MB copy outweighs its HBM read 100-fold."""
+    import torch
+
+    import mxfp4_packed_weight_amd as K
+    from gen import device as D
+    from gen import workloads as W
+    dev = torch.device("cuda:0")
+    n, hidden, inter, k, S = W.N_EXPERTS, W.HIDDEN, W.INTER, W.TOPK, args.cache_slots
+    pool = D.build_expert_pool(0, W.C3, n, device=dev, log=log)
+    host = torch.empty(pool.blob.numel(), dtype=torch.uint8, pin_memory=True)
+    host.copy_(pool.blob)
+    eb = pool.expert_bytes
+    R = D.to_device(W.router_bf16(0, W.C3).view(np.int16), dev)
+    bank = D.to_device(W.tokens_bf16(0, W.C3, args.tokens, batch=1).view(np.int16), dev)
+    ws = torch.empty(K.k3_moe_workspace_bytes(1, n, hidden, inter, k), dtype=torch.uint8,
+                     device=dev)
+    y = torch.empty(hidden, dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+    cache = K.k3_cache_create(n, eb, S)
+    try:
+        for e in range(n):
+            K.k3_cache_set_source(cache, e, host[e * eb:(e + 1) * eb])
+
+        def step(i):
+            K.k3_moe_layer_cached(bank[i % args.tokens], R, cache, n, hidden, inter, k, y, ws,
+                                  stream=stream)
+
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        st0 = K.k3_cache_get_stats(cache)
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(args.warmup + i)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        st1 = K.k3_cache_get_stats(cache)
+    finally:
+        torch.cuda.synchronize()
+        K.k3_cache_destroy(cache)
+    d = {key: st1[key] - st0[key] for key in st1}
+    ms = dt * 1e3 / args.steps
+    h2d = d["bytes_copied"] / dt / 1e9
+    hit = (d["hits"] + d["inflight_reuses"]) / max(1, d["requests"])
+    log(f"C3 cached ({S} slots): {ms:.3f} ms/token, hit rate {hit:.3f}, H2D {h2d:.1f} GB/s")
+    out = {
+        "metric": "decode MoE-layer tokens/s, experts streamed from pinned host memory",
+        "value": round(1e3 / ms, 3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"decode MoE layer, 1 token, 896 MXFP4 experts (7168/1536) in "
+                               f"pinned host memory, {S}-slot HBM LRU cache "
+                               f"({S * eb / 1e9:.2f} GB)",
+                   "cache_slots": S, "n_experts": n, "topk": k},
+        "cache": {**d, "hit_rate": round(hit, 4),
+                  "experts_copied_per_token": round(d["misses"] / args.steps, 3)},
+        "roofline": {"kernel": "host-to-device copies of missed experts (copy engine)",
+                     "bound": "host link", "achieved": round(h2d, 2), "peak": PEAK_H2D_GBS,
+                     "unit": "GB/s", "frac": round(h2d / PEAK_H2D_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
     print(json.dumps(out))
 
 

@@ -316,6 +316,80 @@ k3_status k3_moe_prefill(const uint16_t *X, const double *logits,
                          float *h_f32, uint8_t *h_nib, uint8_t *h_sc, void *ws,
                          size_t ws_bytes, k3_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Expert cache: packed expert blobs (k3_expert_pack layout) in host memory,
+ * a fixed number of HBM slots holding the ones in use; the GPU counterpart
+ * of the pages' expert LRU that streams experts from NVMe into RAM ([ZOR]
+ * "How does a 2.78-trillion-parameter model fit in 8 GB?").
+ *
+ * A request names experts. Each is a hit (resident, copy finished), an
+ * in-flight reuse (its copy was issued and has not finished: the request's
+ * stream waits for that copy, none is issued twice) or a miss (copied from
+ * its host blob into an empty slot, else into the least recently used slot
+ * that is neither pinned nor named by the same request). Copies are
+ * asynchronous on the request's stream; keep one stream per cache so that a
+ * slot is overwritten only after the kernels queued before it. Host blobs
+ * should be pinned (hipHostMalloc) for the copies to be asynchronous.
+ *
+ * k3_cache_create     n_slots HBM slots of expert_bytes (a multiple of 256)
+ *                     for experts 0..n_experts-1 on the current device,
+ *                     plus one all-zero blob and the pointer table
+ *                     ((n_slots + 1) * expert_bytes + 8 * n_experts bytes).
+ *                     K3_ERR_CONFIG on sizes outside 1 <= n_slots <=
+ *                     n_experts <= K3_MAX_EXPERTS; *out is NULL on failure.
+ * k3_cache_destroy    frees everything; the caller first synchronises the
+ *                     streams that used the cache.
+ * k3_cache_set_source host blob of an expert (kept by the caller).
+ * k3_cache_pin        pinned experts are never evicted.
+ * k3_cache_fetch      makes ids[0..count) (host array) resident; K3_ERR_ARG
+ *                     for an id outside [0, n_experts), K3_ERR_CONFIG for a
+ *                     missing expert without a source, K3_ERR_MEMORY (and
+ *                     nothing changed) if the distinct misses exceed the
+ *                     slots that are neither pinned nor already named.
+ *                     Calls on one cache are serialised by a lock.
+ * k3_cache_table      device array of n_experts pointers (owned by the
+ *                     cache): a resident expert's entry points at its slot,
+ *                     every other entry at an all-zero blob of the same
+ *                     size. Pass it as `experts` to the layer calls on the
+ *                     fetch's stream.
+ * k3_cache_get_stats, k3_cache_histogram (n_experts counts), k3_cache_trace
+ *                     (every requested id in order; *len = full length,
+ *                     at most cap copied).
+ * k3_cache_replay     runs the same policy on a recorded trace on the host
+ *                     alone (requests of request_size ids, every copy taken
+ *                     as finished), e.g. to choose a slot count.
+ * k3_moe_layer_cached the decode layer for one token through a cache:
+ *                     router and top-k on the device, the selection copied
+ *                     to the host (this call waits for it), the fetch, then
+ *                     the expert launch on the cache's table. Arguments as
+ *                     k3_moe_layer_ex; refused while the stream is being
+ *                     captured (the host decides the copies).
+ * ---------------------------------------------------------------------- */
+typedef struct k3_cache_stats {
+  uint64_t requests, hits, misses, inflight_reuses, evictions, bytes_copied;
+} k3_cache_stats;
+typedef struct ExpertCacheImpl *k3_cache_t;
+
+k3_status k3_cache_create(int n_experts, size_t expert_bytes, int n_slots,
+                          k3_cache_t *out);
+void k3_cache_destroy(k3_cache_t cache);
+k3_status k3_cache_set_source(k3_cache_t cache, int expert, const void *host_blob);
+k3_status k3_cache_pin(k3_cache_t cache, int expert, int pinned);
+k3_status k3_cache_fetch(k3_cache_t cache, const int32_t *ids, int count,
+                         k3_stream_t stream);
+const uint8_t *const *k3_cache_table(k3_cache_t cache);
+k3_status k3_cache_get_stats(k3_cache_t cache, k3_cache_stats *out);
+k3_status k3_cache_histogram(k3_cache_t cache, uint64_t *counts);
+k3_status k3_cache_trace(k3_cache_t cache, int32_t *buf, size_t cap, size_t *len);
+k3_status k3_cache_replay(const int32_t *trace, size_t len, int n_experts,
+                          int n_slots, const int32_t *pinned, int n_pinned,
+                          int request_size, k3_cache_stats *out);
+k3_status k3_moe_layer_cached(const uint16_t *x, const uint16_t *router_w,
+                              k3_cache_t cache, int n_experts, int hidden,
+                              int inter, int k, uint16_t *y, float *y_f32,
+                              int32_t *idx, float *w, double *logits, void *ws,
+                              size_t ws_bytes, k3_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

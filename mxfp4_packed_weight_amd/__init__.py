@@ -23,6 +23,17 @@ K3_MAX_EXPERTS, K3_MAX_TOPK = 4096, 64
 
 # (name, restype, argtypes) of every exported symbol in include/k3moe.h
 _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+
+
+class k3_cache_stats(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_uint64) for f in
+                ("requests", "hits", "misses", "inflight_reuses", "evictions", "bytes_copied")]
+
+    def as_dict(self):
+        return {f: int(getattr(self, f)) for f, _ in self._fields_}
+
+
+_stats_p = ctypes.POINTER(k3_cache_stats)
 SIGNATURES = [
     ("k3_strerror", ctypes.c_char_p, [_i]),
     ("k3_last_error", ctypes.c_char_p, []),
@@ -60,6 +71,18 @@ SIGNATURES = [
     ("k3_moe_prefill_workspace_bytes", _sz, [_i, _i, _i, _i, _i]),
     ("k3_moe_prefill", _i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
                             _vp, _vp, _vp, _sz, _vp]),
+    ("k3_cache_create", _i, [_i, _sz, _i, ctypes.POINTER(_vp)]),
+    ("k3_cache_destroy", None, [_vp]),
+    ("k3_cache_set_source", _i, [_vp, _i, _vp]),
+    ("k3_cache_pin", _i, [_vp, _i, _i]),
+    ("k3_cache_fetch", _i, [_vp, _vp, _i, _vp]),
+    ("k3_cache_table", _vp, [_vp]),
+    ("k3_cache_get_stats", _i, [_vp, _stats_p]),
+    ("k3_cache_histogram", _i, [_vp, _vp]),
+    ("k3_cache_trace", _i, [_vp, _vp, _sz, ctypes.POINTER(_sz)]),
+    ("k3_cache_replay", _i, [_vp, _sz, _i, _i, _vp, _i, _i, _stats_p]),
+    ("k3_moe_layer_cached", _i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
+                                 _vp, _sz, _vp]),
 ]
 
 
@@ -106,9 +129,11 @@ def _call(name, *args):
 
 
 def _dp(t):
-    """Device pointer of a torch tensor (None -> NULL)."""
+    """Device pointer of a torch tensor or a raw address (None -> NULL)."""
     if t is None:
         return None
+    if isinstance(t, int):
+        return ctypes.c_void_p(t)
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -285,3 +310,77 @@ def k3_moe_prefill(X, logits, bias, experts, n_experts, hidden, inter, k, T, Y, 
     _call("k3_moe_prefill", _dp(X), _dp(logits), _dp(bias), _dp(experts), n_experts, hidden,
           inter, k, T, _dp(Y), _dp(Y_f32), _dp(idx), _dp(w), _dp(h_f32), _dp(h_nib), _dp(h_sc),
           _dp(ws), _nbytes(ws), _stream(stream))
+
+
+# ---- expert cache ---------------------------------------------------------
+# A cache is the opaque handle (an int) k3_cache_create returns; host blobs
+# are pinned CPU torch tensors or numpy arrays that the caller keeps alive.
+
+def _ids(ids):
+    a = np.ascontiguousarray(ids, np.int32)
+    return a, ctypes.c_void_p(a.ctypes.data)
+
+
+def k3_cache_create(n_experts, expert_bytes, n_slots):
+    h = _vp()
+    _call("k3_cache_create", n_experts, expert_bytes, n_slots, ctypes.byref(h))
+    return h.value
+
+
+def k3_cache_destroy(cache):
+    lib().k3_cache_destroy(_vp(cache))
+
+
+def k3_cache_set_source(cache, expert, host_blob):
+    ptr = host_blob.data_ptr() if hasattr(host_blob, "data_ptr") else host_blob.ctypes.data
+    _call("k3_cache_set_source", _vp(cache), expert, _vp(ptr))
+
+
+def k3_cache_pin(cache, expert, pinned=True):
+    _call("k3_cache_pin", _vp(cache), expert, int(bool(pinned)))
+
+
+def k3_cache_fetch(cache, ids, stream=None):
+    a, p = _ids(ids)
+    _call("k3_cache_fetch", _vp(cache), p, a.size, _stream(stream))
+
+
+def k3_cache_table(cache):
+    """Device address of the cache's expert pointer table (an int)."""
+    return lib().k3_cache_table(_vp(cache))
+
+
+def k3_cache_get_stats(cache):
+    st = k3_cache_stats()
+    _call("k3_cache_get_stats", _vp(cache), ctypes.byref(st))
+    return st.as_dict()
+
+
+def k3_cache_histogram(cache, n_experts):
+    out = np.zeros(n_experts, np.uint64)
+    _call("k3_cache_histogram", _vp(cache), _hp(out))
+    return out
+
+
+def k3_cache_trace(cache):
+    n = _sz()
+    _call("k3_cache_trace", _vp(cache), None, 0, ctypes.byref(n))
+    out = np.zeros(max(1, n.value), np.int32)
+    _call("k3_cache_trace", _vp(cache), _hp(out), out.size, ctypes.byref(n))
+    return out[:n.value]
+
+
+def k3_cache_replay(trace, n_experts, n_slots, pinned=(), request_size=1):
+    t, tp = _ids(trace)
+    pn, pp = _ids(pinned)
+    st = k3_cache_stats()
+    _call("k3_cache_replay", tp, t.size, n_experts, n_slots, pp if pn.size else None,
+          pn.size, request_size, ctypes.byref(st))
+    return st.as_dict()
+
+
+def k3_moe_layer_cached(x, router_w, cache, n_experts, hidden, inter, k, y, ws, y_f32=None,
+                        idx=None, w=None, logits=None, stream=None):
+    _call("k3_moe_layer_cached", _dp(x), _dp(router_w), _vp(cache), n_experts, hidden, inter,
+          k, _dp(y), _dp(y_f32), _dp(idx), _dp(w), _dp(logits), _dp(ws), _nbytes(ws),
+          _stream(stream))

@@ -584,6 +584,57 @@ k3_status k3_moe_layer_ex(const uint16_t *x, const uint16_t *router_w,
   return K3_OK;
 }
 
+k3_status k3_moe_layer_cached(const uint16_t *x, const uint16_t *router_w,
+                              k3_cache_t cache, int n_experts, int hidden,
+                              int inter, int k, uint16_t *y, float *y_f32,
+                              int32_t *idx, float *w, double *logits, void *ws,
+                              size_t ws_bytes, k3_stream_t stream) {
+  const char *fn = "k3_moe_layer_cached";
+  K3_NEED_PTR(fn, x);
+  K3_NEED_PTR(fn, router_w);
+  K3_NEED_PTR(fn, y);
+  K3_NEED_PTR(fn, ws);
+  if (!cache) return fail(K3_ERR_ARG, "%s: cache is NULL", fn);
+  if ((y_f32 && !aligned16(y_f32)) || (idx && !aligned16(idx)) ||
+      (w && !aligned16(w)) || (logits && !aligned16(logits)))
+    return fail(K3_ERR_ARG, "%s: an optional output is not 16-byte aligned", fn);
+  if (k3_status s = check_routing(fn, 1, n_experts, k)) return s;
+  if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
+  K3_NEED(fn, n_experts <= kFusedTopkMaxExperts,
+          "%s: n_experts=%d above the %d the expert launch ranks", fn, n_experts,
+          kFusedTopkMaxExperts);
+  K3_NEED(fn, moe_experts_grid() <= (unsigned)kMaxSyncGrid,
+          "%s: %u compute units exceed the %d arrival slots", fn,
+          moe_experts_grid(), kMaxSyncGrid);
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  K3_NEED(fn, hipStreamIsCapturing(stream, &cap) == hipSuccess &&
+                  cap == hipStreamCaptureStatusNone,
+          "%s: cannot be captured: the host chooses the copies per token", fn);
+  const WsLayout L = ws_layout(1, n_experts, hidden, inter, k);
+  if (k3_status s = need_ws(fn, ws_bytes, L.total)) return s;
+  uint8_t *base = static_cast<uint8_t *>(ws);
+  double *lg = logits ? logits : reinterpret_cast<double *>(base + L.logits);
+  int32_t *ix = idx ? idx : reinterpret_cast<int32_t *>(base + L.idx);
+  float *wt = w ? w : reinterpret_cast<float *>(base + L.w);
+  float *h = reinterpret_cast<float *>(base + L.h);
+  float *yp = reinterpret_cast<float *>(base + L.yp);
+  int32_t *sel = cache_selection_buffer(cache);
+  // the token's selection decides the copies: router and top-k, then wait
+  K3_LAUNCH(fn, launch_router(x, router_w, 1, hidden, n_experts, lg, stream));
+  K3_LAUNCH(fn, launch_topk_f64(lg, nullptr, 1, n_experts, k, ix, wt, stream));
+  K3_LAUNCH(fn, hipMemcpyAsync(sel, ix, sizeof(int32_t) * k, hipMemcpyDeviceToHost,
+                               stream));
+  K3_LAUNCH(fn, hipStreamSynchronize(stream));
+  if (k3_status s = k3_cache_fetch(cache, sel, k, stream)) return s;
+  // the expert launch ranks the same logits again and reads the cache's
+  // table, which holds every expert of this selection
+  K3_LAUNCH(fn, launch_moe_experts(x, lg, k3_cache_table(cache), n_experts, k,
+                                   hidden, inter, h, yp,
+                                   reinterpret_cast<uint64_t *>(base + L.sync),
+                                   next_layer_seq(), ix, wt, y, y_f32, stream));
+  return K3_OK;
+}
+
 k3_status k3_moe_layer(const uint16_t *x, const uint16_t *router_w,
                        const uint8_t *const *experts, int n_experts,
                        int hidden, int inter, int k, uint16_t *y, void *ws,

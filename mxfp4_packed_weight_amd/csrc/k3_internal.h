@@ -177,6 +177,9 @@ hipError_t launch_moe_experts(const uint16_t *x, const double *logits,
                               uint64_t *slots, uint64_t val, int32_t *idx,
                               float *w, uint16_t *y, float *y_f32,
                               hipStream_t s);
+// Pinned host buffer of K3_MAX_TOPK ints owned by an expert cache
+// (k3_cache.hip): where k3_moe_layer_cached receives a token's selection.
+int32_t *cache_selection_buffer(k3_cache_t c);
 hipError_t launch_router(const uint16_t *x, const uint16_t *R, int T,
                          int hidden, int n, double *logits, hipStream_t s);
 hipError_t launch_topk_f64(const double *logits, const float *bias, int T,

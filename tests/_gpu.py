@@ -38,3 +38,22 @@ def normwise(got, ref):
 
 
 TOL = 1e-5
+
+
+def pinned_copy(pool):
+    """Pinned host copy of an ExpertPool's packed blobs (the sources of an
+    expert cache)."""
+    import torch
+    host = torch.empty(pool.blob.numel(), dtype=torch.uint8, pin_memory=True)
+    host.copy_(pool.blob)
+    return host
+
+
+def make_cache(pool, host, n_slots):
+    """An expert cache of n_slots slots whose sources are `host`'s blobs."""
+    import mxfp4_packed_weight_amd as K
+    c = K.k3_cache_create(pool.n_experts, pool.expert_bytes, n_slots)
+    eb = pool.expert_bytes
+    for e in range(pool.n_experts):
+        K.k3_cache_set_source(c, e, host[e * eb:(e + 1) * eb])
+    return c

@@ -211,3 +211,27 @@ def test_one_token_from_logits_takes_the_decode_launch(c4_pool):
                                lambda e: W.expert_weights(0, W.C3, e, hidden, inter),
                                k, hidden, inter, [0])
             say(f"one token from logits: normwise {err:.3e}")
+
+
+def test_batched_layer_with_routing_bias():
+    """The routing bias steers selection only ([ZOR] "How is the C engine
+    actually built?", invariant 3): batched layer from logits with a bias
+    against the oracle's layer with the same bias (selection on sigmoid +
+    bias, weights from the unbiased scores)."""
+    cfg, seed, n, hidden, inter, k, T = 76, 10, 40, 256, 128, 6, 9
+    say("batched layer with a routing bias")
+    pool = D.build_expert_pool(seed, cfg, n, hidden, inter, 114, 120, workers=2)
+    X = W.tokens_bf16(seed, cfg, T, hidden)
+    logits = W.zipf_router_logits(seed, T, n, 1.1, cfg).astype(np.float64)
+    bias = W.routing_bias(seed, n, 0.5).astype(np.float32)
+    out = run_batched(pool, X, n, hidden, inter, k, logits=logits, bias=bias)
+    ex = {e: W.expert_weights(seed, cfg, e, hidden, inter, 114, 120) for e in range(n)}
+    oracle.set_threads(16)
+    Y_ref, idx_ref, w_ref = oracle.moe_from_logits(X, logits, ex, k, hidden, inter,
+                                                   bias=bias.astype(np.float64))
+    plain = np.stack([oracle.topk(logits[t], k)[0] for t in range(T)])
+    assert not np.array_equal(np.sort(plain, 1), np.sort(idx_ref, 1)), "bias changed nothing"
+    assert np.array_equal(out["idx"], idx_ref)
+    assert np.max(np.abs(out["w"] - w_ref)) <= 1e-6
+    for t in range(T):
+        assert normwise(out["Y32"][t], Y_ref[t]) <= TOL, t

@@ -1,0 +1,197 @@
+"""GPU checks of the expert cache through the C ABI.
+
+- The decode layer through a cache of fewer slots than experts gives the
+  same bits (y, fp32 y, top-k indices, weights, logits) as the layer on the
+  fully resident pool, token after token, while experts are evicted and
+  copied back in from pinned host blobs.
+- The live cache's counters equal those of the host-only replay of the
+  trace it recorded (every copy there had finished: the layer waits for the
+  selection before fetching), its histogram is the trace's, and every copy
+  moved one expert blob.
+- After each fetch the device table sends every requested expert to its own
+  slot (one request is never handed one slot twice: [SAT] "The bug the code
+  confesses to") and every other expert to a slot or to the all-zero blob.
+- A repeated request issues no second copy; pinned experts keep their slot
+  through evictions ([SAT] "The cache the project exists for").
+- Refusals: ids outside the pool, an expert with no source, a request larger
+  than the evictable slots, a capture of the cached layer.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import gen
+import mxfp4_packed_weight_amd as K
+from gen import device as D
+from gen import workloads as W
+from tests._gpu import empty, make_cache, pinned_copy, say, up
+
+pytestmark = pytest.mark.gpu
+
+CFG, SEED, N, HIDDEN, INTER, KTOP = 76, 11, 48, 384, 224, 8
+
+
+def hip_runtime():
+    """The HIP runtime this process already runs (torch's and the library's:
+    one runtime per process), opened by the path it was mapped from."""
+    paths = {line.split()[-1] for line in open("/proc/self/maps")
+             if "libamdhip64" in line and line.split()[-1].startswith("/")}
+    assert len(paths) == 1, paths
+    return ctypes.CDLL(paths.pop())
+
+
+def read_table(cache, n):
+    """The cache's device pointer table, copied to the host."""
+    import torch
+    torch.cuda.synchronize()
+    hip = hip_runtime()
+    hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    out = np.zeros(n, np.uint64)
+    rc = hip.hipMemcpy(out.ctypes.data, K.k3_cache_table(cache), 8 * n, 2)  # device to host
+    assert rc == 0
+    return out
+
+
+def layer(fn, table_or_cache, xd, R_d, n, hidden, inter, k, ws):
+    import torch
+    y = empty(hidden, torch.int16)
+    y32 = empty(hidden, torch.float32)
+    idx = empty(k, torch.int32)
+    w = empty(k, torch.float32)
+    lg = empty(n, torch.float64)
+    fn(xd, R_d, table_or_cache, n, hidden, inter, k, y, ws, y_f32=y32, idx=idx, w=w, logits=lg)
+    return dict(y=y.cpu().numpy().view(np.uint16), y32=y32.cpu().numpy().view(np.uint32),
+                idx=idx.cpu().numpy(), w=w.cpu().numpy().view(np.uint32),
+                logits=lg.cpu().numpy().view(np.uint64))
+
+
+def check_table(tab, idx, slot_lo, n_slots, expert_bytes):
+    sel = tab[idx]
+    assert len(set(sel.tolist())) == len(idx), "two requested experts share a slot"
+    off = sel.astype(np.int64) - int(slot_lo)
+    assert np.all((off >= 0) & (off < n_slots * expert_bytes) & (off % expert_bytes == 0))
+    inside = (tab >= slot_lo) & (tab < slot_lo + n_slots * expert_bytes)
+    outside = np.unique(tab[~inside])
+    assert outside.size <= 1, "non-resident entries must all name the zero blob"
+    resident = tab[inside]
+    assert len(np.unique(resident)) == resident.size, "two experts share a slot"
+    return outside
+
+
+@pytest.fixture(scope="module")
+def small_pool():
+    pool = D.build_expert_pool(SEED, CFG, N, HIDDEN, INTER, 114, 120, workers=2)
+    R = gen.normal_bf16(gen.key(SEED, CFG, gen.KIND_ROUTER), N * HIDDEN, 0, 0.02).reshape(
+        N, HIDDEN)
+    return pool, up(R), pinned_copy(pool)
+
+
+def test_cached_layer_matches_resident_layer(small_pool):
+    import torch
+    pool, R_d, host = small_pool
+    slots, tokens = 12, 24
+    say(f"cached layer: {N} experts through {slots} slots, {tokens} tokens")
+    ws = empty(K.k3_moe_workspace_bytes(1, N, HIDDEN, INTER, KTOP), torch.uint8)
+    ws2 = empty(K.k3_moe_workspace_bytes(1, N, HIDDEN, INTER, KTOP), torch.uint8)
+    X = W.tokens_bf16(SEED, CFG, tokens, HIDDEN)
+    c = make_cache(pool, host, slots)
+    try:
+        slot_lo = None
+        trace = []
+        for t in range(tokens):
+            xd = up(X[t])
+            want = layer(K.k3_moe_layer_ex, pool.table, xd, R_d, N, HIDDEN, INTER, KTOP, ws)
+            got = layer(K.k3_moe_layer_cached, c, xd, R_d, N, HIDDEN, INTER, KTOP, ws2)
+            for key in want:
+                assert np.array_equal(got[key], want[key]), (t, key)
+            trace.extend(got["idx"].tolist())
+            tab = read_table(c, N)
+            if slot_lo is None:
+                slot_lo = int(tab[got["idx"]].min())  # first token fills slots 0..k-1
+            check_table(tab, got["idx"], slot_lo, slots, pool.expert_bytes)
+        st = K.k3_cache_get_stats(c)
+        ref = K.k3_cache_replay(np.array(trace, np.int32), N, slots, (), KTOP)
+        assert st["bytes_copied"] == st["misses"] * pool.expert_bytes
+        ref["bytes_copied"] = st["bytes_copied"]
+        assert st == ref
+        assert st["evictions"] > 0, "the run must evict to exercise the cache"
+        assert np.array_equal(K.k3_cache_trace(c), np.array(trace, np.int32))
+        assert np.array_equal(K.k3_cache_histogram(c, N),
+                              np.bincount(trace, minlength=N).astype(np.uint64))
+        say(f"cached layer: {st}")
+    finally:
+        torch.cuda.synchronize()
+        K.k3_cache_destroy(c)
+
+
+def test_repeat_request_and_pins(small_pool):
+    import torch
+    pool, _, host = small_pool
+    c = make_cache(pool, host, 10)
+    try:
+        K.k3_cache_pin(c, 0)
+        K.k3_cache_pin(c, 1)
+        first = list(range(8))
+        K.k3_cache_fetch(c, first)
+        K.k3_cache_fetch(c, first)  # no synchronisation: copies may be in flight
+        st = K.k3_cache_get_stats(c)
+        assert st["misses"] == 8 and st["hits"] + st["inflight_reuses"] == 8
+        assert st["bytes_copied"] == 8 * pool.expert_bytes
+        tab0 = read_table(c, N)
+        K.k3_cache_fetch(c, list(range(8, 16)))  # evicts 2..7, never 0 and 1
+        tab1 = read_table(c, N)
+        assert tab1[0] == tab0[0] and tab1[1] == tab0[1]
+        zero = np.unique(tab0[16:])
+        assert zero.size == 1
+        assert np.all(tab1[2:8] == zero[0])
+        st = K.k3_cache_get_stats(c)
+        assert st["evictions"] == 6 and st["misses"] == 16
+        # unpinned, expert 0 is the least recently used and goes first
+        K.k3_cache_pin(c, 0, False)
+        K.k3_cache_fetch(c, [20])
+        tab2 = read_table(c, N)
+        assert tab2[0] == zero[0] and tab2[20] == tab0[0] and tab2[1] == tab0[1]
+    finally:
+        torch.cuda.synchronize()
+        K.k3_cache_destroy(c)
+
+
+def test_cache_refusals(small_pool):
+    import torch
+    pool, R_d, host = small_pool
+    c = K.k3_cache_create(N, pool.expert_bytes, 4)
+    try:
+        K.k3_cache_set_source(c, 3, host[3 * pool.expert_bytes:4 * pool.expert_bytes])
+        for ids, status in [([N], K.K3_ERR_ARG), ([-1], K.K3_ERR_ARG),
+                            ([5], K.K3_ERR_CONFIG)]:
+            with pytest.raises(K.K3Error) as e:
+                K.k3_cache_fetch(c, ids)
+            assert e.value.status == status
+        for e_ in range(N):
+            K.k3_cache_set_source(c, e_, host[e_ * pool.expert_bytes:(e_ + 1) * pool.expert_bytes])
+        with pytest.raises(K.K3Error) as e:
+            K.k3_cache_fetch(c, [0, 1, 2, 3, 4])
+        assert e.value.status == K.K3_ERR_MEMORY
+        assert K.k3_cache_get_stats(c)["requests"] == 0  # a refused request changes nothing
+        with pytest.raises(K.K3Error) as e:
+            K.k3_cache_create(N, pool.expert_bytes, N + 1)
+        assert e.value.status == K.K3_ERR_CONFIG
+        # captured, the cached layer is refused before it queues anything
+        ws = empty(K.k3_moe_workspace_bytes(1, N, HIDDEN, INTER, KTOP), torch.uint8)
+        xd = up(W.tokens_bf16(SEED, CFG, 1, HIDDEN)[0])
+        y = empty(HIDDEN, torch.int16)
+        s = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        refused = None
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            try:
+                K.k3_moe_layer_cached(xd, R_d, c, N, HIDDEN, INTER, KTOP, y, ws, stream=s)
+            except K.K3Error as err:
+                refused = err
+            y.zero_()
+        assert refused is not None and refused.status == K.K3_ERR_CONFIG
+    finally:
+        torch.cuda.synchronize()
+        K.k3_cache_destroy(c)

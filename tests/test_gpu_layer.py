@@ -19,7 +19,7 @@ import mxfp4_packed_weight_amd as K
 import oracle
 from gen import device as D
 from gen import workloads as W
-from tests._gpu import TOL, empty, normwise, say, up
+from tests._gpu import TOL, empty, make_cache, normwise, pinned_copy, say, up
 
 pytestmark = pytest.mark.gpu
 
@@ -188,6 +188,46 @@ def test_layer_c3_tokens_in_a_row(c3_pool):
         xd = up(X[t])
         out = layer_outputs(pool, R_d, xd, n, hidden, inter, k, ws)
         assert_same(out, stage_outputs(pool, R_d, xd, n, hidden, inter, k))
+
+
+def test_cached_layer_c3_full_size(c3_pool):
+    """The C3 layer with the 896 experts in pinned host memory behind a
+    40-slot HBM cache: six tokens, each bit-identical (y, fp32 y, indices,
+    weights) to the layer on the resident pool, the cache's counters equal
+    to the host replay of its trace."""
+    import torch
+    pool, R, R_d = c3_pool
+    n, hidden, inter, k = W.N_EXPERTS, W.HIDDEN, W.INTER, W.TOPK
+    say("cached layer C3: pinned host copy of the 896 experts, 40 slots")
+    host = pinned_copy(pool)
+    ws = empty(K.k3_moe_workspace_bytes(1, n, hidden, inter, k), torch.uint8)
+    X = W.tokens_bf16(0, W.C3, 6, hidden, batch=7)
+    c = make_cache(pool, host, 40)
+    try:
+        trace = []
+        for t in range(6):
+            xd = up(X[t])
+            want = layer_outputs(pool, R_d, xd, n, hidden, inter, k, ws)
+            y = empty(hidden, torch.int16)
+            y32 = empty(hidden, torch.float32)
+            idx = empty(k, torch.int32)
+            w = empty(k, torch.float32)
+            K.k3_moe_layer_cached(xd, R_d, c, n, hidden, inter, k, y, ws, y_f32=y32, idx=idx,
+                                  w=w)
+            assert np.array_equal(idx.cpu().numpy(), want["idx"])
+            assert np.array_equal(w.cpu().numpy().view(np.uint32), want["w"].view(np.uint32))
+            assert np.array_equal(y32.cpu().numpy().view(np.uint32), want["y32"].view(np.uint32))
+            assert np.array_equal(y.cpu().numpy().view(np.uint16), want["y"])
+            trace.extend(want["idx"].tolist())
+        st = K.k3_cache_get_stats(c)
+        ref = K.k3_cache_replay(np.array(trace, np.int32), n, 40, (), k)
+        ref["bytes_copied"] = st["misses"] * pool.expert_bytes
+        assert st == ref, (st, ref)
+        say(f"cached layer C3: {st}")
+    finally:
+        torch.cuda.synchronize()
+        K.k3_cache_destroy(c)
+        del host
 
 
 def test_layer_in_a_captured_graph():
