@@ -11,8 +11,11 @@
 - After each fetch the device table sends every requested expert to its own
   slot (one request is never handed one slot twice: [SAT] "The bug the code
   confesses to") and every other expert to a slot or to the all-zero blob.
-- A repeated request issues no second copy; pinned experts keep their slot
-  through evictions ([SAT] "The cache the project exists for").
+- A repeated request issues no second copy: while the first copies are
+  still queued it waits for them (in-flight reuse, the third slot state of
+  [SAT] "The bug the code confesses to"), afterwards it hits. Pinned
+  experts keep their slot through evictions ([SAT] "The cache the project
+  exists for").
 - Refusals: ids outside the pool, an expert with no source, a request larger
   than the evictable slots, a capture of the cached layer.
 """
@@ -152,6 +155,41 @@ def test_repeat_request_and_pins(small_pool):
         K.k3_cache_fetch(c, [20])
         tab2 = read_table(c, N)
         assert tab2[0] == zero[0] and tab2[20] == tab0[0] and tab2[1] == tab0[1]
+    finally:
+        torch.cuda.synchronize()
+        K.k3_cache_destroy(c)
+
+
+def test_inflight_copy_is_waited_for_not_repeated(small_pool):
+    """The stream is held by a bounded spin kernel, so the first fetch's
+    copies are still queued when the same experts are requested again: all
+    eight are in-flight reuses (no hit, no second copy). Once the stream
+    drains they are hits, and gate/up through the cache's table gives the
+    same bits as through the resident pool's."""
+    import torch
+    pool, _, host = small_pool
+    ids = [3, 9, 14, 22, 27, 31, 40, 45]
+    c = make_cache(pool, host, 10)
+    try:
+        torch.cuda.synchronize()
+        torch.cuda._sleep(50_000_000)  # tens of milliseconds of spinning, then it ends
+        K.k3_cache_fetch(c, ids)
+        K.k3_cache_fetch(c, ids)
+        st = K.k3_cache_get_stats(c)
+        assert st["misses"] == 8 and st["inflight_reuses"] == 8 and st["hits"] == 0, st
+        assert st["bytes_copied"] == 8 * pool.expert_bytes
+        torch.cuda.synchronize()
+        K.k3_cache_fetch(c, ids)
+        st = K.k3_cache_get_stats(c)
+        assert st["hits"] == 8 and st["misses"] == 8, st
+        xd = up(W.tokens_bf16(SEED, CFG, 1, HIDDEN)[0])
+        idx = up(np.array(ids, np.int32))
+        h_pool = empty((8, INTER), torch.float32)
+        h_cache = empty((8, INTER), torch.float32)
+        K.k3_expert_gate_up(xd, pool.table, idx, 8, HIDDEN, INTER, h_pool)
+        K.k3_expert_gate_up(xd, K.k3_cache_table(c), idx, 8, HIDDEN, INTER, h_cache)
+        assert np.array_equal(h_pool.cpu().numpy().view(np.uint32),
+                              h_cache.cpu().numpy().view(np.uint32))
     finally:
         torch.cuda.synchronize()
         K.k3_cache_destroy(c)
