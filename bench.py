@@ -80,12 +80,14 @@ def main():
     ap.add_argument("--tokens", type=int, default=512, help="distinct tokens in the bank")
     ap.add_argument("--router-copies", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=("c3", "c4", "c5", "c3-cached"), default="c3",
+    ap.add_argument("--workload", choices=("c3", "c4", "c5", "c3-cached", "c3-dequant"),
+                    default="c3",
                     help="c3: single-token decode layer (the headline line); c4: batched "
                          "decode, 64 tokens with Zipf(1.1) logits; c5: prefill, 2048 tokens "
                          "with uniform logits on the FP4 matrix unit; c3-cached: the c3 "
                          "layer with experts streamed from pinned host memory through an "
-                         "HBM cache of --cache-slots slots")
+                         "HBM cache of --cache-slots slots; c3-dequant: the expert stage "
+                         "from dequantised fp32 copies against the packed bytes")
     ap.add_argument("--cache-slots", type=int, default=128,
                     help="HBM slots of the expert cache (c3-cached)")
     ap.add_argument("--calib", action="store_true",
@@ -116,6 +118,8 @@ def main():
         return bench_c5(args)
     if args.workload == "c3-cached":
         return bench_c3_cached(args)
+    if args.workload == "c3-dequant":
+        return bench_c3_dequant(args)
 
     dev = torch.device("cuda:0")
     n, hidden, inter, k = W.N_EXPERTS, W.HIDDEN, W.INTER, W.TOPK
@@ -299,6 +303,92 @@ def bench_c4(args):
             "kind": "oracle", "tokens_per_s": cb["tokens_per_s"],
             "sample": cb["sample"] + "; the oracle reads every selected expert once per token, "
                       "so a 64-token batch costs it 64 such layers"}
+    print(json.dumps(out))
+
+
+def bench_c3_dequant(args):
+    """Dequantise-then-multiply control at C3 shapes. 64 experts are held
+    both packed (17.5 MB each) and as dense fp32 copies (132 MB each, 8.5 GB
+    in all); each step takes a fresh token and 16 distinct experts drawn
+    from the 64 (seeded), and the same selection runs through the packed
+    stages (k3_expert_gate_up, k3_expert_down) and the dense ones
+    (k3_experts_dense). `value` is the dense stage's time per token; the
+    packed time, the byte ratio (7.53) and the time ratio sit beside it."""
+    import torch
+
+    import mxfp4_packed_weight_amd as K
+    from gen import device as D
+    from gen import workloads as W
+    dev = torch.device("cuda:0")
+    hidden, inter, k, n = W.HIDDEN, W.INTER, W.TOPK, 64
+    pool = D.build_expert_pool(0, W.C3, n, device=dev, log=log)
+    db = K.k3_expert_dense_bytes(hidden, inter)
+    dense = torch.empty((n, db // 4), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for e in range(n):  # warm the kernel, then time the expansion of all 64
+        K.k3_expert_dequantize(pool.expert_view(e), hidden, inter, dense[e], stream)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for e in range(n):
+        K.k3_expert_dequantize(pool.expert_view(e), hidden, inter, dense[e], stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    dq_us = ev0.elapsed_time(ev1) * 1e3 / n
+    table = D.to_device(np.array([dense[e].data_ptr() for e in range(n)], np.uint64).view(
+        np.int64), dev)
+    T = args.tokens
+    rng = np.random.default_rng(2024)
+    sel = np.stack([rng.choice(n, k, replace=False) for _ in range(T)]).astype(np.int32)
+    idx = D.to_device(sel, dev)
+    bank = D.to_device(W.tokens_bf16(0, W.C3, T, batch=3).view(np.int16), dev)
+    h = torch.empty((k, inter), dtype=torch.float32, device=dev)
+    yp = torch.empty((k, hidden), dtype=torch.float32, device=dev)
+
+    def packed(i):
+        K.k3_expert_gate_up(bank[i % T], pool.table, idx[i % T], k, hidden, inter, h, stream)
+        K.k3_expert_down(h, pool.table, idx[i % T], k, hidden, inter, yp, stream)
+
+    def dense_step(i):
+        K.k3_experts_dense(bank[i % T], table, idx[i % T], k, hidden, inter, h, yp, stream)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(args.steps):
+            fn(args.warmup + i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3 / args.steps
+
+    p_us = timed(packed)
+    d_us = timed(dense_step)
+    p_bytes, d_bytes = k * BYTES_PER_EXPERT, k * db
+    log(f"C3 expert stage: packed {p_us:.1f} us ({p_bytes / p_us / 1e3:.0f} GB/s), dense fp32 "
+        f"{d_us:.1f} us ({d_bytes / d_us / 1e3:.0f} GB/s), ratio {d_us / p_us:.2f}; "
+        f"dequantise {dq_us:.1f} us per expert")
+    out = {
+        "metric": "expert stage per token from dequantised fp32 copies (control for the packed "
+                  "MXFP4 path)",
+        "value": round(d_us, 3), "unit": "us/token", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(d_us / 1e3, 6), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "16 SwiGLU experts (hidden 7168, inter 1536) per token, drawn "
+                               "from 64 held both packed and as dense fp32 (8.5 GB)",
+                   "n_experts": n, "topk": k},
+        "packed_us": round(p_us, 3), "dense_us": round(d_us, 3),
+        "time_ratio": round(d_us / p_us, 3), "byte_ratio": round(d_bytes / p_bytes, 3),
+        "dequantize_us_per_expert": round(dq_us, 2),
+        "dequantize_GBs": round((BYTES_PER_EXPERT + db) / dq_us / 1e3, 1),
+        "roofline": {"kernel": "dense_gate_up_kernel + dense_down_kernel (k3_experts_dense)",
+                     "bound": "hbm", "achieved": round(d_bytes / d_us / 1e3, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(d_bytes / d_us / 1e3 / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": d_bytes},
+        "cpu_baseline": None,
+    }
     print(json.dumps(out))
 
 

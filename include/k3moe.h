@@ -317,6 +317,35 @@ k3_status k3_moe_prefill(const uint16_t *X, const double *logits,
                          size_t ws_bytes, k3_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Dequantise-then-multiply control: the byte gap the pages price ([SAT]
+ * "Reduction one": an expert is 17.55 MB packed and 132 MB as floats; the
+ * product waits on bytes). Not on the packed path; it exists to measure it.
+ *
+ * k3_expert_dense_bytes  12 * hidden * inter (0 for unsupported shapes).
+ * k3_expert_dequantize   expert (k3_expert_pack blob, device) -> dense
+ *                        (device fp32, k3_expert_dense_bytes): gate
+ *                        [inter][hidden], up [inter][hidden], down
+ *                        [hidden][inter], row-major, back to back. Weight =
+ *                        E2M1(code) * 2^(e-127), exact for exponent bytes
+ *                        0..252 (253 and 254 may overflow to inf); groups
+ *                        with exponent byte 255 are written as zeros.
+ * k3_experts_dense       yp[j] = W_down h[j], h[j] = SiLU(W_gate x) *
+ *                        (W_up x) for the dense blob dense_experts[idx[j]],
+ *                        j < k: the stages of k3_expert_gate_up and
+ *                        k3_expert_down from dense fp32 copies (fp32
+ *                        accumulation, fixed order per row). x bf16
+ *                        [hidden], h fp32 [k][inter], yp fp32 [k][hidden];
+ *                        dense_experts a device pointer table, idx device
+ *                        int32 [k] indexing it. Pointers 16-byte aligned.
+ * ---------------------------------------------------------------------- */
+size_t k3_expert_dense_bytes(int hidden, int inter);
+k3_status k3_expert_dequantize(const uint8_t *expert, int hidden, int inter,
+                               float *dense, k3_stream_t stream);
+k3_status k3_experts_dense(const uint16_t *x, const float *const *dense_experts,
+                           const int32_t *idx, int k, int hidden, int inter,
+                           float *h, float *yp, k3_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Expert cache: packed expert blobs (k3_expert_pack layout) in host memory,
  * a fixed number of HBM slots holding the ones in use; the GPU counterpart
  * of the pages' expert LRU that streams experts from NVMe into RAM ([ZOR]

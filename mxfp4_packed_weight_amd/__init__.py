@@ -71,6 +71,9 @@ SIGNATURES = [
     ("k3_moe_prefill_workspace_bytes", _sz, [_i, _i, _i, _i, _i]),
     ("k3_moe_prefill", _i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
                             _vp, _vp, _vp, _sz, _vp]),
+    ("k3_expert_dense_bytes", _sz, [_i, _i]),
+    ("k3_expert_dequantize", _i, [_vp, _i, _i, _vp, _vp]),
+    ("k3_experts_dense", _i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
     ("k3_cache_create", _i, [_i, _sz, _i, ctypes.POINTER(_vp)]),
     ("k3_cache_destroy", None, [_vp]),
     ("k3_cache_set_source", _i, [_vp, _i, _vp]),
@@ -310,6 +313,21 @@ def k3_moe_prefill(X, logits, bias, experts, n_experts, hidden, inter, k, T, Y, 
     _call("k3_moe_prefill", _dp(X), _dp(logits), _dp(bias), _dp(experts), n_experts, hidden,
           inter, k, T, _dp(Y), _dp(Y_f32), _dp(idx), _dp(w), _dp(h_f32), _dp(h_nib), _dp(h_sc),
           _dp(ws), _nbytes(ws), _stream(stream))
+
+
+# ---- dequantise-then-multiply control -------------------------------------
+
+def k3_expert_dense_bytes(hidden, inter):
+    return lib().k3_expert_dense_bytes(hidden, inter)
+
+
+def k3_expert_dequantize(expert, hidden, inter, dense, stream=None):
+    _call("k3_expert_dequantize", _dp(expert), hidden, inter, _dp(dense), _stream(stream))
+
+
+def k3_experts_dense(x, dense_experts, idx, k, hidden, inter, h, yp, stream=None):
+    _call("k3_experts_dense", _dp(x), _dp(dense_experts), _dp(idx), k, hidden, inter, _dp(h),
+          _dp(yp), _stream(stream))
 
 
 # ---- expert cache ---------------------------------------------------------

@@ -421,6 +421,38 @@ k3_status k3_expert_gate_up(const uint16_t *x, const uint8_t *const *experts,
   return K3_OK;
 }
 
+size_t k3_expert_dense_bytes(int hidden, int inter) {
+  if (check_expert_dims("k3_expert_dense_bytes", hidden, inter) != K3_OK) return 0;
+  return (size_t)3 * hidden * inter * sizeof(float);
+}
+
+k3_status k3_expert_dequantize(const uint8_t *expert, int hidden, int inter,
+                               float *dense, k3_stream_t stream) {
+  const char *fn = "k3_expert_dequantize";
+  K3_NEED_PTR(fn, expert);
+  K3_NEED_PTR(fn, dense);
+  if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
+  K3_LAUNCH(fn, launch_dequant_expert(expert, hidden, inter, dense, stream));
+  return K3_OK;
+}
+
+k3_status k3_experts_dense(const uint16_t *x, const float *const *dense_experts,
+                           const int32_t *idx, int k, int hidden, int inter,
+                           float *h, float *yp, k3_stream_t stream) {
+  const char *fn = "k3_experts_dense";
+  K3_NEED_PTR(fn, x);
+  K3_NEED_PTR(fn, dense_experts);
+  K3_NEED_PTR(fn, idx);
+  K3_NEED_PTR(fn, h);
+  K3_NEED_PTR(fn, yp);
+  K3_NEED(fn, k >= 1 && k <= K3_MAX_TOPK, "%s: k=%d outside [1, %d]", fn, k,
+          K3_MAX_TOPK);
+  if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
+  K3_LAUNCH(fn, launch_experts_dense(x, dense_experts, idx, k, hidden, inter, h, yp,
+                                     stream));
+  return K3_OK;
+}
+
 k3_status k3_expert_gate_up_routed(const uint16_t *x, const double *logits,
                                    const uint8_t *const *experts, int n_experts,
                                    int k, int hidden, int inter, float *h,

@@ -163,6 +163,12 @@ hipError_t launch_gate_up_routed(const uint16_t *x, const double *logits,
                                  const uint8_t *const *experts, int n, int k,
                                  int hidden, int inter, float *h, int32_t *idx,
                                  float *w, hipStream_t s);
+// Dequantise-then-multiply control (k3_dense.hip).
+hipError_t launch_dequant_expert(const uint8_t *blob, int hidden, int inter,
+                                 float *dense, hipStream_t s);
+hipError_t launch_experts_dense(const uint16_t *x, const float *const *table,
+                                const int32_t *idx, int k, int hidden, int inter,
+                                float *h, float *yp, hipStream_t s);
 hipError_t launch_combine(const float *yp, const float *w, int k, int hidden,
                           uint16_t *y, float *y_f32, hipStream_t s);
 // The decode layer's expert work in one launch (k3_expert.hip): top-k of
