@@ -15,6 +15,7 @@ _SO = os.path.join(_HERE, "libk3gen.so")
 _lib = None
 
 KIND_MATRIX, KIND_EXPERT, KIND_ROUTER, KIND_TOKENS, KIND_LOGITS, KIND_BIAS = 1, 2, 3, 4, 5, 6
+KIND_SHARED = 7  # shared experts' bf16 weights
 
 
 def build():

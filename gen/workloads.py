@@ -12,7 +12,7 @@ Codes are uniform over the 16 E2M1 codes; exponent bytes uniform in
 counter-based stream keyed by (seed, config, kind, a, b), so any expert or
 token can be regenerated alone.
 """
-from . import (KIND_BIAS, KIND_LOGITS, KIND_ROUTER, KIND_TOKENS, expert, key,
+from . import (KIND_BIAS, KIND_LOGITS, KIND_ROUTER, KIND_SHARED, KIND_TOKENS, expert, key,
                mxfp4_matrix, normal_bf16, normal_f32, uniform_f32, zipf_logits)
 
 HIDDEN, INTER, N_EXPERTS, TOPK = 7168, 1536, 896, 16
@@ -49,6 +49,24 @@ def zipf_router_logits(seed, T, n_experts=N_EXPERTS, s=1.1, cfg=C4, batch=0):
 
 def uniform_router_logits(seed, T, n_experts=N_EXPERTS, cfg=C5, batch=0):
     return uniform_f32(key(seed, cfg, KIND_LOGITS, batch, 0), T * n_experts).reshape(T, n_experts)
+
+
+N_SHARED = 2
+SHARED_SIGMA = 0.02
+
+
+def shared_experts_bf16(seed, cfg=C3, n_shared=N_SHARED, hidden=HIDDEN, inter=INTER,
+                        sigma=SHARED_SIGMA):
+    """n_shared shared experts: dicts gate/up [inter][hidden], down
+    [hidden][inter], bf16 N(0, sigma) (the router's distribution)."""
+    out = []
+    for s in range(n_shared):
+        def m(i, rows, cols):
+            return normal_bf16(key(seed, cfg, KIND_SHARED, s, i), rows * cols, 0.0,
+                               sigma).reshape(rows, cols)
+        out.append({"gate": m(0, inter, hidden), "up": m(1, inter, hidden),
+                    "down": m(2, hidden, inter)})
+    return out
 
 
 def routing_bias(seed, n_experts=N_EXPERTS, scale=0.1, cfg=C3):

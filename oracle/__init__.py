@@ -31,6 +31,21 @@ class Expert(ctypes.Structure):
                 ("gate_nib", "gate_sc", "up_nib", "up_sc", "down_nib", "down_sc")]
 
 
+class Shared(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("gate", "up", "down")]
+
+
+def _shared_table(shared):
+    """shared: list of dicts gate/up/down -> bf16 arrays (uint16)."""
+    table = (Shared * max(1, len(shared)))()
+    keep = []
+    for i, S in enumerate(shared):
+        arrs = [_c(S[m], np.uint16) for m in ("gate", "up", "down")]
+        table[i] = Shared(*[a.ctypes.data for a in arrs])
+        keep.append(arrs)
+    return table, keep
+
+
 def _declare(L):
     i, d, vp = ctypes.c_int, ctypes.c_double, ctypes.c_void_p
     L.k3o_e2m1.restype = d
@@ -55,6 +70,8 @@ def _declare(L):
     L.k3o_mxfp4_quant.argtypes = [vp, i, i, vp, vp]
     L.k3o_mxfp4_matmul.argtypes = [vp, vp, i, vp, vp, i, i, vp]
     L.k3o_set_threads.argtypes = [i]
+    L.k3o_shared_expert.argtypes = [ctypes.POINTER(Shared), i, i, vp, vp, vp]
+    L.k3o_moe_layer_shared.argtypes = [vp, vp, vp, i, i, i, i, vp, i, i, vp, vp, vp]
     return L
 
 
@@ -190,6 +207,34 @@ class Oracle:
         _check(self.L.k3o_moe_layer(_p(x), _p(R), ctypes.cast(table, ctypes.c_void_p), n,
                                     hidden, inter, k, _p(y), _p(idx), _p(w)), "moe_layer")
         del keep
+        return y, idx, w
+
+    def shared_expert(self, S, x):
+        """S: dict gate/up [inter][hidden], down [hidden][inter] bf16 (uint16).
+        Returns (y [hidden], h [inter]) in fp64."""
+        inter, hidden = S["gate"].shape
+        table, keep = _shared_table([S])
+        x = _c(x, np.float64)
+        y = np.zeros(hidden, np.float64)
+        h = np.zeros(inter, np.float64)
+        _check(self.L.k3o_shared_expert(table, hidden, inter, _p(x), _p(h), _p(y)), "shared")
+        del keep
+        return y, h
+
+    def moe_layer_shared(self, x_bf16, R_bf16, experts, k, hidden, inter, shared):
+        x, R = _c(x_bf16, np.uint16), _c(R_bf16, np.uint16)
+        n = R.shape[0]
+        table, keep = _expert_table(experts, n)
+        stab, skeep = _shared_table(shared)
+        inter_s = shared[0]["gate"].shape[0] if shared else 0
+        y = np.zeros(hidden, np.float64)
+        idx = np.zeros(k, np.int32)
+        w = np.zeros(k, np.float64)
+        _check(self.L.k3o_moe_layer_shared(_p(x), _p(R), ctypes.cast(table, ctypes.c_void_p),
+                                           n, hidden, inter, k,
+                                           ctypes.cast(stab, ctypes.c_void_p), len(shared),
+                                           inter_s, _p(y), _p(idx), _p(w)), "moe_layer_shared")
+        del keep, skeep
         return y, idx, w
 
     def moe_from_logits(self, X_bf16, logits, experts, k, hidden, inter, bias=None):

@@ -290,6 +290,65 @@ int k3o_moe_from_logits(const uint16_t *X, const double *logits,
   return 0;
 }
 
+/* ---------------------------------------------------------------------- */
+/* Shared experts                                                          */
+/* ---------------------------------------------------------------------- */
+
+/* One shared expert: a SwiGLU FFN whose three matrices are bf16 and stay in
+ * the resident set, run on every token beside the routed ones ([ZOR] "How
+ * does a 2.78-trillion-parameter model fit in 8 GB?": two shared experts per
+ * layer, classed with the always-on bf16 weights). The pages give neither
+ * their width nor how their output joins the routed one; the reading taken
+ * here: the routed expert's shapes, and y = routed mix + the shared outputs,
+ * unweighted. g = W_gate x, u = W_up x, h = SiLU(g) * u, y = W_down h, all in
+ * double over the exactly widened bf16 weights; sums run in index order. */
+static double dot_bf16_row(const uint16_t *row, const double *v, int n) {
+  double acc = 0.0;
+  for (int c = 0; c < n; c++) acc += k3o_bf16_to_f64(row[c]) * v[c];
+  return acc;
+}
+
+int k3o_shared_expert(const k3o_shared *S, int hidden, int inter,
+                      const double *x, double *h, double *y) {
+  if (!S || !S->gate || !S->up || !S->down || !x || !y) return 1;
+  if (hidden <= 0 || inter <= 0) return 2;
+  double *hh = h ? h : (double *)malloc(sizeof(double) * (size_t)inter);
+  if (!hh) return 1;
+  for (int i = 0; i < inter; i++) {
+    const double g = dot_bf16_row(S->gate + (size_t)i * hidden, x, hidden);
+    const double u = dot_bf16_row(S->up + (size_t)i * hidden, x, hidden);
+    hh[i] = k3o_silu(g) * u;
+  }
+  for (int r = 0; r < hidden; r++)
+    y[r] = dot_bf16_row(S->down + (size_t)r * inter, hh, inter);
+  if (!h) free(hh);
+  return 0;
+}
+
+/* The decode layer with shared experts: the routed layer's y, then the
+ * shared experts' outputs added in order s = 0, 1, ... */
+int k3o_moe_layer_shared(const uint16_t *x, const uint16_t *R,
+                         const k3o_expert *experts, int n_experts, int hidden,
+                         int inter, int k, const k3o_shared *shared,
+                         int n_shared, int inter_shared, double *y,
+                         int32_t *idx, double *w) {
+  if (!shared && n_shared > 0) return 1;
+  if (n_shared < 0) return 2;
+  int rc = k3o_moe_layer(x, R, experts, n_experts, hidden, inter, k, y, idx, w);
+  if (rc) return rc;
+  double *xd = (double *)malloc(sizeof(double) * (size_t)hidden);
+  double *ys = (double *)malloc(sizeof(double) * (size_t)hidden);
+  if (!xd || !ys) rc = 1;
+  for (int i = 0; !rc && i < hidden; i++) xd[i] = k3o_bf16_to_f64(x[i]);
+  for (int s = 0; !rc && s < n_shared; s++) {
+    rc = k3o_shared_expert(&shared[s], hidden, inter_shared, xd, NULL, ys);
+    for (int r = 0; !rc && r < hidden; r++) y[r] += ys[r];
+  }
+  free(xd);
+  free(ys);
+  return rc;
+}
+
 /* Pairs (t, j) grouped by expert, ascending token inside each expert. */
 int k3o_permute(const int32_t *idx, int T, int k, int n_experts,
                 int32_t *counts, int32_t *offsets, int32_t *pair_token,

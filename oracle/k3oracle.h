@@ -90,6 +90,22 @@ int k3o_permute(const int32_t *idx, int T, int k, int n_experts,
                 int32_t *counts, int32_t *offsets, int32_t *pair_token,
                 int32_t *pair_slot);
 
+/* ---- shared experts (bf16, every token) -------------------------------- */
+typedef struct {
+  const uint16_t *gate, *up; /* bf16 [inter][hidden], row-major */
+  const uint16_t *down;      /* bf16 [hidden][inter], row-major */
+} k3o_shared;
+int k3o_shared_expert(const k3o_shared *S, int hidden, int inter,
+                      const double *x, double *h /* [inter] or NULL */,
+                      double *y /* [hidden] */);
+/* The routed layer (k3o_moe_layer) plus the n_shared shared experts'
+ * outputs, added in order. */
+int k3o_moe_layer_shared(const uint16_t *x, const uint16_t *R,
+                         const k3o_expert *experts, int n_experts, int hidden,
+                         int inter, int k, const k3o_shared *shared,
+                         int n_shared, int inter_shared, double *y,
+                         int32_t *idx, double *w);
+
 /* ---- MXFP4 activation quantiser (prefill) ------------------------------ */
 int k3o_mxfp4_quant(const double *v, int rows, int cols, uint8_t *nib,
                     uint8_t *sc);

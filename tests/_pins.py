@@ -139,6 +139,63 @@ def check_expert_crosscheck(O, hidden=256, inter=96, seed=21, elo=114, ehi=120):
     assert np.max(np.abs(y - yy)) <= 1e-12 * np.max(np.abs(yy))
 
 
+def check_shared_expert_crosscheck(O, hidden=320, inter=96, seed=22):
+    """The shared expert (bf16 weights) against numpy: matrices widened from
+    their bf16 bits, matmul, SiLU in its tanh form."""
+    from gen import workloads as W
+    S = W.shared_experts_bf16(seed, 96, 1, hidden, inter, 0.05)[0]
+    x = I.bf16_to_float_bits(gen.normal_bf16(gen.key(seed, 96, gen.KIND_TOKENS), hidden))
+    y, h = O.shared_expert(S, x)
+    g = I.bf16_to_float_bits(S["gate"]) @ x
+    u = I.bf16_to_float_bits(S["up"]) @ x
+    hh = np.array([I.silu_tanh_form(a) for a in g]) * u
+    yy = I.bf16_to_float_bits(S["down"]) @ hh
+    assert np.max(np.abs(h - hh)) <= 1e-12 * np.max(np.abs(hh))
+    assert np.max(np.abs(y - yy)) <= 1e-12 * np.max(np.abs(yy))
+
+
+def check_shared_expert_by_hand(O):
+    """hidden 32, inter 32: gate row i = 2 e_i, up row i = e_{i+1}, down =
+    identity rows 0..31, x_j = j/8: h_i = SiLU(2 x_i) x_{i+1}, y = h."""
+    n = 32
+    def bf(a):
+        return (np.asarray(a, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    gate = np.zeros((n, n)); up = np.zeros((n, n)); down = np.eye(n)
+    for i in range(n):
+        gate[i, i] = 2.0
+        up[i, (i + 1) % n] = 1.0
+    x = np.arange(n) / 8.0
+    S = {"gate": bf(gate), "up": bf(up), "down": bf(down)}
+    y, h = O.shared_expert(S, x)
+    want = np.array([2 * x[i] / (1 + np.exp(-2 * x[i])) * x[(i + 1) % n] for i in range(n)])
+    assert np.max(np.abs(h - want)) <= 1e-14 * np.max(np.abs(want))
+    assert np.max(np.abs(y - want)) <= 1e-14 * np.max(np.abs(want))
+
+
+def check_layer_shared_adds(O, seed=33):
+    """The layer with shared experts is the routed layer plus each shared
+    output (numpy-computed), added in order."""
+    from gen import workloads as W
+    n, hidden, inter, k, inter_s = 12, 128, 64, 3, 96
+    R = gen.normal_bf16(gen.key(seed, 97, gen.KIND_ROUTER), n * hidden, 0, 0.05).reshape(n, hidden)
+    x = gen.normal_bf16(gen.key(seed, 97, gen.KIND_TOKENS), hidden)
+    experts = {e: gen.expert(seed, 97, e, hidden, inter, 114, 120) for e in range(n)}
+    shared = W.shared_experts_bf16(seed, 97, 2, hidden, inter_s, 0.05)
+    y0, idx0, w0 = O.moe_layer(x, R, experts, k, hidden, inter)
+    y1, idx1, w1 = O.moe_layer_shared(x, R, experts, k, hidden, inter, shared)
+    assert np.array_equal(idx0, idx1) and np.array_equal(w0, w1)
+    xf = I.bf16_to_float_bits(x)
+    want = y0.copy()
+    for S in shared:
+        g = I.bf16_to_float_bits(S["gate"]) @ xf
+        u = I.bf16_to_float_bits(S["up"]) @ xf
+        want += I.bf16_to_float_bits(S["down"]) @ (np.array([I.silu_tanh_form(a) for a in g]) * u)
+    assert np.max(np.abs(y1 - want)) <= 1e-12 * np.max(np.abs(want))
+    # no shared experts: the plain layer, bit for bit
+    y2, _, _ = O.moe_layer_shared(x, R, experts, k, hidden, inter, [])
+    assert np.array_equal(y2, y0)
+
+
 def check_silu(O):
     assert O.silu(0.0) == 0.0
     for v in [0.1, 0.5, 1.0, 2.0, 5.0, 10.0, 30.0, 100.0, 1000.0]:
@@ -324,4 +381,5 @@ ALL = [check_e2m1_table, check_e8m0, check_golden_nibble_order, check_bruteforce
        check_router_logits, check_topk_bruteforce, check_topk_ties_lower_index,
        check_topk_bias_selects_only, check_combine, check_moe_layer_small,
        check_quant_ties_and_saturation, check_quant_invariants, check_quant_roundtrip,
-       check_matmul, check_permute]
+       check_matmul, check_permute, check_shared_expert_crosscheck, check_shared_expert_by_hand,
+       check_layer_shared_adds]

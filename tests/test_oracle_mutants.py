@@ -36,6 +36,12 @@ MUTANTS = {
     "quant_scale_off_by_one": ("int E = (ex - 1) - 2;", "int E = (ex - 1) - 3;"),
     "router_drops_last_term": ("for (int k = 0; k < hidden; k++)\n      acc +=",
                                "for (int k = 0; k < hidden - 1; k++)\n      acc +="),
+    "shared_gate_up_swapped": ("hh[i] = k3o_silu(g) * u;", "hh[i] = k3o_silu(u) * g;"),
+    "shared_down_transposed": ("y[r] = dot_bf16_row(S->down + (size_t)r * inter, hh, inter);",
+                               "{ y[r] = 0.0; for (int c = 0; c < inter; c++) y[r] += "
+                               "k3o_bf16_to_f64(S->down[(size_t)c * hidden + r]) * hh[c]; }"),
+    "shared_not_added": ("for (int r = 0; !rc && r < hidden; r++) y[r] += ys[r];",
+                         "(void)ys;"),
     "combine_drops_rank0": ("for (int j = 0; j < k; j++) acc += w[j] * ye[(size_t)j * hidden + i];",
                             "for (int j = 1; j < k; j++) acc += w[j] * ye[(size_t)j * hidden + i];"),
 }
