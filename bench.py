@@ -80,14 +80,15 @@ def main():
     ap.add_argument("--tokens", type=int, default=512, help="distinct tokens in the bank")
     ap.add_argument("--router-copies", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=("c3", "c4", "c5", "c3-cached", "c3-dequant"),
-                    default="c3",
+    ap.add_argument("--workload", choices=("c3", "c4", "c5", "c3-cached", "c3-dequant",
+                                           "c3-shared"), default="c3",
                     help="c3: single-token decode layer (the headline line); c4: batched "
                          "decode, 64 tokens with Zipf(1.1) logits; c5: prefill, 2048 tokens "
                          "with uniform logits on the FP4 matrix unit; c3-cached: the c3 "
                          "layer with experts streamed from pinned host memory through an "
                          "HBM cache of --cache-slots slots; c3-dequant: the expert stage "
-                         "from dequantised fp32 copies against the packed bytes")
+                         "from dequantised fp32 copies against the packed bytes; c3-shared: "
+                         "the c3 layer plus two bf16 shared experts (7168/1536)")
     ap.add_argument("--cache-slots", type=int, default=128,
                     help="HBM slots of the expert cache (c3-cached)")
     ap.add_argument("--calib", action="store_true",
@@ -120,6 +121,8 @@ def main():
         return bench_c3_cached(args)
     if args.workload == "c3-dequant":
         return bench_c3_dequant(args)
+    if args.workload == "c3-shared":
+        return bench_c3_shared(args)
 
     dev = torch.device("cuda:0")
     n, hidden, inter, k = W.N_EXPERTS, W.HIDDEN, W.INTER, W.TOPK
@@ -387,6 +390,78 @@ def bench_c3_dequant(args):
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(d_bytes / d_us / 1e3 / PEAK_HBM_GBS, 4), "traffic": None,
                      "algorithmic_bytes_per_launch": d_bytes},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out))
+
+
+def bench_c3_shared(args):
+    """The C3 decode layer with two shared experts (bf16, hidden 7168, inter
+    1536: 132 MB read on every token) added to the routed mix. `value` is the
+    effective HBM rate of all weights a token reads (16 routed experts'
+    packed bytes, the shared experts' bf16 bytes, the router) over the layer
+    time; the shared stage alone is timed for its roofline."""
+    import torch
+
+    import mxfp4_packed_weight_amd as K
+    from gen import device as D
+    from gen import workloads as W
+    dev = torch.device("cuda:0")
+    n, hidden, inter, k, ns = W.N_EXPERTS, W.HIDDEN, W.INTER, W.TOPK, W.N_SHARED
+    pool = D.build_expert_pool(0, W.C3, n, device=dev, log=log)
+    shared = W.shared_experts_bf16(0, W.C3)
+    blobs = [D.to_device(np.concatenate([S["gate"].ravel(), S["up"].ravel(),
+                                         S["down"].ravel()]).view(np.int16), dev)
+             for S in shared]
+    table = D.to_device(np.array([b.data_ptr() for b in blobs], np.uint64).view(np.int64), dev)
+    R = D.to_device(W.router_bf16(0, W.C3).view(np.int16), dev)
+    routers = [R] + [R.clone() for _ in range(args.router_copies - 1)]
+    bank = D.to_device(W.tokens_bf16(0, W.C3, args.tokens, batch=1).view(np.int16), dev)
+    ws = torch.empty(K.k3_moe_layer_shared_workspace_bytes(n, hidden, inter, k, ns, inter),
+                     dtype=torch.uint8, device=dev)
+    y = torch.empty(hidden, dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, steps):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(steps):
+            fn(args.warmup + i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3 / steps
+
+    us = timed(lambda i: K.k3_moe_layer_shared(
+        bank[i % args.tokens], routers[i % len(routers)], pool.table, n, hidden, inter, k,
+        table, ns, inter, y, ws, stream=stream), args.steps)
+    h = torch.empty((ns, inter), dtype=torch.float32, device=dev)
+    ys = torch.empty(hidden, dtype=torch.float32, device=dev)
+    sh_us = timed(lambda i: K.k3_shared_experts(bank[i % args.tokens], table, ns, hidden, inter,
+                                                h, ys, stream), max(args.steps, 50))
+    sbytes = ns * K.k3_shared_expert_bytes(hidden, inter)
+    total = k * BYTES_PER_EXPERT + sbytes + ROUTER_BYTES
+    value = total / us / 1e3
+    log(f"C3 layer + {ns} shared experts: {us:.2f} us/token, {value:.1f} GB/s of weights; "
+        f"shared stage {sh_us:.2f} us ({sbytes / sh_us / 1e3:.1f} GB/s)")
+    out = {
+        "metric": "effective HBM GB/s of all weights a decode token reads (routed MXFP4 + "
+                  "shared bf16 + router); MoE-layer tokens/s",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "decode MoE layer, 1 token: router 896x7168, top-16 of 896 "
+                               "MXFP4 experts (7168/1536) + 2 bf16 shared experts (7168/1536)",
+                   "n_experts": n, "topk": k, "n_shared": ns, "bytes_per_step": total},
+        "tokens_per_s": round(1e6 / us, 1),
+        "shared_stage_us": round(sh_us, 3),
+        "roofline": {"kernel": "shared_gate_up_kernel + shared_down_kernel (k3_shared_experts)",
+                     "bound": "hbm", "achieved": round(sbytes / sh_us / 1e3, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(sbytes / sh_us / 1e3 / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": sbytes},
         "cpu_baseline": None,
     }
     print(json.dumps(out))

@@ -64,6 +64,7 @@ typedef int k3_status;
  * expert dimensions (the expert kernels keep one activation vector in LDS). */
 #define K3_MAX_EXPERTS 4096
 #define K3_MAX_TOPK 64
+#define K3_MAX_SHARED 8
 #define K3_MAX_HIDDEN 16384
 #define K3_MAX_INTER 4096
 
@@ -315,6 +316,43 @@ k3_status k3_moe_prefill(const uint16_t *X, const double *logits,
                          uint16_t *Y, float *Y_f32, int32_t *idx, float *w,
                          float *h_f32, uint8_t *h_nib, uint8_t *h_sc, void *ws,
                          size_t ws_bytes, k3_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Shared experts: SwiGLU FFNs with bf16 weights that run on every token and
+ * are added to the routed mix ([ZOR] "How does a 2.78-trillion-parameter
+ * model fit in 8 GB?": two per layer, in the always-on bf16 set; the pages
+ * give neither their width nor how they join the routed output: here any
+ * inter_shared (a multiple of 32, <= K3_MAX_INTER) and an unweighted sum).
+ *
+ * k3_shared_expert_bytes  6 * hidden * inter (0 for unsupported shapes).
+ * k3_shared_experts       ys[r] = sum_{s < n_shared} (W_down(s) h[s])[r],
+ *                         h[s] = SiLU(W_gate(s) x) * (W_up(s) x). shared: a
+ *                         device array of n_shared device pointers, each to a
+ *                         blob of gate [inter][hidden], up [inter][hidden],
+ *                         down [hidden][inter], bf16 row-major, 16-byte
+ *                         aligned. x bf16 [hidden]; h fp32 [n_shared][inter];
+ *                         ys fp32 [hidden]. 1 <= n_shared <= K3_MAX_SHARED.
+ *                         fp32 accumulation in a fixed order per row.
+ * k3_moe_layer_shared     the decode layer of k3_moe_layer_ex with the
+ *                         shared experts' ys added to each output row after
+ *                         the routed rank-order sum (y_f32 = routed + ys,
+ *                         then y = bf16 RNE of it). n_shared may be 0 (then
+ *                         the plain layer). Workspace of
+ *                         k3_moe_layer_shared_workspace_bytes bytes.
+ * ---------------------------------------------------------------------- */
+size_t k3_shared_expert_bytes(int hidden, int inter);
+k3_status k3_shared_experts(const uint16_t *x, const uint16_t *const *shared,
+                            int n_shared, int hidden, int inter, float *h,
+                            float *ys, k3_stream_t stream);
+size_t k3_moe_layer_shared_workspace_bytes(int n_experts, int hidden, int inter,
+                                           int k, int n_shared, int inter_shared);
+k3_status k3_moe_layer_shared(const uint16_t *x, const uint16_t *router_w,
+                              const uint8_t *const *experts, int n_experts,
+                              int hidden, int inter, int k,
+                              const uint16_t *const *shared, int n_shared,
+                              int inter_shared, uint16_t *y, float *y_f32,
+                              int32_t *idx, float *w, double *logits, void *ws,
+                              size_t ws_bytes, k3_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Dequantise-then-multiply control: the byte gap the pages price ([SAT]

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libk3moe.so")
 _lib = None
 
 K3_OK, K3_ERR_ARG, K3_ERR_CONFIG, K3_ERR_MEMORY, K3_ERR_DEVICE = 0, 1, 2, 3, 4
-K3_MAX_EXPERTS, K3_MAX_TOPK = 4096, 64
+K3_MAX_EXPERTS, K3_MAX_TOPK, K3_MAX_SHARED = 4096, 64, 8
 
 # (name, restype, argtypes) of every exported symbol in include/k3moe.h
 _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -71,6 +71,11 @@ SIGNATURES = [
     ("k3_moe_prefill_workspace_bytes", _sz, [_i, _i, _i, _i, _i]),
     ("k3_moe_prefill", _i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
                             _vp, _vp, _vp, _sz, _vp]),
+    ("k3_shared_expert_bytes", _sz, [_i, _i]),
+    ("k3_shared_experts", _i, [_vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
+    ("k3_moe_layer_shared_workspace_bytes", _sz, [_i, _i, _i, _i, _i, _i]),
+    ("k3_moe_layer_shared", _i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _vp, _vp, _vp,
+                                 _vp, _vp, _vp, _sz, _vp]),
     ("k3_expert_dense_bytes", _sz, [_i, _i]),
     ("k3_expert_dequantize", _i, [_vp, _i, _i, _vp, _vp]),
     ("k3_experts_dense", _i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
@@ -313,6 +318,30 @@ def k3_moe_prefill(X, logits, bias, experts, n_experts, hidden, inter, k, T, Y, 
     _call("k3_moe_prefill", _dp(X), _dp(logits), _dp(bias), _dp(experts), n_experts, hidden,
           inter, k, T, _dp(Y), _dp(Y_f32), _dp(idx), _dp(w), _dp(h_f32), _dp(h_nib), _dp(h_sc),
           _dp(ws), _nbytes(ws), _stream(stream))
+
+
+# ---- shared experts ---------------------------------------------------------
+
+def k3_shared_expert_bytes(hidden, inter):
+    return lib().k3_shared_expert_bytes(hidden, inter)
+
+
+def k3_shared_experts(x, shared, n_shared, hidden, inter, h, ys, stream=None):
+    _call("k3_shared_experts", _dp(x), _dp(shared), n_shared, hidden, inter, _dp(h), _dp(ys),
+          _stream(stream))
+
+
+def k3_moe_layer_shared_workspace_bytes(n_experts, hidden, inter, k, n_shared, inter_shared):
+    return lib().k3_moe_layer_shared_workspace_bytes(n_experts, hidden, inter, k, n_shared,
+                                                     inter_shared)
+
+
+def k3_moe_layer_shared(x, router_w, experts, n_experts, hidden, inter, k, shared, n_shared,
+                        inter_shared, y, ws, y_f32=None, idx=None, w=None, logits=None,
+                        stream=None):
+    _call("k3_moe_layer_shared", _dp(x), _dp(router_w), _dp(experts), n_experts, hidden, inter,
+          k, _dp(shared), n_shared, inter_shared, _dp(y), _dp(y_f32), _dp(idx), _dp(w),
+          _dp(logits), _dp(ws), _nbytes(ws), _stream(stream))
 
 
 # ---- dequantise-then-multiply control -------------------------------------

@@ -561,6 +561,49 @@ size_t k3_moe_workspace_bytes(int T, int n_experts, int hidden, int inter,
   return ws_layout(T, n_experts, hidden, inter, k).total;
 }
 
+// The layer's launches once its arguments are checked: router, then the
+// expert work in one launch (its stages marked by a per-call value; a graph
+// being captured would replay one value, so it gets the separate launches,
+// as does a selection over more than 1024 experts). `add` (or NULL) is
+// added to each output row before the bf16 cast.
+static k3_status layer_launches(const char *fn, const uint16_t *x,
+                                const uint16_t *router_w,
+                                const uint8_t *const *experts, int n_experts,
+                                int hidden, int inter, int k, uint16_t *y,
+                                float *y_f32, int32_t *idx, float *w,
+                                double *logits, uint8_t *base, const WsLayout &L,
+                                const float *add, hipStream_t stream) {
+  double *lg = logits ? logits : reinterpret_cast<double *>(base + L.logits);
+  int32_t *ix = idx ? idx : reinterpret_cast<int32_t *>(base + L.idx);
+  float *wt = w ? w : reinterpret_cast<float *>(base + L.w);
+  float *h = reinterpret_cast<float *>(base + L.h);
+  float *yp = reinterpret_cast<float *>(base + L.yp);
+  K3_LAUNCH(fn, launch_router(x, router_w, 1, hidden, n_experts, lg, stream));
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (n_experts <= kFusedTopkMaxExperts &&
+      moe_experts_grid() <= (unsigned)kMaxSyncGrid &&
+      hipStreamIsCapturing(stream, &cap) == hipSuccess &&
+      cap == hipStreamCaptureStatusNone) {
+    K3_LAUNCH(fn, launch_moe_experts(x, lg, experts, n_experts, k, hidden,
+                                     inter, h, yp,
+                                     reinterpret_cast<uint64_t *>(base + L.sync),
+                                     next_layer_seq(), ix, wt, y, y_f32, stream, add));
+    return K3_OK;
+  }
+  if (n_experts <= kFusedTopkMaxExperts) {  // top-k inside the gate/up launch
+    K3_LAUNCH(fn, launch_gate_up_routed(x, lg, experts, n_experts, k, hidden,
+                                        inter, h, ix, wt, stream));
+  } else {
+    K3_LAUNCH(fn, launch_topk_f64(lg, nullptr, 1, n_experts, k, ix, wt, stream));
+    K3_LAUNCH(fn, launch_gate_up(x, experts, ix, nullptr, k, hidden, inter, h,
+                                 stream));
+  }
+  K3_LAUNCH(fn, launch_down(h, experts, ix, nullptr, k, hidden, inter, yp,
+                            stream));
+  K3_LAUNCH(fn, launch_combine(yp, wt, k, hidden, y, y_f32, stream, add));
+  return K3_OK;
+}
+
 k3_status k3_moe_layer_ex(const uint16_t *x, const uint16_t *router_w,
                           const uint8_t *const *experts, int n_experts,
                           int hidden, int inter, int k, uint16_t *y,
@@ -581,39 +624,98 @@ k3_status k3_moe_layer_ex(const uint16_t *x, const uint16_t *router_w,
   if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
   const WsLayout L = ws_layout(1, n_experts, hidden, inter, k);
   if (k3_status s = need_ws(fn, ws_bytes, L.total)) return s;
-  uint8_t *base = static_cast<uint8_t *>(ws);
-  double *lg = logits ? logits : reinterpret_cast<double *>(base + L.logits);
-  int32_t *ix = idx ? idx : reinterpret_cast<int32_t *>(base + L.idx);
-  float *wt = w ? w : reinterpret_cast<float *>(base + L.w);
-  float *h = reinterpret_cast<float *>(base + L.h);
-  float *yp = reinterpret_cast<float *>(base + L.yp);
-  K3_LAUNCH(fn, launch_router(x, router_w, 1, hidden, n_experts, lg, stream));
-  // The expert work in one launch, its stages marked by a per-call value; a
-  // graph being captured would replay one value, so it gets the separate
-  // launches (as does a selection over more than 1024 experts).
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  if (n_experts <= kFusedTopkMaxExperts &&
-      moe_experts_grid() <= (unsigned)kMaxSyncGrid &&
-      hipStreamIsCapturing(stream, &cap) == hipSuccess &&
-      cap == hipStreamCaptureStatusNone) {
-    K3_LAUNCH(fn, launch_moe_experts(x, lg, experts, n_experts, k, hidden,
-                                     inter, h, yp,
-                                     reinterpret_cast<uint64_t *>(base + L.sync),
-                                     next_layer_seq(), ix, wt, y, y_f32, stream));
-    return K3_OK;
-  }
-  if (n_experts <= kFusedTopkMaxExperts) {  // top-k inside the gate/up launch
-    K3_LAUNCH(fn, launch_gate_up_routed(x, lg, experts, n_experts, k, hidden,
-                                        inter, h, ix, wt, stream));
-  } else {
-    K3_LAUNCH(fn, launch_topk_f64(lg, nullptr, 1, n_experts, k, ix, wt, stream));
-    K3_LAUNCH(fn, launch_gate_up(x, experts, ix, nullptr, k, hidden, inter, h,
-                                 stream));
-  }
-  K3_LAUNCH(fn, launch_down(h, experts, ix, nullptr, k, hidden, inter, yp,
-                            stream));
-  K3_LAUNCH(fn, launch_combine(yp, wt, k, hidden, y, y_f32, stream));
+  return layer_launches(fn, x, router_w, experts, n_experts, hidden, inter, k, y,
+                        y_f32, idx, w, logits, static_cast<uint8_t *>(ws), L,
+                        nullptr, stream);
+}
+
+size_t k3_shared_expert_bytes(int hidden, int inter) {
+  if (check_expert_dims("k3_shared_expert_bytes", hidden, inter) != K3_OK) return 0;
+  return (size_t)3 * hidden * inter * sizeof(uint16_t);
+}
+
+k3_status k3_shared_experts(const uint16_t *x, const uint16_t *const *shared,
+                            int n_shared, int hidden, int inter, float *h,
+                            float *ys, k3_stream_t stream) {
+  const char *fn = "k3_shared_experts";
+  K3_NEED_PTR(fn, x);
+  K3_NEED_PTR(fn, shared);
+  K3_NEED_PTR(fn, h);
+  K3_NEED_PTR(fn, ys);
+  K3_NEED(fn, n_shared >= 1 && n_shared <= K3_MAX_SHARED,
+          "%s: n_shared=%d outside [1, %d]", fn, n_shared, K3_MAX_SHARED);
+  if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
+  K3_LAUNCH(fn, launch_shared_experts(x, shared, n_shared, hidden, inter, h, ys, stream));
   return K3_OK;
+}
+
+// Workspace of k3_moe_layer_shared: the layer's, then h of the shared
+// experts and their summed output.
+struct SharedWs {
+  WsLayout L;
+  size_t hs, ys, total;
+};
+static SharedWs shared_ws(int n, int hidden, int inter, int k, int n_shared,
+                          int inter_shared) {
+  SharedWs S;
+  S.L = ws_layout(1, n, hidden, inter, k);
+  size_t off = S.L.total;
+  S.hs = off;
+  off += align256((size_t)n_shared * inter_shared * sizeof(float));
+  S.ys = off;
+  off += align256((size_t)hidden * sizeof(float));
+  S.total = off;
+  return S;
+}
+
+size_t k3_moe_layer_shared_workspace_bytes(int n_experts, int hidden, int inter,
+                                           int k, int n_shared, int inter_shared) {
+  if (n_experts < 1 || k < 1 || n_shared < 0 || n_shared > K3_MAX_SHARED) return 0;
+  if (check_expert_dims("k3_moe_layer_shared_workspace_bytes", hidden, inter) != K3_OK)
+    return 0;
+  if (n_shared > 0 &&
+      check_expert_dims("k3_moe_layer_shared_workspace_bytes", hidden, inter_shared) != K3_OK)
+    return 0;
+  return shared_ws(n_experts, hidden, inter, k, n_shared, inter_shared).total;
+}
+
+k3_status k3_moe_layer_shared(const uint16_t *x, const uint16_t *router_w,
+                              const uint8_t *const *experts, int n_experts,
+                              int hidden, int inter, int k,
+                              const uint16_t *const *shared, int n_shared,
+                              int inter_shared, uint16_t *y, float *y_f32,
+                              int32_t *idx, float *w, double *logits, void *ws,
+                              size_t ws_bytes, k3_stream_t stream) {
+  const char *fn = "k3_moe_layer_shared";
+  K3_NEED_PTR(fn, x);
+  K3_NEED_PTR(fn, router_w);
+  K3_NEED_PTR(fn, experts);
+  K3_NEED_PTR(fn, y);
+  K3_NEED_PTR(fn, ws);
+  if ((y_f32 && !aligned16(y_f32)) || (idx && !aligned16(idx)) ||
+      (w && !aligned16(w)) || (logits && !aligned16(logits)))
+    return fail(K3_ERR_ARG, "%s: an optional output is not 16-byte aligned",
+                fn);
+  K3_NEED(fn, n_shared >= 0 && n_shared <= K3_MAX_SHARED,
+          "%s: n_shared=%d outside [0, %d]", fn, n_shared, K3_MAX_SHARED);
+  if (n_shared > 0) {
+    K3_NEED_PTR(fn, shared);
+    if (k3_status s = check_expert_dims(fn, hidden, inter_shared)) return s;
+  }
+  if (k3_status s = check_routing(fn, 1, n_experts, k)) return s;
+  if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
+  const SharedWs S = shared_ws(n_experts, hidden, inter, k, n_shared, inter_shared);
+  if (k3_status s = need_ws(fn, ws_bytes, S.total)) return s;
+  uint8_t *base = static_cast<uint8_t *>(ws);
+  float *ys = nullptr;
+  if (n_shared > 0) {  // independent of the routing: first
+    ys = reinterpret_cast<float *>(base + S.ys);
+    K3_LAUNCH(fn, launch_shared_experts(x, shared, n_shared, hidden, inter_shared,
+                                        reinterpret_cast<float *>(base + S.hs), ys,
+                                        stream));
+  }
+  return layer_launches(fn, x, router_w, experts, n_experts, hidden, inter, k, y,
+                        y_f32, idx, w, logits, base, S.L, ys, stream);
 }
 
 k3_status k3_moe_layer_cached(const uint16_t *x, const uint16_t *router_w,

@@ -166,7 +166,8 @@ __global__ __launch_bounds__(kThreads) void moe_experts_kernel(
     const uint8_t *const *__restrict__ experts, int n, int k, int hidden,
     int inter, float *h, float *yp, uint64_t *slots, uint64_t val,
     int32_t *__restrict__ idx_out, float *__restrict__ w_out,
-    uint16_t *__restrict__ y, float *__restrict__ y_f32) {
+    uint16_t *__restrict__ y, float *__restrict__ y_f32,
+    const float *__restrict__ add) {
   __shared__ float part[kPartFloats];
   __shared__ TopkWgLds tk;
   __shared__ int bad;
@@ -248,6 +249,7 @@ __global__ __launch_bounds__(kThreads) void moe_experts_kernel(
         for (int j = 0; j < 16; ++j)
           if (j0 + j < k) acc = fmaf(tk.wt[j0 + j], v[j], acc);
       }
+      if (add) acc += add[row];  // e.g. the shared experts' output
       if (y_f32) y_f32[row] = acc;
       if (y) y[row] = f32_to_bf16_rne(acc);
     }
@@ -260,10 +262,12 @@ __global__ __launch_bounds__(kThreads) void moe_experts_kernel(
     }
 }
 
-// y[i] = sum_j w[j] * yp[j][i] in rank order j = 0..k-1, then bf16 (RNE).
+// y[i] = sum_j w[j] * yp[j][i] in rank order j = 0..k-1 (+ add[i] when
+// given), then bf16 (RNE).
 __global__ __launch_bounds__(256) void combine_kernel(
     const float *__restrict__ yp, const float *__restrict__ w, int k,
-    int hidden, uint16_t *__restrict__ y, float *__restrict__ y_f32) {
+    int hidden, uint16_t *__restrict__ y, float *__restrict__ y_f32,
+    const float *__restrict__ add) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= hidden) return;
   float acc = 0.f;
@@ -276,6 +280,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
     for (int j = 0; j < 16; ++j)
       if (j0 + j < k) acc = fmaf(w[j0 + j], v[j], acc);
   }
+  if (add) acc += add[i];
   if (y_f32) y_f32[i] = acc;
   if (y) y[i] = f32_to_bf16_rne(acc);
 }
@@ -338,18 +343,18 @@ hipError_t launch_moe_experts(const uint16_t *x, const double *logits,
                               int hidden, int inter, float *h, float *yp,
                               uint64_t *slots, uint64_t val, int32_t *idx,
                               float *w, uint16_t *y, float *y_f32,
-                              hipStream_t s) {
+                              hipStream_t s, const float *add) {
   // one workgroup per compute unit: the whole grid fits at once
   hipLaunchKernelGGL(moe_experts_kernel, dim3(moe_experts_grid()),
                      dim3(kThreads), 0, s, x, logits, experts, n, k, hidden,
-                     inter, h, yp, slots, val, idx, w, y, y_f32);
+                     inter, h, yp, slots, val, idx, w, y, y_f32, add);
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const float *yp, const float *w, int k, int hidden,
-                          uint16_t *y, float *y_f32, hipStream_t s) {
+                          uint16_t *y, float *y_f32, hipStream_t s, const float *add) {
   hipLaunchKernelGGL(combine_kernel, dim3((hidden + 255) / 256), dim3(256), 0,
-                     s, yp, w, k, hidden, y, y_f32);
+                     s, yp, w, k, hidden, y, y_f32, add);
   return hipGetLastError();
 }
 

@@ -170,7 +170,13 @@ hipError_t launch_experts_dense(const uint16_t *x, const float *const *table,
                                 const int32_t *idx, int k, int hidden, int inter,
                                 float *h, float *yp, hipStream_t s);
 hipError_t launch_combine(const float *yp, const float *w, int k, int hidden,
-                          uint16_t *y, float *y_f32, hipStream_t s);
+                          uint16_t *y, float *y_f32, hipStream_t s,
+                          const float *add = nullptr);
+// Shared experts (k3_shared.hip): h [n_shared][inter], ys [hidden] = the sum
+// of their outputs.
+hipError_t launch_shared_experts(const uint16_t *x, const uint16_t *const *shared,
+                                 int n_shared, int hidden, int inter, float *h,
+                                 float *ys, hipStream_t s);
 // The decode layer's expert work in one launch (k3_expert.hip): top-k of
 // the logits, gate/up, down, combine. slots: 2 * kMaxSyncGrid arrival words
 // (moe_experts_grid() <= kMaxSyncGrid workgroups); val: this call's value,
@@ -182,7 +188,7 @@ hipError_t launch_moe_experts(const uint16_t *x, const double *logits,
                               int hidden, int inter, float *h, float *yp,
                               uint64_t *slots, uint64_t val, int32_t *idx,
                               float *w, uint16_t *y, float *y_f32,
-                              hipStream_t s);
+                              hipStream_t s, const float *add = nullptr);
 // Pinned host buffer of K3_MAX_TOPK ints owned by an expert cache
 // (k3_cache.hip): where k3_moe_layer_cached receives a token's selection.
 int32_t *cache_selection_buffer(k3_cache_t c);

@@ -1,0 +1,118 @@
+// Shared experts: SwiGLU FFNs with bf16 weights that run on every token
+// beside the routed ones and stay resident ([ZOR] "How does a
+// 2.78-trillion-parameter model fit in 8 GB?": two per layer, classed with
+// the always-on bf16 set). Their output is added to the routed mix.
+//
+// Blob of one shared expert: gate [inter][hidden], up [inter][hidden], down
+// [hidden][inter], bf16 row-major, back to back. The work is a plain
+// HBM-bound GEMV: one wave per output row, 16-byte loads (8 weights) per
+// lane, products on the dot2 bf16 path, lanes summed in a fixed order, so
+// reruns are bit-identical.
+#include "k3_decode.h"
+#include "k3_internal.h"
+
+namespace k3 {
+
+namespace {
+
+constexpr int kSharedWaves = 4;
+
+__device__ __forceinline__ float lanes_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// 8 bf16 weights (one 16-byte load) times 8 bf16 activations, added to acc
+// as four dot2 steps in order.
+__device__ __forceinline__ float dot8_bf16(const uint4 w, const uint4 a, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.x),
+                                        __builtin_bit_cast(bf16x2, a.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.y),
+                                        __builtin_bit_cast(bf16x2, a.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.z),
+                                        __builtin_bit_cast(bf16x2, a.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w),
+                                        __builtin_bit_cast(bf16x2, a.w), acc, false);
+  return acc;
+}
+
+typedef uint32_t u32v4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld16_nt(const uint16_t *p) {
+  const u32v4 v = __builtin_nontemporal_load(reinterpret_cast<const u32v4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// One wave per (shared expert s, h row i): lane l takes columns 8l + 512m
+// (m ascending) of the gate and up rows; h[s][i] = SiLU(g) * u.
+__global__ __launch_bounds__(64 * kSharedWaves) void shared_gate_up_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *const *__restrict__ shared,
+    int n_shared, int hidden, int inter, float *__restrict__ h) {
+  const int gw = blockIdx.x * kSharedWaves + (threadIdx.x >> 6);
+  if (gw >= n_shared * inter) return;
+  const int lane = threadIdx.x & 63, s = gw / inter, i = gw % inter;
+  const uint16_t *blob = shared[s];
+  const uint16_t *gr = blob + (size_t)i * hidden;
+  const uint16_t *ur = blob + (size_t)(inter + i) * hidden;
+  const uint4 *xv = reinterpret_cast<const uint4 *>(x);
+  float ag = 0.f, au = 0.f;
+#pragma unroll 4
+  for (int c8 = lane; 8 * c8 < hidden; c8 += 64) {
+    const uint4 g = ld16_nt(gr + 8 * c8), u = ld16_nt(ur + 8 * c8), a = xv[c8];
+    ag = dot8_bf16(g, a, ag);
+    au = dot8_bf16(u, a, au);
+  }
+  ag = lanes_sum(ag);
+  au = lanes_sum(au);
+  if (lane == 0) h[(size_t)s * inter + i] = silu(ag) * au;
+}
+
+// One wave per output row r: ys[r] = sum over s of W_down(s)[r] . h[s];
+// lane l takes columns 8l + 512m of every shared expert in turn (s
+// ascending, then m ascending), then the lanes are summed.
+__global__ __launch_bounds__(64 * kSharedWaves) void shared_down_kernel(
+    const float *__restrict__ h, const uint16_t *const *__restrict__ shared,
+    int n_shared, int hidden, int inter, float *__restrict__ ys) {
+  const int r = blockIdx.x * kSharedWaves + (threadIdx.x >> 6);
+  if (r >= hidden) return;
+  const int lane = threadIdx.x & 63;
+  float acc = 0.f;
+  for (int s = 0; s < n_shared; ++s) {
+    const uint16_t *dr = shared[s] + (size_t)2 * inter * hidden + (size_t)r * inter;
+    const float4 *hv = reinterpret_cast<const float4 *>(h + (size_t)s * inter);
+#pragma unroll 2
+    for (int c8 = lane; 8 * c8 < inter; c8 += 64) {
+      const uint4 w = ld16_nt(dr + 8 * c8);
+      const float4 h0 = hv[2 * c8], h1 = hv[2 * c8 + 1];
+      acc = fmaf(__uint_as_float(w.x << 16), h0.x, acc);
+      acc = fmaf(__uint_as_float(w.x & 0xFFFF0000u), h0.y, acc);
+      acc = fmaf(__uint_as_float(w.y << 16), h0.z, acc);
+      acc = fmaf(__uint_as_float(w.y & 0xFFFF0000u), h0.w, acc);
+      acc = fmaf(__uint_as_float(w.z << 16), h1.x, acc);
+      acc = fmaf(__uint_as_float(w.z & 0xFFFF0000u), h1.y, acc);
+      acc = fmaf(__uint_as_float(w.w << 16), h1.z, acc);
+      acc = fmaf(__uint_as_float(w.w & 0xFFFF0000u), h1.w, acc);
+    }
+  }
+  acc = lanes_sum(acc);
+  if (lane == 0) ys[r] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_shared_experts(const uint16_t *x, const uint16_t *const *shared,
+                                 int n_shared, int hidden, int inter, float *h,
+                                 float *ys, hipStream_t s) {
+  const unsigned b1 = (unsigned)(((size_t)n_shared * inter + kSharedWaves - 1) / kSharedWaves);
+  hipLaunchKernelGGL(shared_gate_up_kernel, dim3(b1), dim3(64 * kSharedWaves), 0, s, x, shared,
+                     n_shared, hidden, inter, h);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned b2 = (unsigned)((hidden + kSharedWaves - 1) / kSharedWaves);
+  hipLaunchKernelGGL(shared_down_kernel, dim3(b2), dim3(64 * kSharedWaves), 0, s, h, shared,
+                     n_shared, hidden, inter, ys);
+  return hipGetLastError();
+}
+
+}  // namespace k3

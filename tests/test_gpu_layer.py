@@ -230,6 +230,34 @@ def test_cached_layer_c3_full_size(c3_pool):
         del host
 
 
+def test_layer_with_shared_experts_c3_full_size(c3_pool):
+    """The C3 layer with two 7168/1536 bf16 shared experts (132 MB): indices
+    bit-exact, y within 1e-5 of the oracle's layer with shared experts."""
+    import torch
+    pool, R, R_d = c3_pool
+    n, hidden, inter, k = W.N_EXPERTS, W.HIDDEN, W.INTER, W.TOPK
+    say("layer with 2 shared experts, C3")
+    shared = W.shared_experts_bf16(0, W.C3)
+    blobs = [up(np.concatenate([S["gate"].ravel(), S["up"].ravel(), S["down"].ravel()]))
+             for S in shared]
+    table = up(np.array([b.data_ptr() for b in blobs], np.uint64))
+    ws = empty(K.k3_moe_layer_shared_workspace_bytes(n, hidden, inter, k, 2, inter),
+               torch.uint8)
+    x = W.tokens_bf16(0, W.C3, 1, hidden, batch=11)[0]
+    y = empty(hidden, torch.int16)
+    y32 = empty(hidden, torch.float32)
+    idx = empty(k, torch.int32)
+    K.k3_moe_layer_shared(up(x), R_d, pool.table, n, hidden, inter, k, table, 2, inter, y, ws,
+                          y_f32=y32, idx=idx)
+    lg = oracle.router_logits(x, R)
+    idx_ref, _ = oracle.topk(lg, k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    experts = {int(e): W.expert_weights(0, W.C3, int(e)) for e in idx_ref}
+    oracle.set_threads(16)
+    y_ref, _, _ = oracle.moe_layer_shared(x, R, experts, k, hidden, inter, shared)
+    assert normwise(y32.cpu().numpy(), y_ref) <= TOL
+
+
 def test_layer_in_a_captured_graph():
     """Captured into a HIP graph, the layer takes the separate launches (its
     single expert launch marks stages with a per-call value a replay would
