@@ -572,13 +572,15 @@ static k3_status layer_launches(const char *fn, const uint16_t *x,
                                 int hidden, int inter, int k, uint16_t *y,
                                 float *y_f32, int32_t *idx, float *w,
                                 double *logits, uint8_t *base, const WsLayout &L,
-                                const float *add, hipStream_t stream) {
+                                const float *add, hipStream_t stream,
+                                bool routed_already = false) {
   double *lg = logits ? logits : reinterpret_cast<double *>(base + L.logits);
   int32_t *ix = idx ? idx : reinterpret_cast<int32_t *>(base + L.idx);
   float *wt = w ? w : reinterpret_cast<float *>(base + L.w);
   float *h = reinterpret_cast<float *>(base + L.h);
   float *yp = reinterpret_cast<float *>(base + L.yp);
-  K3_LAUNCH(fn, launch_router(x, router_w, 1, hidden, n_experts, lg, stream));
+  if (!routed_already)
+    K3_LAUNCH(fn, launch_router(x, router_w, 1, hidden, n_experts, lg, stream));
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
   if (n_experts <= kFusedTopkMaxExperts &&
       moe_experts_grid() <= (unsigned)kMaxSyncGrid &&
@@ -707,15 +709,19 @@ k3_status k3_moe_layer_shared(const uint16_t *x, const uint16_t *router_w,
   const SharedWs S = shared_ws(n_experts, hidden, inter, k, n_shared, inter_shared);
   if (k3_status s = need_ws(fn, ws_bytes, S.total)) return s;
   uint8_t *base = static_cast<uint8_t *>(ws);
-  float *ys = nullptr;
-  if (n_shared > 0) {  // independent of the routing: first
-    ys = reinterpret_cast<float *>(base + S.ys);
-    K3_LAUNCH(fn, launch_shared_experts(x, shared, n_shared, hidden, inter_shared,
-                                        reinterpret_cast<float *>(base + S.hs), ys,
-                                        stream));
-  }
-  return layer_launches(fn, x, router_w, experts, n_experts, hidden, inter, k, y,
-                        y_f32, idx, w, logits, base, S.L, ys, stream);
+  if (n_shared == 0)
+    return layer_launches(fn, x, router_w, experts, n_experts, hidden, inter, k, y,
+                          y_f32, idx, w, logits, base, S.L, nullptr, stream);
+  // The router rows and the shared experts' gate/up rows in one launch, the
+  // shared down stage, then the expert launch, whose combine adds ys.
+  float *ys = reinterpret_cast<float *>(base + S.ys);
+  float *hs = reinterpret_cast<float *>(base + S.hs);
+  double *lg = logits ? logits : reinterpret_cast<double *>(base + S.L.logits);
+  K3_LAUNCH(fn, launch_router_shared(x, router_w, hidden, n_experts, lg, shared, n_shared,
+                                     inter_shared, hs, stream));
+  K3_LAUNCH(fn, launch_shared_down(hs, shared, n_shared, hidden, inter_shared, ys, stream));
+  return layer_launches(fn, x, router_w, experts, n_experts, hidden, inter, k, y, y_f32,
+                        idx, w, lg, base, S.L, ys, stream, true);
 }
 
 k3_status k3_moe_layer_cached(const uint16_t *x, const uint16_t *router_w,

@@ -177,6 +177,14 @@ hipError_t launch_combine(const float *yp, const float *w, int k, int hidden,
 hipError_t launch_shared_experts(const uint16_t *x, const uint16_t *const *shared,
                                  int n_shared, int hidden, int inter, float *h,
                                  float *ys, hipStream_t s);
+// One token's router logits and the shared experts' h in one launch, then
+// their down stage (the two halves of launch_router + launch_shared_experts).
+hipError_t launch_router_shared(const uint16_t *x, const uint16_t *R, int hidden,
+                                int n_experts, double *logits,
+                                const uint16_t *const *shared, int n_shared, int inter,
+                                float *h, hipStream_t s);
+hipError_t launch_shared_down(const float *h, const uint16_t *const *shared, int n_shared,
+                              int hidden, int inter, float *ys, hipStream_t s);
 // The decode layer's expert work in one launch (k3_expert.hip): top-k of
 // the logits, gate/up, down, combine. slots: 2 * kMaxSyncGrid arrival words
 // (moe_experts_grid() <= kMaxSyncGrid workgroups); val: this call's value,

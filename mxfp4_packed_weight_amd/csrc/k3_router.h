@@ -96,4 +96,19 @@ __device__ __forceinline__ double router_row_part(const uint16_t *__restrict__ R
   return wave_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
 }
 
+// Logit of router row e for token x: the kRouterSplit waves of the
+// calling workgroup each take their part and wave 0's lane 0 stores
+// (p0 + p1) + (p2 + p3). `partial` is the workgroup's LDS scratch.
+__device__ __forceinline__ void router_row_logit(const uint16_t *__restrict__ Rrow,
+                                                 const uint16_t *__restrict__ x,
+                                                 int hidden, double *partial,
+                                                 double *out) {
+  const int w = wave_id();
+  const double p = router_row_part<false>(Rrow, x, nullptr, hidden, w);
+  if ((threadIdx.x & 63) == 0) partial[w] = p;
+  __syncthreads();
+  if (threadIdx.x == 0) *out = (partial[0] + partial[1]) + (partial[2] + partial[3]);
+  __syncthreads();
+}
+
 }  // namespace k3

@@ -27,16 +27,10 @@ __global__ __launch_bounds__(kRouterSplit * 64) void router_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ R, int hidden,
     int n, int T, double *__restrict__ logits) {
   __shared__ double partial[kRouterSplit];
-  const int e = blockIdx.x, w = wave_id();
-  for (int t = blockIdx.y; t < T; t += gridDim.y) {
-    const double p = router_row_part<false>(R + (size_t)e * hidden,
-                                            x + (size_t)t * hidden, nullptr, hidden, w);
-    if ((threadIdx.x & 63) == 0) partial[w] = p;
-    __syncthreads();
-    if (threadIdx.x == 0)
-      logits[(size_t)t * n + e] = (partial[0] + partial[1]) + (partial[2] + partial[3]);
-    __syncthreads();
-  }
+  const int e = blockIdx.x;
+  for (int t = blockIdx.y; t < T; t += gridDim.y)
+    router_row_logit(R + (size_t)e * hidden, x + (size_t)t * hidden, hidden, partial,
+                     logits + (size_t)t * n + e);
 }
 
 

@@ -10,6 +10,7 @@
 // reruns are bit-identical.
 #include "k3_decode.h"
 #include "k3_internal.h"
+#include "k3_router.h"
 
 namespace k3 {
 
@@ -44,13 +45,13 @@ __device__ __forceinline__ uint4 ld16_nt(const uint16_t *p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// One wave per (shared expert s, h row i): lane l takes columns 8l + 512m
-// (m ascending) of the gate and up rows; h[s][i] = SiLU(g) * u.
-__global__ __launch_bounds__(64 * kSharedWaves) void shared_gate_up_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *const *__restrict__ shared,
-    int n_shared, int hidden, int inter, float *__restrict__ h) {
-  const int gw = blockIdx.x * kSharedWaves + (threadIdx.x >> 6);
-  if (gw >= n_shared * inter) return;
+// Row gw = (shared expert s, h row i) of the gate/up stage, by one wave:
+// lane l takes columns 8l + 512m (m ascending) of the gate and up rows,
+// h[s][i] = SiLU(g) * u.
+__device__ __forceinline__ void shared_gate_up_row(const uint16_t *__restrict__ x,
+                                                   const uint16_t *const *__restrict__ shared,
+                                                   int hidden, int inter, int gw,
+                                                   float *__restrict__ h) {
   const int lane = threadIdx.x & 63, s = gw / inter, i = gw % inter;
   const uint16_t *blob = shared[s];
   const uint16_t *gr = blob + (size_t)i * hidden;
@@ -66,6 +67,34 @@ __global__ __launch_bounds__(64 * kSharedWaves) void shared_gate_up_kernel(
   ag = lanes_sum(ag);
   au = lanes_sum(au);
   if (lane == 0) h[(size_t)s * inter + i] = silu(ag) * au;
+}
+
+__global__ __launch_bounds__(64 * kSharedWaves) void shared_gate_up_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *const *__restrict__ shared,
+    int n_shared, int hidden, int inter, float *__restrict__ h) {
+  const int gw = blockIdx.x * kSharedWaves + (threadIdx.x >> 6);
+  if (gw < n_shared * inter) shared_gate_up_row(x, shared, hidden, inter, gw, h);
+}
+
+// The decode layer's router and the shared experts' gate/up stage in one
+// launch (both are row dot products against the same token): blocks
+// [0, n) are router rows (as router_kernel, the same bits), the rest take
+// kSharedWaves shared rows each (as shared_gate_up_kernel). The router rows
+// are dispatched first; their short latency-bound work then hides under the
+// shared rows' stream instead of paying a launch of its own.
+static_assert(kSharedWaves == kRouterSplit, "one block shape serves both row kinds");
+__global__ __launch_bounds__(64 * kSharedWaves) void router_shared_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ R, int n_experts,
+    double *__restrict__ logits, const uint16_t *const *__restrict__ shared,
+    int n_shared, int hidden, int inter, float *__restrict__ h) {
+  __shared__ double partial[kRouterSplit];
+  if ((int)blockIdx.x < n_experts) {
+    router_row_logit(R + (size_t)blockIdx.x * hidden, x, hidden, partial,
+                     logits + blockIdx.x);
+    return;
+  }
+  const int gw = ((int)blockIdx.x - n_experts) * kSharedWaves + (threadIdx.x >> 6);
+  if (gw < n_shared * inter) shared_gate_up_row(x, shared, hidden, inter, gw, h);
 }
 
 // One wave per output row r: ys[r] = sum over s of W_down(s)[r] . h[s];
@@ -100,6 +129,25 @@ __global__ __launch_bounds__(64 * kSharedWaves) void shared_down_kernel(
 }
 
 }  // namespace
+
+hipError_t launch_router_shared(const uint16_t *x, const uint16_t *R, int hidden,
+                                int n_experts, double *logits,
+                                const uint16_t *const *shared, int n_shared, int inter,
+                                float *h, hipStream_t s) {
+  const unsigned blocks = (unsigned)(n_experts + ((size_t)n_shared * inter + kSharedWaves - 1) /
+                                                     kSharedWaves);
+  hipLaunchKernelGGL(router_shared_kernel, dim3(blocks), dim3(64 * kSharedWaves), 0, s, x, R,
+                     n_experts, logits, shared, n_shared, hidden, inter, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_shared_down(const float *h, const uint16_t *const *shared, int n_shared,
+                              int hidden, int inter, float *ys, hipStream_t s) {
+  const unsigned b2 = (unsigned)((hidden + kSharedWaves - 1) / kSharedWaves);
+  hipLaunchKernelGGL(shared_down_kernel, dim3(b2), dim3(64 * kSharedWaves), 0, s, h, shared,
+                     n_shared, hidden, inter, ys);
+  return hipGetLastError();
+}
 
 hipError_t launch_shared_experts(const uint16_t *x, const uint16_t *const *shared,
                                  int n_shared, int hidden, int inter, float *h,
