@@ -425,6 +425,10 @@ k3_status k3_experts_dense(const uint16_t *x, const float *const *dense_experts,
  * k3_cache_replay     runs the same policy on a recorded trace on the host
  *                     alone (requests of request_size ids, every copy taken
  *                     as finished), e.g. to choose a slot count.
+ * k3_cache_replay_opt the same replay with the optimal offline victim
+ *                     (Belady: the evictable slot whose expert is next used
+ *                     farthest ahead; never again is farthest; ties to the
+ *                     lowest slot): the bound for an online policy.
  * k3_moe_layer_cached the decode layer for one token through a cache:
  *                     router and top-k on the device, the selection copied
  *                     to the host (this call waits for it), the fetch, then
@@ -451,6 +455,9 @@ k3_status k3_cache_trace(k3_cache_t cache, int32_t *buf, size_t cap, size_t *len
 k3_status k3_cache_replay(const int32_t *trace, size_t len, int n_experts,
                           int n_slots, const int32_t *pinned, int n_pinned,
                           int request_size, k3_cache_stats *out);
+k3_status k3_cache_replay_opt(const int32_t *trace, size_t len, int n_experts,
+                              int n_slots, const int32_t *pinned, int n_pinned,
+                              int request_size, k3_cache_stats *out);
 k3_status k3_moe_layer_cached(const uint16_t *x, const uint16_t *router_w,
                               k3_cache_t cache, int n_experts, int hidden,
                               int inter, int k, uint16_t *y, float *y_f32,

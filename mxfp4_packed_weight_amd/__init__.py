@@ -89,6 +89,7 @@ SIGNATURES = [
     ("k3_cache_histogram", _i, [_vp, _vp]),
     ("k3_cache_trace", _i, [_vp, _vp, _sz, ctypes.POINTER(_sz)]),
     ("k3_cache_replay", _i, [_vp, _sz, _i, _i, _vp, _i, _i, _stats_p]),
+    ("k3_cache_replay_opt", _i, [_vp, _sz, _i, _i, _vp, _i, _i, _stats_p]),
     ("k3_moe_layer_cached", _i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
                                  _vp, _sz, _vp]),
 ]
@@ -422,6 +423,15 @@ def k3_cache_replay(trace, n_experts, n_slots, pinned=(), request_size=1):
     pn, pp = _ids(pinned)
     st = k3_cache_stats()
     _call("k3_cache_replay", tp, t.size, n_experts, n_slots, pp if pn.size else None,
+          pn.size, request_size, ctypes.byref(st))
+    return st.as_dict()
+
+
+def k3_cache_replay_opt(trace, n_experts, n_slots, pinned=(), request_size=1):
+    t, tp = _ids(trace)
+    pn, pp = _ids(pinned)
+    st = k3_cache_stats()
+    _call("k3_cache_replay_opt", tp, t.size, n_experts, n_slots, pp if pn.size else None,
           pn.size, request_size, ctypes.byref(st))
     return st.as_dict()
 

@@ -12,6 +12,11 @@
 //   - a miss takes an empty slot, else evicts the least recently used slot
 //     that is neither pinned nor named by the same request;
 //   - every request updates a per-expert histogram and an ordered trace.
+// k3_cache_replay_opt runs the same request rules with the optimal offline
+// victim (the expert next used farthest ahead, Belady's rule), the bound an
+// online policy can be compared against when sizing the cache from a trace
+// ([A176] "The interesting design decisions": LRU against Belady over the
+// same range of cache sizes).
 // Device side (ExpertCache): the slots are one allocation; a miss is an
 // asynchronous host-to-device copy on the caller's stream followed by an
 // event, and the entries of the device table of expert pointers (what the
@@ -395,6 +400,97 @@ k3_status k3_cache_replay(const int32_t *trace, size_t len, int n_experts,
               K3_ERR_MEMORY);
   }
   *out = p.st;
+  return K3_OK;
+}
+
+k3_status k3_cache_replay_opt(const int32_t *trace, size_t len, int n_experts,
+                              int n_slots, const int32_t *pinned, int n_pinned,
+                              int request_size, k3_cache_stats *out) {
+  const char *fn = "k3_cache_replay_opt";
+  if (!trace || !out || (n_pinned > 0 && !pinned))
+    return (set_error("%s: NULL argument", fn), K3_ERR_ARG);
+  if (n_experts < 1 || n_slots < 1 || n_slots > n_experts || request_size < 1)
+    return (set_error("%s: need 1 <= n_slots <= n_experts and request_size >= 1", fn),
+            K3_ERR_CONFIG);
+  for (size_t i = 0; i < len; ++i)
+    if (trace[i] < 0 || trace[i] >= n_experts)
+      return (set_error("%s: trace entry %zu = %d outside [0, %d)", fn, i, trace[i], n_experts),
+              K3_ERR_ARG);
+  std::vector<char> pin(n_experts, 0);
+  for (int i = 0; i < n_pinned; ++i) {
+    if (pinned[i] < 0 || pinned[i] >= n_experts)
+      return (set_error("%s: pinned expert %d outside [0, %d)", fn, pinned[i], n_experts),
+              K3_ERR_ARG);
+    pin[pinned[i]] = 1;
+  }
+  // next_pos[i]: the next position of trace[i] after i (len when none)
+  std::vector<size_t> next_pos(len), last(n_experts, len);
+  for (size_t i = len; i-- > 0;) {
+    next_pos[i] = last[trace[i]];
+    last[trace[i]] = i;
+  }
+  // next use of each expert from the current position on
+  std::vector<size_t> next_use(last);
+  std::vector<int> holder(n_slots, -1), slot_of(n_experts, -1);
+  k3_cache_stats st{};
+  for (size_t r0 = 0; r0 < len; r0 += request_size) {
+    const size_t r1 = std::min(len, r0 + (size_t)request_size);
+    // whole request: every named expert must be resident at once
+    std::vector<char> named(n_slots, 0), fresh(n_slots, 0);
+    int need = 0;
+    for (size_t i = r0; i < r1; ++i) {
+      const int e = trace[i];
+      if (slot_of[e] >= 0) named[slot_of[e]] = 1;
+    }
+    {
+      std::vector<int> seen;
+      for (size_t i = r0; i < r1; ++i)
+        if (slot_of[trace[i]] < 0 &&
+            std::find(seen.begin(), seen.end(), trace[i]) == seen.end()) {
+          seen.push_back(trace[i]);
+          ++need;
+        }
+    }
+    int free_slots = 0;
+    for (int j = 0; j < n_slots; ++j)
+      if (!named[j] && (holder[j] < 0 || !pin[holder[j]])) ++free_slots;
+    if (need > free_slots)
+      return (set_error("%s: request at %zu does not fit %d slots", fn, r0, n_slots),
+              K3_ERR_MEMORY);
+    for (size_t i = r0; i < r1; ++i) {
+      const int e = trace[i];
+      ++st.requests;
+      next_use[e] = next_pos[i];
+      int s = slot_of[e];
+      if (s >= 0) {
+        if (fresh[s]) ++st.inflight_reuses;
+        else ++st.hits;
+        continue;
+      }
+      // an empty slot, else the evictable slot whose expert is next used
+      // farthest ahead (never again counts as farthest); ties: lowest slot
+      for (int j = 0; j < n_slots && s < 0; ++j)
+        if (holder[j] < 0) s = j;
+      if (s < 0) {
+        size_t best = 0;
+        for (int j = 0; j < n_slots; ++j) {
+          if (named[j] || pin[holder[j]]) continue;
+          const size_t nu = next_use[holder[j]];
+          if (s < 0 || nu > best) {
+            best = nu;
+            s = j;
+          }
+        }
+        slot_of[holder[s]] = -1;
+        ++st.evictions;
+      }
+      holder[s] = e;
+      slot_of[e] = s;
+      named[s] = fresh[s] = 1;
+      ++st.misses;
+    }
+  }
+  *out = st;
   return K3_OK;
 }
 
