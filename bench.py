@@ -63,9 +63,23 @@ def cpu_baseline(budget_s=15.0, max_tokens=600):
         spent += time.perf_counter() - t0
         tokens += 1
     per_token = spent / tokens
+    # the same oracle on one thread (bit-identical results), a short sample
+    oracle.set_threads(1)
+    spent1, tokens1 = 0.0, 0
+    while spent1 < budget_s / 3 and tokens1 < 40:
+        x = W.tokens_bf16(0, W.C3, 1, batch=20_000 + tokens1)[0]
+        t0 = time.perf_counter()
+        oracle.moe_layer(x, R, experts, W.TOPK, W.HIDDEN, W.INTER)
+        spent1 += time.perf_counter() - t0
+        tokens1 += 1
+    oracle.set_threads(threads)
     return {"value": round(BYTES_PER_EXPERT * W.TOPK / per_token / 1e9, 4), "unit": "GB/s",
             "cores": threads, "kind": "oracle",
             "tokens_per_s": round(1.0 / per_token, 4),
+            "single_thread": {"tokens_per_s": round(tokens1 / spent1, 4), "cores": 1,
+                              "value": round(BYTES_PER_EXPERT * W.TOPK * tokens1 / spent1 / 1e9,
+                                             4),
+                              "sample": f"{tokens1} fresh tokens, {spent1:.1f} s"},
             "sample": f"{tokens} fresh decode tokens through the full oracle layer (router "
                       f"896x7168 + top-16 + 16 SwiGLU experts 7168/1536 + combine, fp64, "
                       f"{threads} OpenMP threads), {spent:.1f} s; selected expert ids read "
@@ -80,9 +94,10 @@ def main():
     ap.add_argument("--tokens", type=int, default=512, help="distinct tokens in the bank")
     ap.add_argument("--router-copies", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=("c3", "c4", "c5", "c3-cached", "c3-dequant",
-                                           "c3-shared"), default="c3",
-                    help="c3: single-token decode layer (the headline line); c4: batched "
+    ap.add_argument("--workload", choices=("c3", "c1", "c2", "c4", "c5", "c3-cached",
+                                           "c3-dequant", "c3-shared"), default="c3",
+                    help="c3: single-token decode layer (the headline line); c1: one MXFP4 "
+                         "GEMV 256x1024; c2: one 7168/1536 expert; c4: batched "
                          "decode, 64 tokens with Zipf(1.1) logits; c5: prefill, 2048 tokens "
                          "with uniform logits on the FP4 matrix unit; c3-cached: the c3 "
                          "layer with experts streamed from pinned host memory through an "
@@ -113,6 +128,8 @@ def main():
     from gen import device as D
     from gen import workloads as W
 
+    if args.workload in ("c1", "c2"):
+        return bench_c1_c2(args)
     if args.workload == "c4":
         return bench_c4(args)
     if args.workload == "c5":
@@ -184,6 +201,13 @@ def main():
     log(f"expert launch (top-k, gate/up, down, combine): {ex_us:.2f} us/launch, "
         f"{achieved:.1f} GB/s")
 
+    # per-step spread: the same layer steps, one pair of events each
+    spread = step_spread(step, args.warmup + args.steps, min(args.steps, 200), stream)
+    # calibration: one streaming read over the whole 15.7 GB pool
+    cal = calibrated_read(pool.blob, stream)
+    log(f"calibrated read {cal:.1f} GB/s; layer steps p10/p50/p90 "
+        f"{spread['p10']:.2f}/{spread['p50']:.2f}/{spread['p90']:.2f} us")
+
     traffic = None
     tpath = os.path.join(ROOT, "profiles", TRAFFIC_JSON)
     if os.path.exists(tpath):
@@ -213,18 +237,155 @@ def main():
                    "router_bytes_per_step": ROUTER_BYTES},
         "tokens_per_s": round(1e3 / ms_per_step, 1),
         "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "calibrated_read_GBs": round(cal, 1),
+        "pct_of_calibrated_read": round(100 * value / cal, 2),
+        "step_us": spread,
         "all_bytes_GBs": round((expert_bytes + ROUTER_BYTES) / (ms_per_step * 1e-3) / 1e9, 2),
         "roofline": {"kernel": "moe_experts_kernel (top-k, gate/up, down, combine; "
                                "k3_moe_layer_from_logits with T = 1)",
                      "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "launch_us": round(ex_us, 3), "algorithmic_bytes_per_launch": ex_bytes},
+                     "launch_us": round(ex_us, 3), "algorithmic_bytes_per_launch": ex_bytes,
+                     "frac_of_calibrated_read": round(achieved / cal, 4)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (bounded sample)")
         out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out))
+
+
+def step_spread(step, first, n, stream):
+    """p10 / p50 / p90 of n single steps (microseconds), each between its own
+    pair of events on `stream`."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        step(first + i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = np.sort([a.elapsed_time(b) * 1e3 for a, b in evs])
+    return {"p10": round(float(np.percentile(t, 10)), 3), "p50": round(float(np.median(t)), 3),
+            "p90": round(float(np.percentile(t, 90)), 3), "n": n}
+
+
+def calibrated_read(buf, stream, reps=3):
+    """HBM read rate (GB/s) of the library's calibration kernel streaming
+    `buf` (a uint8 device tensor of at least 4 GB) once per call."""
+    import torch
+
+    import mxfp4_packed_weight_amd as K
+    sink = torch.zeros(4, dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() // 16 * 16
+    K.k3_hbm_read_probe(buf, nbytes, sink, stream)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        K.k3_hbm_read_probe(buf, nbytes, sink, stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+
+
+def bench_c1_c2(args):
+    """C1: one MXFP4 GEMV of a 256x1024 matrix (fp32 x). C2: one routed
+    SwiGLU expert (hidden 7168, inter 1536, bf16 x). Each is timed (i) as a
+    single call on one resident operand, back to back, and (ii) rotating
+    over distinct HBM copies, 4096 matrices (570 MB) for C1 and 64 experts
+    (1.12 GB) for C2, so no call is served from the 256 MB last-level cache.
+    `value` is (ii)'s rate of packed bytes."""
+    import torch
+
+    import mxfp4_packed_weight_amd as K
+    import oracle
+    from gen import device as D
+    from gen import workloads as W
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, steps):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(steps):
+            fn(args.warmup + i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3 / steps
+
+    threads = min(16, os.cpu_count() or 1)
+    oracle.set_threads(threads)
+    if args.workload == "c1":
+        rows, cols, ncopy, nbase = 256, 1024, 4096, 64
+        mb = K.k3_mxfp4_packed_bytes(rows, cols)
+        base = torch.empty((nbase, mb), dtype=torch.uint8, device=dev)
+        mats = []
+        for i in range(nbase):
+            nib, sc = W.mxfp4_matrix(0, W.C1, rows, cols, W.ELO, W.EHI, a=i)
+            mats.append((nib, sc))
+            K.k3_mxfp4_pack(D.to_device(nib, dev), D.to_device(sc, dev), rows, cols, base[i],
+                            stream)
+        pool = base.repeat(ncopy // nbase, 1)  # 4096 distinct addresses
+        x = D.to_device(W.c1_inputs(0)[2], dev)
+        y = torch.empty(rows, dtype=torch.float32, device=dev)
+        single = timed(lambda i: K.k3_mxfp4_gemv(x, pool[0], rows, cols, y, stream), args.steps)
+        rot = timed(lambda i: K.k3_mxfp4_gemv(x, pool[i % ncopy], rows, cols, y, stream),
+                    max(args.steps, ncopy))
+        nbytes, name = mb, "one MXFP4 GEMV, W 256x1024 (139,264 B packed), x fp32"
+        xh = W.c1_inputs(0)[2].astype(np.float64)
+        t0, n = time.perf_counter(), 0
+        while n < 1000 and time.perf_counter() - t0 < 10:
+            oracle.gemv(*mats[n % nbase], xh)
+            n += 1
+        cpu_s = (time.perf_counter() - t0) / n
+        cpu_sample = f"{n} oracle GEMVs (fp64, {threads} threads)"
+    else:
+        hidden, inter, ne = W.HIDDEN, W.INTER, 64
+        pool = D.build_expert_pool(0, W.C2, ne, device=dev, log=log)
+        x = D.to_device(W.tokens_bf16(0, W.C2, 1)[0].view(np.int16), dev)
+        y = torch.empty(hidden, dtype=torch.float32, device=dev)
+        h = torch.empty(inter, dtype=torch.float32, device=dev)
+        single = timed(lambda i: K.k3_expert_swiglu(x, pool.expert_view(0), hidden, inter, y, h,
+                                                    stream), args.steps)
+        rot = timed(lambda i: K.k3_expert_swiglu(x, pool.expert_view(i % ne), hidden, inter, y, h,
+                                                 stream), args.steps)
+        nbytes, name = BYTES_PER_EXPERT, "one routed SwiGLU expert, hidden 7168, inter 1536, x bf16"
+        E = W.expert_weights(0, W.C2, 0)
+        xf = oracle.bf16_to_f64(W.tokens_bf16(0, W.C2, 1)[0])
+        t0, n = time.perf_counter(), 0
+        while n < 10 and time.perf_counter() - t0 < 15:
+            oracle.expert_swiglu(E, xf)
+            n += 1
+        cpu_s = (time.perf_counter() - t0) / n
+        cpu_sample = f"{n} oracle experts (fp64, {threads} threads)"
+    value = nbytes / rot / 1e3
+    log(f"{args.workload.upper()}: single call {single:.2f} us, rotating {rot:.2f} us "
+        f"({value:.1f} GB/s)")
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(rot / 1e3, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": name, "bytes_per_call": nbytes,
+                   "rotation": "4096 copies (570 MB)" if args.workload == "c1"
+                   else "64 experts (1.12 GB)"},
+        "single_call_us": round(single, 3), "rotating_call_us": round(rot, 3),
+        "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "roofline": {"kernel": "gemv_f32_kernel" if args.workload == "c1"
+                     else "gate_up_kernel + down_kernel (k3_expert_swiglu)",
+                     "bound": "hbm", "achieved": round(value, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(value / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": nbytes},
+        "cpu_baseline": {"value": round(nbytes / cpu_s / 1e9, 4), "unit": "GB/s",
+                         "cores": threads, "kind": "oracle", "sample": cpu_sample},
+    }
     print(json.dumps(out))
 
 

@@ -354,6 +354,15 @@ k3_status k3_moe_layer_shared(const uint16_t *x, const uint16_t *router_w,
                               int32_t *idx, float *w, double *logits, void *ws,
                               size_t ws_bytes, k3_stream_t stream);
 
+/* Calibration read for measurements: streams `bytes` (a positive multiple
+ * of 16; buf 16-byte aligned, device) once with 16-byte non-temporal loads,
+ * one 512-thread workgroup per compute unit. The HBM read rate it reaches is
+ * the yardstick the kernels' rates are also reported against. sink: device
+ * uint32 [1], written only in the unlikely case the data folds to a fixed
+ * value (it keeps the loads from being dropped). */
+k3_status k3_hbm_read_probe(const void *buf, size_t bytes, uint32_t *sink,
+                            k3_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * Dequantise-then-multiply control: the byte gap the pages price ([SAT]
  * "Reduction one": an expert is 17.55 MB packed and 132 MB as floats; the

@@ -71,6 +71,7 @@ SIGNATURES = [
     ("k3_moe_prefill_workspace_bytes", _sz, [_i, _i, _i, _i, _i]),
     ("k3_moe_prefill", _i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
                             _vp, _vp, _vp, _sz, _vp]),
+    ("k3_hbm_read_probe", _i, [_vp, _sz, _vp, _vp]),
     ("k3_shared_expert_bytes", _sz, [_i, _i]),
     ("k3_shared_experts", _i, [_vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
     ("k3_moe_layer_shared_workspace_bytes", _sz, [_i, _i, _i, _i, _i, _i]),
@@ -319,6 +320,12 @@ def k3_moe_prefill(X, logits, bias, experts, n_experts, hidden, inter, k, T, Y, 
     _call("k3_moe_prefill", _dp(X), _dp(logits), _dp(bias), _dp(experts), n_experts, hidden,
           inter, k, T, _dp(Y), _dp(Y_f32), _dp(idx), _dp(w), _dp(h_f32), _dp(h_nib), _dp(h_sc),
           _dp(ws), _nbytes(ws), _stream(stream))
+
+
+# ---- measurement ------------------------------------------------------------
+
+def k3_hbm_read_probe(buf, nbytes, sink, stream=None):
+    _call("k3_hbm_read_probe", _dp(buf), nbytes, _dp(sink), _stream(stream))
 
 
 # ---- shared experts ---------------------------------------------------------

@@ -421,6 +421,17 @@ k3_status k3_expert_gate_up(const uint16_t *x, const uint8_t *const *experts,
   return K3_OK;
 }
 
+k3_status k3_hbm_read_probe(const void *buf, size_t bytes, uint32_t *sink,
+                            k3_stream_t stream) {
+  const char *fn = "k3_hbm_read_probe";
+  K3_NEED_PTR(fn, buf);
+  K3_NEED_PTR(fn, sink);
+  K3_NEED(fn, bytes >= 16 && bytes % 16 == 0, "%s: bytes=%zu must be a positive multiple of 16",
+          fn, bytes);
+  K3_LAUNCH(fn, launch_read_probe(buf, bytes, sink, stream));
+  return K3_OK;
+}
+
 size_t k3_expert_dense_bytes(int hidden, int inter) {
   if (check_expert_dims("k3_expert_dense_bytes", hidden, inter) != K3_OK) return 0;
   return (size_t)3 * hidden * inter * sizeof(float);

@@ -197,6 +197,8 @@ hipError_t launch_moe_experts(const uint16_t *x, const double *logits,
                               uint64_t *slots, uint64_t val, int32_t *idx,
                               float *w, uint16_t *y, float *y_f32,
                               hipStream_t s, const float *add = nullptr);
+// Calibration read of `bytes` (a multiple of 16) at `buf` (k3_probe.hip).
+hipError_t launch_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s);
 // Pinned host buffer of K3_MAX_TOPK ints owned by an expert cache
 // (k3_cache.hip): where k3_moe_layer_cached receives a token's selection.
 int32_t *cache_selection_buffer(k3_cache_t c);

@@ -252,3 +252,18 @@ def test_topk_cases(case):
                              None if bias is None else bias.astype(np.float64))
         assert np.array_equal(idx_h[t], ii), (case, t, idx_h[t], ii)
         assert np.max(np.abs(w_h[t] - ww)) <= 1e-6
+
+
+def test_hbm_read_probe_runs_and_refuses():
+    """The calibration read streams a buffer and leaves the sink alone
+    (ordinary data does not fold to its magic value); bad sizes are refused."""
+    import torch
+    buf = torch.zeros(1 << 24, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    K.k3_hbm_read_probe(buf, buf.numel(), sink)
+    torch.cuda.synchronize()
+    assert int(sink.sum()) == 0
+    for n in (0, 15, 17):
+        with pytest.raises(K.K3Error) as e:
+            K.k3_hbm_read_probe(buf, n, sink)
+        assert e.value.status == K.K3_ERR_CONFIG
