@@ -151,6 +151,32 @@ def test_decode_layer_small(n, hidden, inter, k):
     check_against_oracle(out, x, R, seed, cfg, n, hidden, inter, k, 114, 120)
 
 
+def test_decode_layer_4096_experts_top64():
+    """The largest selection the ABI takes: 4096 experts (beyond 1024 the
+    layer ranks with the separate top-k launch), k = 64, small experts."""
+    n, hidden, inter, k, cfg, seed = K.K3_MAX_EXPERTS, 64, 32, K.K3_MAX_TOPK, 71, 4
+    say("decode layer n=4096 k=64 (separate launches)")
+    pool = D.build_expert_pool(seed, cfg, n, hidden, inter, 114, 120, workers=4)
+    R = gen.normal_bf16(gen.key(seed, cfg, gen.KIND_ROUTER), n * hidden, 0, 0.05).reshape(
+        n, hidden)
+    x = gen.normal_bf16(gen.key(seed, cfg, gen.KIND_TOKENS), hidden)
+    out = run_layer(pool, up(R), x, n, hidden, inter, k)
+    check_against_oracle(out, x, R, seed, cfg, n, hidden, inter, k, 114, 120)
+
+
+def test_decode_layer_largest_expert_shape():
+    """hidden = K3_MAX_HIDDEN (16384) and inter = K3_MAX_INTER (4096): 107 MB
+    per expert, through the single expert launch."""
+    n, hidden, inter, k, cfg, seed = 8, 16384, 4096, 2, 72, 5
+    say("decode layer hidden=16384 inter=4096 k=2")
+    pool = D.build_expert_pool(seed, cfg, n, hidden, inter, 114, 120, workers=4)
+    R = gen.normal_bf16(gen.key(seed, cfg, gen.KIND_ROUTER), n * hidden, 0, 0.02).reshape(
+        n, hidden)
+    x = gen.normal_bf16(gen.key(seed, cfg, gen.KIND_TOKENS), hidden)
+    out = run_layer(pool, up(R), x, n, hidden, inter, k)
+    check_against_oracle(out, x, R, seed, cfg, n, hidden, inter, k, 114, 120)
+
+
 def test_layer_over_many_tokens_on_one_workspace():
     """Twenty calls in a row on one workspace that starts as random bytes,
     a new token each time (every call must wait on its own arrival values,

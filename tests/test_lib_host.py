@@ -138,6 +138,29 @@ def test_refusals_before_launch(L):
     assert rc == K.K3_ERR_CONFIG
 
 
+def test_refusals_at_the_size_limits(L):
+    """Empty batches, and every size past its documented maximum, are
+    refused before any launch (no GPU needed)."""
+    s = None
+    nb = K.k3_moe_batched_workspace_bytes(1, 16, 128, 64, 2)
+    for T in (0, -1):
+        rc = L.k3_moe_layer_from_logits(_fake(1), _fake(2), None, _fake(3), 16, 128, 64, 2, T,
+                                        _fake(4), None, None, None, _fake(5), nb, s)
+        assert rc == K.K3_ERR_CONFIG, T
+    rc = L.k3_router_topk(_fake(1), None, 1, K.K3_MAX_EXPERTS + 1, 4, _fake(2), _fake(3), s)
+    assert rc == K.K3_ERR_CONFIG
+    rc = L.k3_expert_swiglu(_fake(1), _fake(2), 16384 + 32, 64, _fake(3), _fake(4), s)
+    assert rc == K.K3_ERR_CONFIG  # hidden above K3_MAX_HIDDEN
+    assert K.k3_expert_packed_bytes(16384, 4096) > 0
+    assert K.k3_expert_packed_bytes(16384 + 32, 4096) == 0
+    assert K.k3_moe_layer_shared_workspace_bytes(8, 128, 64, 2, K.K3_MAX_SHARED + 1, 64) == 0
+    h = ctypes.c_void_p()
+    for args in ((0, 256, 1), (8, 256, 0), (8, 256, 9), (8, 100, 4),
+                 (K.K3_MAX_EXPERTS + 1, 256, 4)):
+        rc = L.k3_cache_create(*args, ctypes.byref(h))
+        assert rc == K.K3_ERR_CONFIG and h.value is None, args
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(K, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(K, "_lib", None)
