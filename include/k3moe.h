@@ -406,6 +406,9 @@ k3_status k3_experts_dense(const uint16_t *x, const float *const *dense_experts,
  * asynchronous on the request's stream; keep one stream per cache so that a
  * slot is overwritten only after the kernels queued before it. Host blobs
  * should be pinned (hipHostMalloc) for the copies to be asynchronous.
+ * The policy calls are serialised by a lock; k3_moe_layer_cached also uses
+ * the cache's one pinned selection buffer, so its calls on one cache must
+ * not overlap (one calling thread per cache, as one stream per cache).
  *
  * k3_cache_create     n_slots HBM slots of expert_bytes (a multiple of 256)
  *                     for experts 0..n_experts-1 on the current device,
