@@ -470,6 +470,17 @@ k3_status k3_cache_replay(const int32_t *trace, size_t len, int n_experts,
 k3_status k3_cache_replay_opt(const int32_t *trace, size_t len, int n_experts,
                               int n_slots, const int32_t *pinned, int n_pinned,
                               int request_size, k3_cache_stats *out);
+/* Batched decode through a cache (as k3_moe_layer_from_logits): top-k of
+ * the T tokens, the T*k selection copied to the host (this call waits for
+ * it), one fetch of all of it (K3_ERR_MEMORY when its distinct misses
+ * exceed the evictable slots), then the resident batched layer on the
+ * cache's table, with the same bits. Refused under graph capture. */
+k3_status k3_moe_layer_from_logits_cached(const uint16_t *X, const double *logits,
+                                          const float *bias, k3_cache_t cache,
+                                          int n_experts, int hidden, int inter, int k,
+                                          int T, uint16_t *Y, float *Y_f32,
+                                          int32_t *idx, float *w, void *ws,
+                                          size_t ws_bytes, k3_stream_t stream);
 k3_status k3_moe_layer_cached(const uint16_t *x, const uint16_t *router_w,
                               k3_cache_t cache, int n_experts, int hidden,
                               int inter, int k, uint16_t *y, float *y_f32,

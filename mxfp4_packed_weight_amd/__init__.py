@@ -91,6 +91,8 @@ SIGNATURES = [
     ("k3_cache_trace", _i, [_vp, _vp, _sz, ctypes.POINTER(_sz)]),
     ("k3_cache_replay", _i, [_vp, _sz, _i, _i, _vp, _i, _i, _stats_p]),
     ("k3_cache_replay_opt", _i, [_vp, _sz, _i, _i, _vp, _i, _i, _stats_p]),
+    ("k3_moe_layer_from_logits_cached", _i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp,
+                                             _vp, _vp, _vp, _sz, _vp]),
     ("k3_moe_layer_cached", _i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
                                  _vp, _sz, _vp]),
 ]
@@ -448,3 +450,10 @@ def k3_moe_layer_cached(x, router_w, cache, n_experts, hidden, inter, k, y, ws, 
     _call("k3_moe_layer_cached", _dp(x), _dp(router_w), _vp(cache), n_experts, hidden, inter,
           k, _dp(y), _dp(y_f32), _dp(idx), _dp(w), _dp(logits), _dp(ws), _nbytes(ws),
           _stream(stream))
+
+
+def k3_moe_layer_from_logits_cached(X, logits, bias, cache, n_experts, hidden, inter, k, T, Y,
+                                    ws, Y_f32=None, idx=None, w=None, stream=None):
+    _call("k3_moe_layer_from_logits_cached", _dp(X), _dp(logits), _dp(bias), _vp(cache),
+          n_experts, hidden, inter, k, T, _dp(Y), _dp(Y_f32), _dp(idx), _dp(w), _dp(ws),
+          _nbytes(ws), _stream(stream))

@@ -769,7 +769,8 @@ k3_status k3_moe_layer_cached(const uint16_t *x, const uint16_t *router_w,
   float *wt = w ? w : reinterpret_cast<float *>(base + L.w);
   float *h = reinterpret_cast<float *>(base + L.h);
   float *yp = reinterpret_cast<float *>(base + L.yp);
-  int32_t *sel = cache_selection_buffer(cache);
+  int32_t *sel = cache_selection_buffer(cache, (size_t)k);
+  if (!sel) return fail(K3_ERR_MEMORY, "%s: pinned selection buffer", fn);
   // the token's selection decides the copies: router and top-k, then wait
   K3_LAUNCH(fn, launch_router(x, router_w, 1, hidden, n_experts, lg, stream));
   K3_LAUNCH(fn, launch_topk_f64(lg, nullptr, 1, n_experts, k, ix, wt, stream));
@@ -912,6 +913,41 @@ k3_status k3_moe_layer_from_logits(const uint16_t *X, const double *logits,
   K3_NEED_PTR(fn, logits);
   return batched_common(fn, X, nullptr, logits, bias, experts, n_experts, hidden,
                         inter, k, T, Y, Y_f32, idx, w, ws, ws_bytes, stream);
+}
+
+k3_status k3_moe_layer_from_logits_cached(const uint16_t *X, const double *logits,
+                                          const float *bias, k3_cache_t cache,
+                                          int n_experts, int hidden, int inter, int k,
+                                          int T, uint16_t *Y, float *Y_f32,
+                                          int32_t *idx, float *w, void *ws,
+                                          size_t ws_bytes, k3_stream_t stream) {
+  const char *fn = "k3_moe_layer_from_logits_cached";
+  K3_NEED_PTR(fn, logits);
+  K3_NEED_PTR(fn, ws);
+  if (!cache) return fail(K3_ERR_ARG, "%s: cache is NULL", fn);
+  if (bias && !aligned16(bias)) return fail(K3_ERR_ARG, "%s: bias is not 16-byte aligned", fn);
+  if (k3_status s = check_batch(fn, T, n_experts, k)) return s;
+  if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
+  const BatchWs B = batch_ws(T, n_experts, hidden, inter, k);
+  if (k3_status s = need_ws(fn, ws_bytes, B.total)) return s;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  K3_NEED(fn, hipStreamIsCapturing(stream, &cap) == hipSuccess &&
+                  cap == hipStreamCaptureStatusNone,
+          "%s: cannot be captured: the host chooses the copies per batch", fn);
+  const size_t P = (size_t)T * k;
+  int32_t *sel = cache_selection_buffer(cache, P);
+  if (!sel) return fail(K3_ERR_MEMORY, "%s: pinned selection buffer of %zu ints", fn, P);
+  // the batch's selection decides the copies: top-k, then wait for it
+  uint8_t *base = static_cast<uint8_t *>(ws);
+  int32_t *ix = reinterpret_cast<int32_t *>(base + B.idx);
+  float *wt = reinterpret_cast<float *>(base + B.w);
+  K3_LAUNCH(fn, launch_topk_f64(logits, bias, T, n_experts, k, ix, wt, stream));
+  K3_LAUNCH(fn, hipMemcpyAsync(sel, ix, sizeof(int32_t) * P, hipMemcpyDeviceToHost, stream));
+  K3_LAUNCH(fn, hipStreamSynchronize(stream));
+  if (k3_status s = k3_cache_fetch(cache, sel, (int)P, stream)) return s;
+  // then exactly the resident batched layer, reading the cache's table
+  return batched_common(fn, X, nullptr, logits, bias, k3_cache_table(cache), n_experts,
+                        hidden, inter, k, T, Y, Y_f32, idx, w, ws, ws_bytes, stream);
 }
 
 k3_status k3_moe_layer_batched(const uint16_t *X, const uint16_t *router_w,

@@ -181,12 +181,25 @@ struct ExpertCacheImpl {
   std::vector<const void *> src;           // host blob per expert
   std::vector<hipEvent_t> ev;              // per slot: its last copy
   std::vector<char> ev_live;
-  int32_t *sel_host = nullptr;             // pinned: a token's selection
+  int32_t *sel_host = nullptr;             // pinned: a batch's selection
+  size_t sel_cap = 0;                      // ints sel_host holds
 };
 
 namespace k3 {
 
-int32_t *cache_selection_buffer(k3_cache_t c) { return c ? c->sel_host : nullptr; }
+int32_t *cache_selection_buffer(k3_cache_t c, size_t n) {
+  if (!c) return nullptr;
+  std::lock_guard<std::mutex> g(c->mu);
+  if (n > c->sel_cap) {  // grow (pinned, so the copy into it is a plain DMA)
+    if (c->sel_host) (void)hipHostFree(c->sel_host);
+    c->sel_host = nullptr;
+    c->sel_cap = 0;
+    if (hipHostMalloc((void **)&c->sel_host, sizeof(int32_t) * n, hipHostMallocDefault) ==
+        hipSuccess)
+      c->sel_cap = n;
+  }
+  return c->sel_host;
+}
 
 namespace {
 
@@ -254,6 +267,7 @@ k3_status k3_cache_create(int n_experts, size_t expert_bytes, int n_slots,
   if (e == hipSuccess)
     e = hipHostMalloc((void **)&c->sel_host, sizeof(int32_t) * K3_MAX_TOPK,
                       hipHostMallocDefault);
+  if (e == hipSuccess) c->sel_cap = K3_MAX_TOPK;
   if (e != hipSuccess) {
     k3_cache_destroy(c);
     return device_status(e, fn);

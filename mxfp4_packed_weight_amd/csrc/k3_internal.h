@@ -199,9 +199,10 @@ hipError_t launch_moe_experts(const uint16_t *x, const double *logits,
                               hipStream_t s, const float *add = nullptr);
 // Calibration read of `bytes` (a multiple of 16) at `buf` (k3_probe.hip).
 hipError_t launch_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s);
-// Pinned host buffer of K3_MAX_TOPK ints owned by an expert cache
-// (k3_cache.hip): where k3_moe_layer_cached receives a token's selection.
-int32_t *cache_selection_buffer(k3_cache_t c);
+// Pinned host buffer of at least n ints owned by an expert cache
+// (k3_cache.hip), grown on demand (NULL if that fails): where the cached
+// layers receive a selection.
+int32_t *cache_selection_buffer(k3_cache_t c, size_t n);
 hipError_t launch_router(const uint16_t *x, const uint16_t *R, int T,
                          int hidden, int n, double *logits, hipStream_t s);
 hipError_t launch_topk_f64(const double *logits, const float *bias, int T,

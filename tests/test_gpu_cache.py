@@ -18,6 +18,9 @@
   exists for").
 - Refusals: ids outside the pool, an expert with no source, a request larger
   than the evictable slots, a capture of the cached layer.
+- Batched decode through a cache gives the resident batched layer's bits,
+  batch after batch with evictions between them, and a batch that names
+  more experts than the cache holds is refused with the cache unchanged.
 """
 import ctypes
 
@@ -230,6 +233,73 @@ def test_cache_refusals(small_pool):
                 refused = err
             y.zero_()
         assert refused is not None and refused.status == K.K3_ERR_CONFIG
+    finally:
+        torch.cuda.synchronize()
+        K.k3_cache_destroy(c)
+
+
+def batched_outputs(fn, arg, X, L, T, ws):
+    import torch
+    Y = empty((T, HIDDEN), torch.int16)
+    Y32 = empty((T, HIDDEN), torch.float32)
+    idx = empty((T, KTOP), torch.int32)
+    w = empty((T, KTOP), torch.float32)
+    fn(X, L, None, arg, N, HIDDEN, INTER, KTOP, T, Y, ws, Y_f32=Y32, idx=idx, w=w)
+    return dict(Y=Y.cpu().numpy().view(np.uint16), Y32=Y32.cpu().numpy().view(np.uint32),
+                idx=idx.cpu().numpy(), w=w.cpu().numpy().view(np.uint32))
+
+
+def test_batched_cached_layer_matches_resident(small_pool):
+    """Batches of 4 tokens (top-8 of 48) through 36 slots: each batch fits,
+    their union does not, so experts are evicted between batches. Every batch
+    gives the resident batched layer's bits; the counters equal the replay
+    with one request per batch."""
+    import torch
+    pool, _, host = small_pool
+    T, slots, nb = 4, 36, 6
+    say(f"batched cached layer: {nb} batches of {T} tokens through {slots} slots")
+    ws = empty(K.k3_moe_batched_workspace_bytes(T, N, HIDDEN, INTER, KTOP), torch.uint8)
+    ws2 = empty(K.k3_moe_batched_workspace_bytes(T, N, HIDDEN, INTER, KTOP), torch.uint8)
+    c = make_cache(pool, host, slots)
+    try:
+        trace = []
+        for b in range(nb):
+            X = up(W.tokens_bf16(SEED, CFG, T, HIDDEN, batch=b))
+            L = up(gen.uniform_f32(gen.key(SEED, CFG, gen.KIND_LOGITS, b, 0), T * N).astype(
+                np.float64).reshape(T, N))
+            want = batched_outputs(K.k3_moe_layer_from_logits, pool.table, X, L, T, ws)
+            got = batched_outputs(K.k3_moe_layer_from_logits_cached, c, X, L, T, ws2)
+            for key in want:
+                assert np.array_equal(got[key], want[key]), (b, key)
+            trace.extend(got["idx"].ravel().tolist())
+        st = K.k3_cache_get_stats(c)
+        ref = K.k3_cache_replay(np.array(trace, np.int32), N, slots, (), T * KTOP)
+        ref["bytes_copied"] = st["misses"] * pool.expert_bytes
+        assert st == ref
+        assert st["evictions"] > 0
+        say(f"batched cached layer: {st}")
+    finally:
+        torch.cuda.synchronize()
+        K.k3_cache_destroy(c)
+
+
+def test_batched_cached_layer_refuses_a_batch_larger_than_the_cache(small_pool):
+    """Five tokens whose top-8 sets are disjoint name 40 experts: more than
+    36 slots hold, so the call is refused and the cache is unchanged."""
+    import torch
+    pool, _, host = small_pool
+    T = 5
+    L = np.zeros((T, N))
+    for t in range(T):
+        L[t, 8 * t:8 * t + 8] = 10.0 - np.arange(8) * 0.1
+    ws = empty(K.k3_moe_batched_workspace_bytes(T, N, HIDDEN, INTER, KTOP), torch.uint8)
+    c = make_cache(pool, host, 36)
+    try:
+        X = up(W.tokens_bf16(SEED, CFG, T, HIDDEN))
+        with pytest.raises(K.K3Error) as e:
+            batched_outputs(K.k3_moe_layer_from_logits_cached, c, X, up(L), T, ws)
+        assert e.value.status == K.K3_ERR_MEMORY
+        assert K.k3_cache_get_stats(c)["requests"] == 0
     finally:
         torch.cuda.synchronize()
         K.k3_cache_destroy(c)
