@@ -205,6 +205,15 @@ def main():
     log(f"expert launch (top-k, gate/up, down, combine): {ex_us:.2f} us/launch, "
         f"{achieved:.1f} GB/s")
 
+    # two more timed regions of the same length: the run-to-run spread
+    repeats = [round(value, 2)]
+    for r in range(2):
+        ev0.record(stream)
+        for i in range(args.steps):
+            step(args.warmup + (r + 1) * args.steps + i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        repeats.append(round(expert_bytes / (ev0.elapsed_time(ev1) / args.steps * 1e-3) / 1e9, 2))
     # per-step spread: the same layer steps, one pair of events each
     spread = step_spread(step, args.warmup + args.steps, min(args.steps, 200), stream)
     # calibration: one streaming read over the whole 15.7 GB pool
@@ -244,6 +253,7 @@ def main():
         "calibrated_read_GBs": round(cal, 1),
         "pct_of_calibrated_read": round(100 * value / cal, 2),
         "step_us": spread,
+        "repeats_GBs": repeats,
         "all_bytes_GBs": round((expert_bytes + ROUTER_BYTES) / (ms_per_step * 1e-3) / 1e9, 2),
         "roofline": {"kernel": "moe_experts_kernel (top-k, gate/up, down, combine; "
                                "k3_moe_layer_from_logits with T = 1)",
@@ -439,6 +449,7 @@ def bench_c4(args):
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
     mean_distinct = sum(distinct[(args.warmup + i) % nb] for i in range(args.steps)) / args.steps
+    spread = step_spread(step, args.warmup, min(args.steps, 100), stream)
     nbytes = mean_distinct * BYTES_PER_EXPERT
     value = nbytes / (ms * 1e-3) / 1e9
     log(f"C4 layer: {ms * 1e3:.1f} us/batch, {mean_distinct:.1f} distinct experts, "
@@ -456,6 +467,7 @@ def bench_c4(args):
                    "expert_bytes_per_step": int(nbytes)},
         "tokens_per_s": round(T * 1e3 / ms, 1),
         "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "step_us": spread,
         "roofline": {"kernel": "whole batched layer (k3_moe_layer_from_logits)", "bound": "hbm",
                      "achieved": round(value, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(value / PEAK_HBM_GBS, 4), "traffic": None,
