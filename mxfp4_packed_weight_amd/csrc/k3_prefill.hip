@@ -31,6 +31,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kNB = 4;                 // 16-token column blocks per work item
 constexpr int kPfTok = 16 * kNB;       // tokens per prefill work item
 constexpr int kPfDepth = 2;            // quads in flight per wave
+constexpr int kPfWaves = kNB;          // weight tiles (waves) per workgroup
 
 // |v| / 2^E (exact) -> E2M1 magnitude code, nearest with ties to the even
 // code (0, 1.0, 2.0, 4.0), saturating at 6.
@@ -96,46 +97,60 @@ struct PfItems {
   const int32_t *e, *off, *cnt, *n;
 };
 
-// One wave per (work item, weight tile): C[64 rows][up to 64 tokens] over
-// the whole K of the matrix. kGateUp: the gate/up stack (A = tile s of the
-// expert's gate/up region, B = quantised x rows of the item's tokens);
-// epilogue h = SiLU(gate) * up, quantised per 32 (one group per tile) into
-// hq[pair]; optional fp32 h. Otherwise the down matrix (B = quantised h
-// rows of the item's pairs); epilogue yp[pair][row] fp32.
+// One workgroup of kPfWaves waves per (work item, group of kPfWaves
+// consecutive weight tiles); wave w computes C[64 rows][up to 64 tokens] of
+// tile s = kPfWaves * group + w over the whole K of the matrix. kGateUp: the
+// gate/up stack (A = tile s of the expert's gate/up region, B = quantised x
+// rows of the item's tokens); epilogue h = SiLU(gate) * up, quantised per 32
+// (one group per tile) into hq[pair]; optional fp32 h. Otherwise the down
+// matrix (B = quantised h rows of the item's pairs); epilogue yp[pair][row]
+// fp32.
+//
+// The waves of a workgroup share the item's activations: per quad, wave w
+// gathers only column block w of B (16 tokens x 4 groups, 16 bytes and one
+// exponent byte per lane) and writes it to a double-buffered LDS slot; after
+// one barrier every wave reads all four blocks from LDS. The gathers touch
+// 16 cache lines per instruction, and sharing them cuts their number per
+// wave by four. The weights stream through each wave's own register ring.
 template <bool kGateUp>
-__global__ __launch_bounds__(64) void prefill_gemm_kernel(
+__global__ __launch_bounds__(kPfWaves * 64) void prefill_gemm_kernel(
     const uint8_t *__restrict__ bq, const uint8_t *__restrict__ bsc,
     const int32_t *__restrict__ pair_token, const uint8_t *const *__restrict__ experts,
     PfItems it, int hidden, int inter, uint8_t *__restrict__ hq,
     uint8_t *__restrict__ hsc, float *__restrict__ h32, float *__restrict__ yp) {
+  static_assert(kPfWaves == kNB, "wave w gathers column block w");
+  __shared__ u32x4 bl[kPfDepth][kNB][64];     // B codes of a quad, lane order
+  __shared__ uint32_t bsl[kPfDepth][kNB][64];  // their exponent bytes
   const ExpertLayout L = expert_layout(hidden, inter);
   const MatLayout &M = kGateUp ? L.gu : L.down;
-  const int Tt = M.ntiles;
+  const int Tt = M.ntiles, ngrp = (Tt + kPfWaves - 1) / kPfWaves;
   const int u = blockIdx.x;
-  if (u >= ldc(it.n) * Tt) return;
-  const int item = u / Tt, s = u % Tt;
+  if (u >= ldc(it.n) * ngrp) return;  // the whole workgroup leaves together
+  const int wave = wave_id();
+  const int item = u / ngrp, s = kPfWaves * (u % ngrp) + wave;
+  const bool active = s < Tt;  // else: streams tile Tt - 1, stores nothing
   const int e = ldc(it.e + item), off = ldc(it.off + item), cnt = ldc(it.cnt + item);
   const uint8_t *tile = ldc(experts + e) + (kGateUp ? 0 : L.down_offset) +
-                        (size_t)s * M.tile_bytes;
+                        (size_t)(active ? s : Tt - 1) * M.tile_bytes;
   const int K = M.cols, G = M.G, G4 = M.G4;
   const int lane = threadIdx.x & 63, col = lane & 15, kb = lane >> 4;
 
-  // B rows of this lane for each column block (clamped to a valid row)
-  const uint8_t *brow[kNB];
-  const uint8_t *bsrow[kNB];
+  // which columns of each block hold tokens; the B row this lane gathers
+  // for its wave's own block (clamped to a valid row)
   bool bok[kNB];
 #pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) {
-    const int c = 16 * nb + col;
-    bok[nb] = c < cnt;
-    const int q = off + (bok[nb] ? c : 0);
+  for (int nb = 0; nb < kNB; ++nb) bok[nb] = 16 * nb + col < cnt;
+  const uint8_t *brow, *bsrow;
+  {
+    const int c = 16 * wave + col;
+    const int q = off + (c < cnt ? c : 0);
     const long long r = kGateUp ? (long long)ldc(pair_token + q) : (long long)q;
-    brow[nb] = bq + r * (K / 2);
-    bsrow[nb] = bsc + r * G;
+    brow = bq + r * (K / 2);
+    bsrow = bsc + r * G;
   }
 
-  u32x4 a[kPfDepth][4], b[kPfDepth][kNB];
-  uint32_t asc[kPfDepth][4], bs[kPfDepth][kNB];
+  u32x4 a[kPfDepth][4], b[kPfDepth];
+  uint32_t asc[kPfDepth][4], bs[kPfDepth];
   auto load = [&](int d, int q) {
     const uint8_t *qb = tile + (size_t)kQuadBytes * q;
 #pragma unroll
@@ -146,11 +161,8 @@ __global__ __launch_bounds__(64) void prefill_gemm_kernel(
           (const gu32_t *)(qb + 4096 + 4 * (16 * m + col)));
     }
     const int g = min(4 * q + kb, G - 1);  // groups past G are zero below
-#pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-      b[d][nb] = *(const gu4_t *)(brow[nb] + 16 * g);
-      bs[d][nb] = *(__attribute__((address_space(1))) const uint8_t *)(bsrow[nb] + g);
-    }
+    b[d] = *(const gu4_t *)(brow + 16 * g);
+    bs[d] = *(__attribute__((address_space(1))) const uint8_t *)(bsrow + g);
   };
   v4f acc[kNB][4];
 #pragma unroll
@@ -158,6 +170,11 @@ __global__ __launch_bounds__(64) void prefill_gemm_kernel(
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[nb][m] = v4f{0.f, 0.f, 0.f, 0.f};
   auto consume = [&](int d, int q) {
+    // share this wave's block of quad q; slot d was last read two quads ago,
+    // before the previous barrier
+    bl[d][wave][lane] = b[d];
+    bsl[d][wave][lane] = bs[d];
+    __syncthreads();
     const bool gin = 4 * q + kb < G;
     // B operands once per quad: a column past the item or a group past K
     // contributes nothing (zero codes, unit scale)
@@ -166,10 +183,10 @@ __global__ __launch_bounds__(64) void prefill_gemm_kernel(
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
       const bool use = bok[nb] && gin;
-      const u32x4 bm = b[d][nb];
+      const u32x4 bm = bl[d][nb][lane];
       bv[nb] = v8i{use ? (int)bm.x : 0, use ? (int)bm.y : 0, use ? (int)bm.z : 0,
                    use ? (int)bm.w : 0, 0, 0, 0, 0};
-      eb[nb] = use ? (int)bs[d][nb] : 127;
+      eb[nb] = use ? (int)bsl[d][nb][lane] : 127;
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -211,6 +228,7 @@ __global__ __launch_bounds__(64) void prefill_gemm_kernel(
     consume(0, 0);
   }
 
+  if (!active) return;  // a padding wave of a ragged tile group
   const int j = lane >> 4;  // C rows 4j + i of each 16-row sub-block
   if constexpr (kGateUp) {
     // tile rows 0..31 gate, 32..63 up (the same 32 output rows 32s + r)
@@ -291,8 +309,9 @@ hipError_t launch_prefill_gate_up(const uint8_t *xq, const uint8_t *xsc,
                                   float *h32, hipStream_t s) {
   const ExpertLayout L = expert_layout(hidden, inter);
   const PfItems it{o.item_e, o.item_off, o.item_cnt, o.n_items};
-  hipLaunchKernelGGL(prefill_gemm_kernel<true>,
-                     dim3((unsigned)((long long)max_items * L.gu.ntiles)), dim3(64),
+  const long long ngrp = (L.gu.ntiles + kPfWaves - 1) / kPfWaves;
+  hipLaunchKernelGGL(prefill_gemm_kernel<true>, dim3((unsigned)(max_items * ngrp)),
+                     dim3(kPfWaves * 64),
                      0, s, xq, xsc, o.pair_token, experts, it, hidden, inter, hq,
                      hsc, h32, nullptr);
   return hipGetLastError();
@@ -304,9 +323,9 @@ hipError_t launch_prefill_down(const uint8_t *hq, const uint8_t *hsc,
                                hipStream_t s) {
   const ExpertLayout L = expert_layout(hidden, inter);
   const PfItems it{o.item_e, o.item_off, o.item_cnt, o.n_items};
-  hipLaunchKernelGGL(prefill_gemm_kernel<false>,
-                     dim3((unsigned)((long long)max_items * L.down.ntiles)),
-                     dim3(64), 0, s, hq, hsc, o.pair_token, experts, it, hidden,
+  const long long ngrp = (L.down.ntiles + kPfWaves - 1) / kPfWaves;
+  hipLaunchKernelGGL(prefill_gemm_kernel<false>, dim3((unsigned)(max_items * ngrp)),
+                     dim3(kPfWaves * 64), 0, s, hq, hsc, o.pair_token, experts, it, hidden,
                      inter, nullptr, nullptr, nullptr, yp);
   return hipGetLastError();
 }
