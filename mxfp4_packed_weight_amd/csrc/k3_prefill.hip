@@ -30,8 +30,31 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kNB = 4;                 // 16-token column blocks per work item
 constexpr int kPfTok = 16 * kNB;       // tokens per prefill work item
-constexpr int kPfDepth = 2;            // quads in flight per wave
+#ifndef K3_PF_DEPTH
+#define K3_PF_DEPTH 4
+#endif
+constexpr int kPfDepth = K3_PF_DEPTH;  // weight quads in flight per wave (LDS)
+constexpr int kPfBDepth = 2;           // activation quads in flight (registers)
 constexpr int kPfWaves = kNB;          // weight tiles (waves) per workgroup
+
+typedef __attribute__((address_space(1))) void gvoid_t;
+typedef __attribute__((address_space(3))) void lvoid_t;
+
+// s_waitcnt immediates: vmcnt(n) with the other counters left free, and
+// lgkmcnt(0) with vmcnt and expcnt left free.
+constexpr int vm_wait_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+constexpr int kWaitLgkm0 = 0xC07F;
+// Loads issued per quad: five weight copies (four of 16 bytes and one of 4
+// per lane), then this wave's activation block (16 bytes and one byte).
+constexpr int kPfLoadsA = 5, kPfLoadsB = 2;
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+    case kPfLoadsA + kPfLoadsB: __builtin_amdgcn_s_waitcnt(vm_wait_imm(kPfLoadsA + kPfLoadsB)); break;
+    case kPfLoadsB: __builtin_amdgcn_s_waitcnt(vm_wait_imm(kPfLoadsB)); break;
+    case kPfLoadsA: __builtin_amdgcn_s_waitcnt(vm_wait_imm(kPfLoadsA)); break;
+    default: __builtin_amdgcn_s_waitcnt(vm_wait_imm(0)); break;
+  }
+}
 
 // |v| / 2^E (exact) -> E2M1 magnitude code, nearest with ties to the even
 // code (0, 1.0, 2.0, 4.0), saturating at 6.
@@ -119,8 +142,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_gemm_kernel(
     PfItems it, int hidden, int inter, uint8_t *__restrict__ hq,
     uint8_t *__restrict__ hsc, float *__restrict__ h32, float *__restrict__ yp) {
   static_assert(kPfWaves == kNB, "wave w gathers column block w");
-  __shared__ u32x4 bl[kPfDepth][kNB][64];     // B codes of a quad, lane order
-  __shared__ uint32_t bsl[kPfDepth][kNB][64];  // their exponent bytes
+  __shared__ u32x4 bl[kPfBDepth][kNB][64];     // B codes of a quad, lane order
+  __shared__ uint8_t bsl[kPfBDepth][kNB][64];   // their exponent bytes
   const ExpertLayout L = expert_layout(hidden, inter);
   const MatLayout &M = kGateUp ? L.gu : L.down;
   const int Tt = M.ntiles, ngrp = (Tt + kPfWaves - 1) / kPfWaves;
@@ -149,17 +172,29 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_gemm_kernel(
     bsrow = bsc + r * G;
   }
 
-  u32x4 a[kPfDepth][4], b[kPfDepth];
-  uint32_t asc[kPfDepth][4], bs[kPfDepth];
-  auto load = [&](int d, int q) {
+  // Weights: a ring of kPfDepth quads per wave in LDS, each slot a verbatim
+  // copy of one 4352-byte quad written by direct global -> LDS loads
+  // (non-temporal: each weight byte is read once), so no register holds
+  // weight bytes in flight. The compiler does not see that these loads write
+  // LDS: every slot is read only after an explicit vmcnt wait derived from
+  // the issue order, and refilled only after its reads completed.
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kPfWaves][kPfDepth][kQuadBytes];
+  u32x4 b[kPfBDepth];
+  uint8_t bs[kPfBDepth];  // widened only where used (no early wait for it)
+  auto load_a = [&](int slot, int q) {
     const uint8_t *qb = tile + (size_t)kQuadBytes * q;
+    uint8_t *dst = ring[wave][slot];
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the slot's last reads are done
+    asm volatile("" ::: "memory");
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      a[d][m] = __builtin_nontemporal_load(
-          (const gu4_t *)(qb + 1024 * kb + 16 * (16 * m + col)));
-      asc[d][m] = __builtin_nontemporal_load(
-          (const gu32_t *)(qb + 4096 + 4 * (16 * m + col)));
-    }
+    for (int c = 0; c < 4; ++c)
+      __builtin_amdgcn_global_load_lds((gvoid_t *)(qb + 1024 * c + 16 * lane),
+                                       (lvoid_t *)(dst + 1024 * c), 16, 0, 2);
+    __builtin_amdgcn_global_load_lds((gvoid_t *)(qb + 4096 + 4 * lane),
+                                     (lvoid_t *)(dst + 4096), 4, 0, 2);
+  };
+  auto load_b = [&](int d, int q) {
     const int g = min(4 * q + kb, G - 1);  // groups past G are zero below
     b[d] = *(const gu4_t *)(brow + 16 * g);
     bs[d] = *(__attribute__((address_space(1))) const uint8_t *)(bsrow + g);
@@ -169,12 +204,19 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_gemm_kernel(
   for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[nb][m] = v4f{0.f, 0.f, 0.f, 0.f};
-  auto consume = [&](int d, int q) {
+  auto consume = [&](int slot, int d, int q) {
     // share this wave's block of quad q; slot d was last read two quads ago,
-    // before the previous barrier
+    // before the previous barrier. The exponent byte stays a byte until it is
+    // read back, so that nothing widens it (and waits for its load) early.
     bl[d][wave][lane] = b[d];
     bsl[d][wave][lane] = bs[d];
-    __syncthreads();
+    // Barrier without a fence: the blocks are plain LDS writes, complete
+    // after lgkmcnt(0). (A fence would also wait for the weight copies in
+    // flight, vmcnt(0), and drain the ring at every quad.)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     const bool gin = 4 * q + kb < G;
     // B operands once per quad: a column past the item or a group past K
     // contributes nothing (zero codes, unit scale)
@@ -188,10 +230,36 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_gemm_kernel(
                    use ? (int)bm.w : 0, 0, 0, 0, 0};
       eb[nb] = use ? (int)bsl[d][nb][lane] : 127;
     }
+    // This lane's A operands of the quad: the codes of rows 16m + col of
+    // group 4q + kb and their exponent words, m = 0..3. Read in one block
+    // that waits for its own reads: the slot's copy is known complete from
+    // the explicit vmcnt wait before this step, and reads the compiler does
+    // not see get no conservative vmcnt(0) of its own.
+    u32x4 ar[4];
+    uint32_t sr[4];
+    {
+      typedef __attribute__((address_space(3))) const uint8_t lds_u8;
+      const uint32_t qa = (uint32_t)(size_t)(lds_u8 *)ring[wave][slot];
+      const uint32_t va = qa + 1024 * kb + 16 * col, vs = qa + 4096 + 4 * col;
+      asm volatile(
+          "ds_read_b128 %0, %8\n"
+          "ds_read_b128 %1, %8 offset:256\n"
+          "ds_read_b128 %2, %8 offset:512\n"
+          "ds_read_b128 %3, %8 offset:768\n"
+          "ds_read_b32 %4, %9\n"
+          "ds_read_b32 %5, %9 offset:64\n"
+          "ds_read_b32 %6, %9 offset:128\n"
+          "ds_read_b32 %7, %9 offset:192\n"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(ar[0]), "=&v"(ar[1]), "=&v"(ar[2]), "=&v"(ar[3]), "=&v"(sr[0]),
+            "=&v"(sr[1]), "=&v"(sr[2]), "=&v"(sr[3])
+          : "v"(va), "v"(vs)
+          : "memory");
+    }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      uint32_t ea = (asc[d][m] >> (8 * kb)) & 255u;
-      u32x4 am = a[d][m];
+      u32x4 am = ar[m];
+      uint32_t ea = (sr[m] >> (8 * kb)) & 255u;
       if (ea == 255u) {  // the group contributes nothing
         am = u32x4{0u, 0u, 0u, 0u};
         ea = 127u;
@@ -203,29 +271,72 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_gemm_kernel(
             av, bv[nb], acc[nb][m], 4, 4, 0, (int)ea, 0, eb[nb]);
     }
   };
-  // ring over the quads of K (loads unconditional in the steady loop)
-  int q = 0;
-  const int npro = min(kPfDepth, G4);
-  for (int d = 0; d < npro; ++d) load(d, d);
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  if (G4 >= kPfDepth) {
-    for (; q + 2 * kPfDepth <= G4; q += kPfDepth) {
+  // Loads issued after quad q's activation block (the last loads of quad q)
+  // when quad q is consumed: quad 0's block is followed by quad 1's; quad
+  // q >= 1's by step q - 1's weights (quad q - 1 + kPfDepth) and block
+  // (quad q - 1 + kPfBDepth), when those exist.
+  auto after = [&](int q) {
+    if (q == 0) return G4 > 1 ? kPfLoadsB : 0;
+    return (q - 1 + kPfDepth < G4 ? kPfLoadsA : 0) + (q - 1 + kPfBDepth < G4 ? kPfLoadsB : 0);
+  };
+  // a step whose next loads both exist: unconditional loads and a constant
+  // wait keep the compiler's own waits exact (no register merges)
+  auto steady = [&](int q, int d) {
+    asm volatile("" ::: "memory");  // no earlier load sinks below the wait
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(kPfLoadsA + kPfLoadsB));  // quad q is in
+    asm volatile("" ::: "memory");
+    consume(q % kPfDepth, d, q);
+    load_a(q % kPfDepth, q + kPfDepth);
+    load_b(d, q + kPfBDepth);
+  };
+  auto tail = [&](int q, int d) {
+    asm volatile("" ::: "memory");
+    wait_vmcnt(after(q));
+    asm volatile("" ::: "memory");
+    consume(q % kPfDepth, d, q);
+    if (q + kPfDepth < G4) load_a(q % kPfDepth, q + kPfDepth);
+    if (q + kPfBDepth < G4) load_b(d, q + kPfBDepth);
+  };
+  if (G4 >= kPfDepth + 2) {
 #pragma unroll
-      for (int d = 0; d < kPfDepth; ++d) {
-        consume(d, q + d);
-        load(d, q + kPfDepth + d);
+    for (int q = 0; q < kPfDepth; ++q) load_a(q, q);
+    load_b(0, 0);
+    load_b(1, 1);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(kPfLoadsB));  // quad 0 is in
+    asm volatile("" ::: "memory");
+    consume(0, 0, 0);
+    load_a(0, kPfDepth);
+    load_b(0, kPfBDepth);
+    int q = 1;
+    for (; q + 1 + kPfDepth < G4; q += 2) {
+      steady(q, 1);
+      steady(q + 1, 0);
+    }
+    for (; q < G4; ++q) {
+      if (q & 1)
+        tail(q, 1);
+      else
+        tail(q, 0);
+    }
+  } else {  // short K: every step waits for all of its loads
+    for (int q = 0; q < min(kPfDepth, G4); ++q) load_a(q, q);
+    load_b(0, 0);
+    if (G4 > 1) load_b(1, 1);
+    for (int q = 0; q < G4; ++q) {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+      asm volatile("" ::: "memory");
+      if (q & 1) {
+        consume(q % kPfDepth, 1, q);
+        if (q + kPfDepth < G4) load_a(q % kPfDepth, q + kPfDepth);
+        if (q + kPfBDepth < G4) load_b(1, q + kPfBDepth);
+      } else {
+        consume(q % kPfDepth, 0, q);
+        if (q + kPfDepth < G4) load_a(q % kPfDepth, q + kPfDepth);
+        if (q + kPfBDepth < G4) load_b(0, q + kPfBDepth);
       }
     }
-    for (int d = 0; d < kPfDepth; ++d)
-      if (q + d < G4) {
-        consume(d, q + d);
-        if (q + kPfDepth + d < G4) load(d, q + kPfDepth + d);
-      }
-    q += kPfDepth;
-    for (int d = 0; d < kPfDepth; ++d)
-      if (q + d < G4) consume(d, q + d);
-  } else {
-    consume(0, 0);
   }
 
   if (!active) return;  // a padding wave of a ragged tile group
