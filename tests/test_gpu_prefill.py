@@ -139,8 +139,16 @@ def check_prefill(out, X, logits, experts_of, k, hidden, inter, tokens):
     return max(errs_h), max(errs_y)
 
 
+# The GEMM kernels take a steady path when K has at least 6 quads of 128
+# (K >= 768) and a short path below; tile groups of four are ragged when a
+# matrix's tile count is not a multiple of 4, and the last quad is partial
+# when K % 128 != 0. The last three cases put the steady path on gate/up,
+# then on down (with experts of more than 64 tokens, two items each), with
+# ragged tile groups and partial last quads.
 @pytest.mark.parametrize("n,hidden,inter,k,T", [(12, 256, 128, 4, 40), (5, 96, 160, 5, 70),
-                                                (30, 512, 96, 8, 200), (3, 128, 64, 1, 9)])
+                                                (30, 512, 96, 8, 200), (3, 128, 64, 1, 9),
+                                                (10, 800, 224, 3, 50), (6, 288, 800, 2, 90),
+                                                (4, 256, 800, 2, 200)])
 def test_prefill_small(n, hidden, inter, k, T):
     cfg, seed = 73, 6
     say(f"prefill n={n} hidden={hidden} inter={inter} k={k} T={T}")
