@@ -38,10 +38,6 @@ constexpr int kTokBatch = K3_TOK_BATCH;  // tokens per work item (accumulators p
 constexpr int kBatchTPW = K3_BATCH_TPW;  // tiles per chunk of the grouped kernels
 constexpr int kPermThreads = 1024;
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
-  return __uint_as_float((uint32_t)b << 16);
-}
-
 // Inclusive prefix sum over the block's 1024 threads (wave scans + LDS).
 __device__ int block_scan_incl(int v, int *tmp) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;

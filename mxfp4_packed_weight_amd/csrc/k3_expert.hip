@@ -21,10 +21,6 @@ namespace {
 
 constexpr int kThreads = kNW * 64;
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
-  return __uint_as_float((uint32_t)b << 16);
-}
-
 __global__ __launch_bounds__(kThreads) void gemv_f32_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ tiles, int rows,
     int cols, float *__restrict__ y) {
@@ -119,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_routed_kernel(
   __shared__ float part[kPartFloats];
   __shared__ TopkWgLds tk;
   topk_wg<kNW>(logits, n, k, tk);
-  if (blockIdx.x == 0 && threadIdx.x < k) {
+  if (blockIdx.x == 0 && (int)threadIdx.x < k) {
     idx_out[threadIdx.x] = tk.sel[threadIdx.x];
     w_out[threadIdx.x] = tk.wt[threadIdx.x];
   }
@@ -173,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void moe_experts_kernel(
   __shared__ int bad;
   if (threadIdx.x == 0) bad = 0;
   topk_wg<kNW>(logits, n, k, tk);
-  if (blockIdx.x == 0 && threadIdx.x < k) {
+  if (blockIdx.x == 0 && (int)threadIdx.x < k) {
     idx_out[threadIdx.x] = tk.sel[threadIdx.x];
     w_out[threadIdx.x] = tk.wt[threadIdx.x];
   }

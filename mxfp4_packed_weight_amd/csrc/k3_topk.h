@@ -148,7 +148,7 @@ __device__ __forceinline__ void topk_core(const LT (&raw)[KPL],
   uint32_t pre = 0;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t c = pre | (1u << bit);
-    if (__popcll(__ballot(um >= c)) >= k) pre = c;
+    if ((int)__popcll(__ballot(um >= c)) >= k) pre = c;
   }
   const double tau = (double)f32_unorder(pre);
   // 2. candidates (key >= tau): per-lane count, exclusive prefix over lanes
