@@ -295,28 +295,43 @@ __global__ __launch_bounds__(kThreads) void down_batched_kernel(
 }
 
 // Y[t][i] = sum_j w[t][j] * yp[pair_pos[t*k + j]][i] in rank order j, fp32,
-// then bf16 (RNE).
+// then bf16 (RNE); four consecutive columns per thread (16-byte loads and
+// stores). hidden % 32 == 0, and yp, Y and Y32 are 16-byte aligned (the ABI
+// refuses other outputs). Tokens past the grid's y extent are taken in
+// strides of it.
 __global__ __launch_bounds__(256) void combine_batched_kernel(
     const float *__restrict__ yp, const float *__restrict__ w,
-    const int32_t *__restrict__ pair_pos, int k, int hidden,
+    const int32_t *__restrict__ pair_pos, int k, int hidden, int T,
     uint16_t *__restrict__ Y, float *__restrict__ Y32) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  const int t = blockIdx.y;
+  const int i = 4 * (blockIdx.x * 256 + threadIdx.x);
   if (i >= hidden) return;
-  float acc = 0.f;
-  for (int j0 = 0; j0 < k; j0 += 16) {  // issue a batch of loads, then add
-    float v[16];
+  for (int t = blockIdx.y; t < T; t += gridDim.y) {  // tokens past the grid's y extent
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int j0 = 0; j0 < k; j0 += 16) {  // issue a batch of loads, then add
+      float4 v[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      v[j] = j0 + j < k
-                 ? yp[(size_t)pair_pos[(size_t)t * k + j0 + j] * hidden + i]
-                 : 0.f;
+      for (int j = 0; j < 16; ++j)
+        v[j] = j0 + j < k ? *reinterpret_cast<const float4 *>(
+                                yp + (size_t)pair_pos[(size_t)t * k + j0 + j] * hidden + i)
+                          : float4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (j0 + j < k) acc = fmaf(w[(size_t)t * k + j0 + j], v[j], acc);
+      for (int j = 0; j < 16; ++j)
+        if (j0 + j < k) {
+          const float wj = w[(size_t)t * k + j0 + j];
+          a0 = fmaf(wj, v[j].x, a0);
+          a1 = fmaf(wj, v[j].y, a1);
+          a2 = fmaf(wj, v[j].z, a2);
+          a3 = fmaf(wj, v[j].w, a3);
+        }
+    }
+    const size_t o = (size_t)t * hidden + i;
+    if (Y32) *reinterpret_cast<float4 *>(Y32 + o) = float4{a0, a1, a2, a3};
+    if (Y) {
+      const uint32_t lo = f32_to_bf16_rne(a0) | ((uint32_t)f32_to_bf16_rne(a1) << 16);
+      const uint32_t hi = f32_to_bf16_rne(a2) | ((uint32_t)f32_to_bf16_rne(a3) << 16);
+      *reinterpret_cast<uint2 *>(Y + o) = uint2{lo, hi};
+    }
   }
-  if (Y32) Y32[(size_t)t * hidden + i] = acc;
-  if (Y) Y[(size_t)t * hidden + i] = f32_to_bf16_rne(acc);
 }
 
 unsigned persistent_grid() { return (unsigned)(num_cus() * K3_BATCH_WG_PER_CU); }
@@ -358,8 +373,9 @@ hipError_t launch_combine_batched(const float *yp, const float *w,
                                   const int32_t *pair_pos, int T, int k,
                                   int hidden, uint16_t *Y, float *Y32,
                                   hipStream_t s) {
-  hipLaunchKernelGGL(combine_batched_kernel, dim3((hidden + 255) / 256, T),
-                     dim3(256), 0, s, yp, w, pair_pos, k, hidden, Y, Y32);
+  const unsigned gy = (unsigned)(T < 65535 ? T : 65535);
+  hipLaunchKernelGGL(combine_batched_kernel, dim3((hidden / 4 + 255) / 256, gy), dim3(256), 0,
+                     s, yp, w, pair_pos, k, hidden, T, Y, Y32);
   return hipGetLastError();
 }
 

@@ -235,3 +235,18 @@ def test_batched_layer_with_routing_bias():
     assert np.max(np.abs(out["w"] - w_ref)) <= 1e-6
     for t in range(T):
         assert normwise(out["Y32"][t], Y_ref[t]) <= TOL, t
+
+
+def test_batched_beyond_grid_y():
+    """More tokens than the grid's y extent (65535): the combine strides over
+    tokens."""
+    cfg, seed, n, hidden, inter, k, T = 74, 7, 4, 64, 32, 1, 70000
+    say(f"batched from logits, T={T} tokens")
+    pool = D.build_expert_pool(seed, cfg, n, hidden, inter, 114, 120, workers=2)
+    X = W.tokens_bf16(seed, cfg, T, hidden)
+    logits = W.uniform_router_logits(seed, T, n, cfg).astype(np.float64)
+    out = run_batched(pool, X, n, hidden, inter, k, logits=logits)
+    err = check_tokens(out, X, logits,
+                       lambda e: W.expert_weights(seed, cfg, e, hidden, inter, 114, 120),
+                       k, hidden, inter, [0, 1, 65534, 65535, 65536, T - 1])
+    say(f"T={T}: max normwise {err:.3e} on sampled tokens")
