@@ -39,6 +39,20 @@ def log(msg):
     sys.stderr.flush()
 
 
+def host_info():
+    """The host the oracle baseline ran on: CPU model and logical CPUs."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count()}
+
+
 def cpu_baseline(budget_s=15.0, max_tokens=600):
     """The oracle as it stands, timed on the host's cores over a bounded sample:
     whole decode layers (router GEMV, sigmoid top-16, 16 SwiGLU experts,
@@ -74,7 +88,7 @@ def cpu_baseline(budget_s=15.0, max_tokens=600):
         tokens1 += 1
     oracle.set_threads(threads)
     return {"value": round(BYTES_PER_EXPERT * W.TOPK / per_token / 1e9, 4), "unit": "GB/s",
-            "cores": threads, "kind": "oracle",
+            "cores": threads, "kind": "oracle", "host": host_info(),
             "tokens_per_s": round(1.0 / per_token, 4),
             "single_thread": {"tokens_per_s": round(tokens1 / spent1, 4), "cores": 1,
                               "value": round(BYTES_PER_EXPERT * W.TOPK * tokens1 / spent1 / 1e9,
@@ -398,7 +412,8 @@ def bench_c1_c2(args):
                      "unit": "GB/s", "frac": round(value / PEAK_HBM_GBS, 4), "traffic": None,
                      "algorithmic_bytes_per_launch": nbytes},
         "cpu_baseline": {"value": round(nbytes / cpu_s / 1e9, 4), "unit": "GB/s",
-                         "cores": threads, "kind": "oracle", "sample": cpu_sample},
+                         "cores": threads, "kind": "oracle", "host": host_info(),
+                         "sample": cpu_sample},
     }
     print(json.dumps(out))
 
@@ -480,7 +495,7 @@ def bench_c4(args):
         per_tok = 1.0 / cb["tokens_per_s"]
         out["cpu_baseline"] = {
             "value": round(nbytes / (T * per_tok) / 1e9, 4), "unit": "GB/s", "cores": cb["cores"],
-            "kind": "oracle", "tokens_per_s": cb["tokens_per_s"],
+            "kind": "oracle", "host": cb["host"], "tokens_per_s": cb["tokens_per_s"],
             "sample": cb["sample"] + "; the oracle reads every selected expert once per token, "
                       "so a 64-token batch costs it 64 such layers"}
     print(json.dumps(out))
@@ -829,7 +844,8 @@ def cpu_baseline_c5(budget_s=15.0):
         experts += 1
     full = spent * (T * k) / pairs
     return {"value": round(n * BYTES_PER_EXPERT / full / 1e9, 4), "unit": "GB/s",
-            "cores": threads, "kind": "oracle", "tokens_per_s": round(T / full, 4),
+            "cores": threads, "kind": "oracle", "host": host_info(),
+            "tokens_per_s": round(T / full, 4),
             "sample": f"{experts} experts with their {pairs} routed tokens of one C5 batch "
                       f"through the oracle's quantiser and MXFP4 x MXFP4 products (fp64, "
                       f"{threads} OpenMP threads), {spent:.1f} s, scaled by "
