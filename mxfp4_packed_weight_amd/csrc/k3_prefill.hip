@@ -134,7 +134,8 @@ struct PfItems {
 // exponent byte per lane) and writes it to a double-buffered LDS slot; after
 // one barrier every wave reads all four blocks from LDS. The gathers touch
 // 16 cache lines per instruction, and sharing them cuts their number per
-// wave by four. The weights stream through each wave's own register ring.
+// wave by four. The weights stream through each wave's own ring of quads in
+// LDS (below).
 template <bool kGateUp>
 __global__ __launch_bounds__(kPfWaves * 64) void prefill_gemm_kernel(
     const uint8_t *__restrict__ bq, const uint8_t *__restrict__ bsc,
@@ -175,9 +176,10 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_gemm_kernel(
   // Weights: a ring of kPfDepth quads per wave in LDS, each slot a verbatim
   // copy of one 4352-byte quad written by direct global -> LDS loads
   // (non-temporal: each weight byte is read once), so no register holds
-  // weight bytes in flight. The compiler does not see that these loads write
-  // LDS: every slot is read only after an explicit vmcnt wait derived from
-  // the issue order, and refilled only after its reads completed.
+  // weight bytes in flight. The compiler's own waits around such copies are
+  // missing or too conservative (vmcnt(0)), so a slot is read only after an
+  // explicit vmcnt wait derived from the issue order, by reads it does not
+  // see (one asm block, below), and refilled only after those completed.
   __shared__ __attribute__((aligned(16))) uint8_t ring[kPfWaves][kPfDepth][kQuadBytes];
   u32x4 b[kPfBDepth];
   uint8_t bs[kPfBDepth];  // widened only where used (no early wait for it)
