@@ -88,32 +88,54 @@ __device__ __forceinline__ uint32_t e2m1_code(float v, float inv) {
 }
 
 // Quantiser: v[rows][cols] -> nib[rows][cols/2] (element 2b in the low
-// nibble of byte b) and sc[rows][cols/32]. Each half-wave owns one block of
-// 32 values, one per lane.
+// nibble of byte b) and sc[rows][cols/32]. One lane per block of 32 values:
+// 16-byte loads of the block, its largest magnitude, the block exponent and
+// 32 codes (each by the same rule), one 16-byte store of the codes and one
+// exponent byte. Rows are a multiple of 32 values, and v and nib are 16-byte
+// aligned (the ABI refuses other buffers).
 template <typename T>
 __global__ __launch_bounds__(256) void quant_kernel(const T *__restrict__ v,
                                                     long long nblocks, int cols,
                                                     uint8_t *__restrict__ nib,
                                                     uint8_t *__restrict__ sc) {
-  const long long blk = ((long long)blockIdx.x * 256 + threadIdx.x) >> 5;
-  const int i = threadIdx.x & 31;
-  if (blk >= nblocks) return;  // whole half-waves leave together
+  const long long blk = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (blk >= nblocks) return;
   const int G = cols / 32;
   const long long r = blk / G, g = blk % G;
-  float x;
-  if constexpr (sizeof(T) == 2)
-    x = __uint_as_float((uint32_t)v[r * cols + g * 32 + i] << 16);
-  else
-    x = (float)v[r * cols + g * 32 + i];
-  float a = fabsf(x);
+  float x[32];
+  if constexpr (sizeof(T) == 2) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(v + r * cols + g * 32);
 #pragma unroll
-  for (int d = 1; d < 32; d <<= 1) a = fmaxf(a, __shfl_xor(a, d, 32));
+    for (int q = 0; q < 4; ++q) {
+      const uint4 u = src[q];
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[8 * q + 2 * i] = __uint_as_float(w[i] << 16);
+        x[8 * q + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    }
+  } else {
+    const float4 *src = reinterpret_cast<const float4 *>(v + r * cols + g * 32);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float4 f = src[q];
+      x[4 * q] = f.x;
+      x[4 * q + 1] = f.y;
+      x[4 * q + 2] = f.z;
+      x[4 * q + 3] = f.w;
+    }
+  }
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(x[i]));
   float inv;
   const uint32_t e = mx_scale(a, &inv);
-  const uint32_t c = e2m1_code(x, inv);
-  const uint32_t hi = __shfl_down(c, 1, 32);
-  if ((i & 1) == 0) nib[r * (cols / 2) + g * 16 + i / 2] = (uint8_t)(c | (hi << 4));
-  if (i == 0) sc[r * G + g] = (uint8_t)e;
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) w[i / 8] |= e2m1_code(x[i], inv) << (4 * (i % 8));
+  *reinterpret_cast<uint4 *>(nib + r * (cols / 2) + g * 16) = uint4{w[0], w[1], w[2], w[3]};
+  sc[r * G + g] = (uint8_t)e;
 }
 
 struct PfItems {
@@ -399,8 +421,7 @@ int prefill_tok_batch() { return kPfTok; }
 hipError_t launch_quant_bf16(const uint16_t *v, long long rows, int cols,
                              uint8_t *nib, uint8_t *sc, hipStream_t s) {
   const long long nblocks = rows * (cols / 32);
-  const long long threads = nblocks * 32;
-  hipLaunchKernelGGL(quant_kernel<uint16_t>, dim3((unsigned)((threads + 255) / 256)),
+  hipLaunchKernelGGL(quant_kernel<uint16_t>, dim3((unsigned)((nblocks + 255) / 256)),
                      dim3(256), 0, s, v, nblocks, cols, nib, sc);
   return hipGetLastError();
 }
@@ -408,8 +429,7 @@ hipError_t launch_quant_bf16(const uint16_t *v, long long rows, int cols,
 hipError_t launch_quant_f32(const float *v, long long rows, int cols,
                             uint8_t *nib, uint8_t *sc, hipStream_t s) {
   const long long nblocks = rows * (cols / 32);
-  const long long threads = nblocks * 32;
-  hipLaunchKernelGGL(quant_kernel<float>, dim3((unsigned)((threads + 255) / 256)),
+  hipLaunchKernelGGL(quant_kernel<float>, dim3((unsigned)((nblocks + 255) / 256)),
                      dim3(256), 0, s, v, nblocks, cols, nib, sc);
   return hipGetLastError();
 }
