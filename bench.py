@@ -120,15 +120,18 @@ def main():
                          "through such a cache; c3-dequant: the expert stage "
                          "from dequantised fp32 copies against the packed bytes; c3-shared: "
                          "the c3 layer plus two bf16 shared experts (7168/1536)")
-    ap.add_argument("--cache-slots", type=int, default=128,
-                    help="HBM slots of the expert cache (c3-cached)")
+    ap.add_argument("--cache-slots", type=int, default=None,
+                    help="HBM slots of the expert cache (default 128 for c3-cached, 640 for "
+                         "c4-cached, whose batches touch ~330 distinct experts)")
     ap.add_argument("--calib", action="store_true",
                     help="after the timed region, copy 1 GiB device-to-device three times "
                          "(the known-size kernel the HBM byte counters are scaled by)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
-                         "WRITE_SIZE) of a --calib run into profiles/gate_up_c3_traffic.json")
+                         "WRITE_SIZE) of a --calib run into profiles/experts_c3_traffic.json")
     args = ap.parse_args()
+    if args.cache_slots is None:
+        args.cache_slots = 640 if args.workload == "c4-cached" else 128
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
         return
