@@ -294,6 +294,8 @@ __global__ __launch_bounds__(kThreads) void down_batched_kernel(
       part);
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 // Y[t][i] = sum_j w[t][j] * yp[pair_pos[t*k + j]][i] in rank order j, fp32,
 // then bf16 (RNE); four consecutive columns per thread (16-byte loads and
 // stores). hidden % 32 == 0, and yp, Y and Y32 are 16-byte aligned (the ABI
@@ -308,12 +310,12 @@ __global__ __launch_bounds__(256) void combine_batched_kernel(
   for (int t = blockIdx.y; t < T; t += gridDim.y) {  // tokens past the grid's y extent
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
     for (int j0 = 0; j0 < k; j0 += 16) {  // issue a batch of loads, then add
-      float4 v[16];
+      f32x4 v[16];  // partials are read once: non-temporal
 #pragma unroll
       for (int j = 0; j < 16; ++j)
-        v[j] = j0 + j < k ? *reinterpret_cast<const float4 *>(
-                                yp + (size_t)pair_pos[(size_t)t * k + j0 + j] * hidden + i)
-                          : float4{0.f, 0.f, 0.f, 0.f};
+        v[j] = j0 + j < k ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(
+                                yp + (size_t)pair_pos[(size_t)t * k + j0 + j] * hidden + i))
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 16; ++j)
         if (j0 + j < k) {

@@ -407,8 +407,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_gemm_kernel(
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int row = 64 * s + 16 * m + 4 * j;
-        if (row < hidden)
-          *reinterpret_cast<v4f *>(yp + p * hidden + row) = acc[nb][m];
+        if (row < hidden)  // non-temporal: read once, by the combine
+          __builtin_nontemporal_store(acc[nb][m], reinterpret_cast<v4f *>(yp + p * hidden + row));
       }
     }
   }
