@@ -60,8 +60,10 @@ constexpr int kRouterSplit = 4;  // waves per router row
 // (XLds = false, at xg) or from the workgroup's LDS copy (XLds = true, at
 // xl); R row at Rrow; hidden a multiple of 8. Returns the wave's fp64 sum
 // (four chains per lane, then the DPP tree), the same in every lane; the
-// kRouterSplit partials are added as (p0 + p1) + (p2 + p3).
-template <bool XLds>
+// kRouterSplit partials are added as (p0 + p1) + (p2 + p3). NT: the row is
+// read once (one token), so its loads are non-temporal; with several tokens
+// the row is read once per token and stays cached.
+template <bool XLds, bool NT>
 __device__ __forceinline__ double router_row_part(const uint16_t *__restrict__ Rrow,
                                                   const uint16_t *__restrict__ xg,
                                                   const u32x4 *xl, int hidden,
@@ -80,7 +82,7 @@ __device__ __forceinline__ double router_row_part(const uint16_t *__restrict__ R
     for (int i = 0; i < kRouterCPL; ++i) {
       if (c0 + kStride * i >= nchunk) break;  // wave-uniform
       const int c = min(c0 + lane + kStride * i, nchunk - 1);
-      rv[i] = Rr[c];
+      rv[i] = NT ? __builtin_nontemporal_load(Rr + c) : Rr[c];
       if (!XLds) xv[i] = xr[c];
     }
 #pragma unroll
@@ -99,12 +101,13 @@ __device__ __forceinline__ double router_row_part(const uint16_t *__restrict__ R
 // Logit of router row e for token x: the kRouterSplit waves of the
 // calling workgroup each take their part and wave 0's lane 0 stores
 // (p0 + p1) + (p2 + p3). `partial` is the workgroup's LDS scratch.
+template <bool NT>
 __device__ __forceinline__ void router_row_logit(const uint16_t *__restrict__ Rrow,
                                                  const uint16_t *__restrict__ x,
                                                  int hidden, double *partial,
                                                  double *out) {
   const int w = wave_id();
-  const double p = router_row_part<false>(Rrow, x, nullptr, hidden, w);
+  const double p = router_row_part<false, NT>(Rrow, x, nullptr, hidden, w);
   if ((threadIdx.x & 63) == 0) partial[w] = p;
   __syncthreads();
   if (threadIdx.x == 0) *out = (partial[0] + partial[1]) + (partial[2] + partial[3]);

@@ -23,14 +23,16 @@ namespace {
 // One workgroup of kRouterSplit waves per (row, token); tokens beyond the
 // grid's y extent are taken in strides of it.
 static_assert(kRouterSplit == 4, "the partials are added as (p0 + p1) + (p2 + p3)");
+// NT: one token (each router row is read once, non-temporally).
+template <bool NT>
 __global__ __launch_bounds__(kRouterSplit * 64) void router_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ R, int hidden,
     int n, int T, double *__restrict__ logits) {
   __shared__ double partial[kRouterSplit];
   const int e = blockIdx.x;
   for (int t = blockIdx.y; t < T; t += gridDim.y)
-    router_row_logit(R + (size_t)e * hidden, x + (size_t)t * hidden, hidden, partial,
-                     logits + (size_t)t * n + e);
+    router_row_logit<NT>(R + (size_t)e * hidden, x + (size_t)t * hidden, hidden, partial,
+                         logits + (size_t)t * n + e);
 }
 
 
@@ -77,8 +79,12 @@ hipError_t launch_topk(const LT *logits, const float *bias, int T, int n,
 
 hipError_t launch_router(const uint16_t *x, const uint16_t *R, int T,
                          int hidden, int n, double *logits, hipStream_t s) {
-  hipLaunchKernelGGL(router_kernel, dim3(n, T < 65535 ? T : 65535),
-                     dim3(kRouterSplit * 64), 0, s, x, R, hidden, n, T, logits);
+  if (T == 1)
+    hipLaunchKernelGGL(router_kernel<true>, dim3(n, 1), dim3(kRouterSplit * 64), 0, s, x, R,
+                       hidden, n, T, logits);
+  else
+    hipLaunchKernelGGL(router_kernel<false>, dim3(n, T < 65535 ? T : 65535),
+                       dim3(kRouterSplit * 64), 0, s, x, R, hidden, n, T, logits);
   return hipGetLastError();
 }
 

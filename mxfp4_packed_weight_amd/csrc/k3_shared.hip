@@ -89,8 +89,8 @@ __global__ __launch_bounds__(64 * kSharedWaves) void router_shared_kernel(
     int n_shared, int hidden, int inter, float *__restrict__ h) {
   __shared__ double partial[kRouterSplit];
   if ((int)blockIdx.x < n_experts) {
-    router_row_logit(R + (size_t)blockIdx.x * hidden, x, hidden, partial,
-                     logits + blockIdx.x);
+    router_row_logit<true>(R + (size_t)blockIdx.x * hidden, x, hidden, partial,
+                           logits + blockIdx.x);
     return;
   }
   const int gw = ((int)blockIdx.x - n_experts) * kSharedWaves + (threadIdx.x >> 6);
