@@ -39,6 +39,15 @@ def log(msg):
     sys.stderr.flush()
 
 
+def with_speedup(out):
+    """Adds the GPU-over-oracle ratio of `value` to a line's cpu_baseline
+    (same unit), when both are there."""
+    cb = out.get("cpu_baseline")
+    if cb and cb.get("value"):
+        cb["gpu_over_oracle"] = round(out["value"] / cb["value"], 1)
+    return out
+
+
 def host_info():
     """The host the oracle baseline ran on: CPU model and logical CPUs."""
     model = None
@@ -284,7 +293,7 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (bounded sample)")
         out["cpu_baseline"] = cpu_baseline()
-    print(json.dumps(out))
+    print(json.dumps(with_speedup(out)))
 
 
 def step_spread(step, first, n, stream):
@@ -418,7 +427,7 @@ def bench_c1_c2(args):
                          "cores": threads, "kind": "oracle", "host": host_info(),
                          "sample": cpu_sample},
     }
-    print(json.dumps(out))
+    print(json.dumps(with_speedup(out)))
 
 
 def bench_c4(args):
@@ -501,7 +510,7 @@ def bench_c4(args):
             "kind": "oracle", "host": cb["host"], "tokens_per_s": cb["tokens_per_s"],
             "sample": cb["sample"] + "; the oracle reads every selected expert once per token, "
                       "so a 64-token batch costs it 64 such layers"}
-    print(json.dumps(out))
+    print(json.dumps(with_speedup(out)))
 
 
 def bench_c4_cached(args):
@@ -929,7 +938,7 @@ def bench_c5(args):
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (bounded sample)")
         out["cpu_baseline"] = cpu_baseline_c5()
-    print(json.dumps(out))
+    print(json.dumps(with_speedup(out)))
 
 
 CALIB_BYTES = 1 << 30
