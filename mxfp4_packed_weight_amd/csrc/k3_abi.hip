@@ -576,7 +576,10 @@ size_t k3_moe_workspace_bytes(int T, int n_experts, int hidden, int inter,
 // expert work in one launch (its stages marked by a per-call value; a graph
 // being captured would replay one value, so it gets the separate launches,
 // as does a selection over more than 1024 experts). `add` (or NULL) is
-// added to each output row before the bf16 cast.
+// added to each output row before the bf16 cast. `sh` (or NULL): the shared
+// experts' down stage, whose h an earlier launch wrote; the expert launch
+// takes it between its two stages, the separate launches run it first. Its
+// sum ys is then what is added.
 static k3_status layer_launches(const char *fn, const uint16_t *x,
                                 const uint16_t *router_w,
                                 const uint8_t *const *experts, int n_experts,
@@ -584,7 +587,8 @@ static k3_status layer_launches(const char *fn, const uint16_t *x,
                                 float *y_f32, int32_t *idx, float *w,
                                 double *logits, uint8_t *base, const WsLayout &L,
                                 const float *add, hipStream_t stream,
-                                bool routed_already = false) {
+                                bool routed_already = false,
+                                const SharedStage *sh = nullptr) {
   double *lg = logits ? logits : reinterpret_cast<double *>(base + L.logits);
   int32_t *ix = idx ? idx : reinterpret_cast<int32_t *>(base + L.idx);
   float *wt = w ? w : reinterpret_cast<float *>(base + L.w);
@@ -600,8 +604,13 @@ static k3_status layer_launches(const char *fn, const uint16_t *x,
     K3_LAUNCH(fn, launch_moe_experts(x, lg, experts, n_experts, k, hidden,
                                      inter, h, yp,
                                      reinterpret_cast<uint64_t *>(base + L.sync),
-                                     next_layer_seq(), ix, wt, y, y_f32, stream, add));
+                                     next_layer_seq(), ix, wt, y, y_f32, stream, add, sh));
     return K3_OK;
+  }
+  if (sh) {
+    K3_LAUNCH(fn, launch_shared_down(sh->hs, sh->shared, sh->n_shared, hidden, sh->inter,
+                                     sh->ys, stream));
+    add = sh->ys;
   }
   if (n_experts <= kFusedTopkMaxExperts) {  // top-k inside the gate/up launch
     K3_LAUNCH(fn, launch_gate_up_routed(x, lg, experts, n_experts, k, hidden,
@@ -723,16 +732,17 @@ k3_status k3_moe_layer_shared(const uint16_t *x, const uint16_t *router_w,
   if (n_shared == 0)
     return layer_launches(fn, x, router_w, experts, n_experts, hidden, inter, k, y,
                           y_f32, idx, w, logits, base, S.L, nullptr, stream);
-  // The router rows and the shared experts' gate/up rows in one launch, the
-  // shared down stage, then the expert launch, whose combine adds ys.
+  // The router rows and the shared experts' gate/up rows in one launch, then
+  // the expert work with the shared down stage (its sum ys is added to each
+  // output row).
   float *ys = reinterpret_cast<float *>(base + S.ys);
   float *hs = reinterpret_cast<float *>(base + S.hs);
   double *lg = logits ? logits : reinterpret_cast<double *>(base + S.L.logits);
   K3_LAUNCH(fn, launch_router_shared(x, router_w, hidden, n_experts, lg, shared, n_shared,
                                      inter_shared, hs, stream));
-  K3_LAUNCH(fn, launch_shared_down(hs, shared, n_shared, hidden, inter_shared, ys, stream));
+  const SharedStage sh = {hs, shared, n_shared, inter_shared, ys};
   return layer_launches(fn, x, router_w, experts, n_experts, hidden, inter, k, y, y_f32,
-                        idx, w, lg, base, S.L, ys, stream, true);
+                        idx, w, lg, base, S.L, nullptr, stream, true, &sh);
 }
 
 k3_status k3_moe_layer_cached(const uint16_t *x, const uint16_t *router_w,

@@ -12,6 +12,7 @@
 // convention"). The work is a memory-bound stream of packed bytes ("the wait
 // is for bytes to arrive", [SAT] "Reduction one").
 #include "k3_stream.h"
+#include "k3_shared_row.h"
 #include "k3_sync.h"
 #include "k3_topk.h"
 
@@ -157,13 +158,23 @@ __global__ __launch_bounds__(kThreads) void gate_up_routed_kernel(
 // launch's ramp and the combine launch. Waits are bounded: if the device
 // cannot run the whole grid at once for about a second (another kernel
 // holding compute units), the call writes NaN rather than hang.
+//
+// kShared: the layer also has shared experts, whose h (hs) an earlier launch
+// computed. Between its gate/up and down stages every workgroup takes its
+// slice of the shared down rows (shared_down_row, the bits of the separate
+// shared-down launch), while its expert's h may still be on its way; their
+// sums ys go out device-coherent, and the combine adds them after the routed
+// rank-order sum. Without kShared, `add` (optional) is a finished vector
+// from an earlier launch.
+template <bool kShared>
 __global__ __launch_bounds__(kThreads) void moe_experts_kernel(
     const uint16_t *__restrict__ x, const double *__restrict__ logits,
     const uint8_t *const *__restrict__ experts, int n, int k, int hidden,
     int inter, float *h, float *yp, uint64_t *slots, uint64_t val,
     int32_t *__restrict__ idx_out, float *__restrict__ w_out,
     uint16_t *__restrict__ y, float *__restrict__ y_f32,
-    const float *__restrict__ add) {
+    const float *add, const float *__restrict__ hs,
+    const uint16_t *const *__restrict__ shared, int n_shared, int inter_s) {
   __shared__ float part[kPartFloats];
   __shared__ TopkWgLds tk;
   __shared__ int bad;
@@ -197,6 +208,14 @@ __global__ __launch_bounds__(kThreads) void moe_experts_kernel(
         part);
   }
   arrive(slots, val);
+  if constexpr (kShared) {
+    int r0, r1;
+    wg_range(hidden, &r0, &r1);
+    for (int r = r0 + wave_id(); r < r1; r += kNW) {
+      const float v = shared_down_row(hs, shared, n_shared, hidden, inter_s, r);
+      if (lane == 0) st_dev(const_cast<float *>(add) + r, v);
+    }
+  }
 
   const int Td = L.down.ntiles, total = k * Td;
   int t0, t1;
@@ -233,6 +252,11 @@ __global__ __launch_bounds__(kThreads) void moe_experts_kernel(
   for (int r = r_lo + wave_id(); r < r_hi; r += kNW) {
     const int owner = lane < k ? tile_owner(lane * Td + r, total, G) : 0;
     if (!wave_wait_owners(done, owner, k, val) && lane == 0) bad = 1;
+    if constexpr (kShared) {  // the workgroups that wrote these rows of ys
+      const int s_lo = tile_owner(r * kTileRows, hidden, G);
+      const int s_hi = tile_owner(min((r + 1) * kTileRows, hidden) - 1, hidden, G);
+      if (!wave_wait_range(done, s_lo, s_hi - s_lo + 1, val) && lane == 0) bad = 1;
+    }
     const int row = r * kTileRows + lane;
     if (row < hidden) {
       float acc = 0.f;
@@ -245,7 +269,10 @@ __global__ __launch_bounds__(kThreads) void moe_experts_kernel(
         for (int j = 0; j < 16; ++j)
           if (j0 + j < k) acc = fmaf(tk.wt[j0 + j], v[j], acc);
       }
-      if (add) acc += add[row];  // e.g. the shared experts' output
+      if (kShared)
+        acc += ld_dev(add + row);  // the shared experts' output, from this launch
+      else if (add)
+        acc += add[row];
       if (y_f32) y_f32[row] = acc;
       if (y) y[row] = f32_to_bf16_rne(acc);
     }
@@ -339,11 +366,16 @@ hipError_t launch_moe_experts(const uint16_t *x, const double *logits,
                               int hidden, int inter, float *h, float *yp,
                               uint64_t *slots, uint64_t val, int32_t *idx,
                               float *w, uint16_t *y, float *y_f32,
-                              hipStream_t s, const float *add) {
+                              hipStream_t s, const float *add, const SharedStage *sh) {
   // one workgroup per compute unit: the whole grid fits at once
-  hipLaunchKernelGGL(moe_experts_kernel, dim3(moe_experts_grid()),
-                     dim3(kThreads), 0, s, x, logits, experts, n, k, hidden,
-                     inter, h, yp, slots, val, idx, w, y, y_f32, add);
+  if (sh)
+    hipLaunchKernelGGL(moe_experts_kernel<true>, dim3(moe_experts_grid()), dim3(kThreads), 0,
+                       s, x, logits, experts, n, k, hidden, inter, h, yp, slots, val, idx, w,
+                       y, y_f32, sh->ys, sh->hs, sh->shared, sh->n_shared, sh->inter);
+  else
+    hipLaunchKernelGGL(moe_experts_kernel<false>, dim3(moe_experts_grid()), dim3(kThreads), 0,
+                       s, x, logits, experts, n, k, hidden, inter, h, yp, slots, val, idx, w,
+                       y, y_f32, add, nullptr, nullptr, 0, 0);
   return hipGetLastError();
 }
 

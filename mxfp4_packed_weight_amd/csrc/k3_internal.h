@@ -191,12 +191,21 @@ hipError_t launch_shared_down(const float *h, const uint16_t *const *shared, int
 // never reused in the process.
 constexpr int kMaxSyncGrid = 1024;
 unsigned moe_experts_grid();
+// The shared experts' down stage taken inside the expert launch: hs [n][inter]
+// from an earlier launch, ys [hidden] written here and added by the combine.
+struct SharedStage {
+  const float *hs;
+  const uint16_t *const *shared;
+  int n_shared, inter;
+  float *ys;
+};
 hipError_t launch_moe_experts(const uint16_t *x, const double *logits,
                               const uint8_t *const *experts, int n, int k,
                               int hidden, int inter, float *h, float *yp,
                               uint64_t *slots, uint64_t val, int32_t *idx,
                               float *w, uint16_t *y, float *y_f32,
-                              hipStream_t s, const float *add = nullptr);
+                              hipStream_t s, const float *add = nullptr,
+                              const SharedStage *sh = nullptr);
 // Calibration read of `bytes` (a multiple of 16) at `buf` (k3_probe.hip).
 hipError_t launch_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s);
 // Pinned host buffer of at least n ints owned by an expert cache

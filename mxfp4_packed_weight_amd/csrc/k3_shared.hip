@@ -11,18 +11,13 @@
 #include "k3_decode.h"
 #include "k3_internal.h"
 #include "k3_router.h"
+#include "k3_shared_row.h"
 
 namespace k3 {
 
 namespace {
 
 constexpr int kSharedWaves = 4;
-
-__device__ __forceinline__ float lanes_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
 
 // 8 bf16 weights (one 16-byte load) times 8 bf16 activations, added to acc
 // as four dot2 steps in order.
@@ -36,13 +31,6 @@ __device__ __forceinline__ float dot8_bf16(const uint4 w, const uint4 a, float a
   acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w),
                                         __builtin_bit_cast(bf16x2, a.w), acc, false);
   return acc;
-}
-
-typedef uint32_t u32v4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint4 ld16_nt(const uint16_t *p) {
-  const u32v4 v = __builtin_nontemporal_load(reinterpret_cast<const u32v4 *>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // Row gw = (shared expert s, h row i) of the gate/up stage, by one wave:
@@ -97,35 +85,15 @@ __global__ __launch_bounds__(64 * kSharedWaves) void router_shared_kernel(
   if (gw < n_shared * inter) shared_gate_up_row(x, shared, hidden, inter, gw, h);
 }
 
-// One wave per output row r: ys[r] = sum over s of W_down(s)[r] . h[s];
-// lane l takes columns 8l + 512m of every shared expert in turn (s
-// ascending, then m ascending), then the lanes are summed.
+// One wave per output row r: ys[r] = sum over s of W_down(s)[r] . h[s]
+// (shared_down_row, k3_shared_row.h).
 __global__ __launch_bounds__(64 * kSharedWaves) void shared_down_kernel(
     const float *__restrict__ h, const uint16_t *const *__restrict__ shared,
     int n_shared, int hidden, int inter, float *__restrict__ ys) {
   const int r = blockIdx.x * kSharedWaves + (threadIdx.x >> 6);
   if (r >= hidden) return;
-  const int lane = threadIdx.x & 63;
-  float acc = 0.f;
-  for (int s = 0; s < n_shared; ++s) {
-    const uint16_t *dr = shared[s] + (size_t)2 * inter * hidden + (size_t)r * inter;
-    const float4 *hv = reinterpret_cast<const float4 *>(h + (size_t)s * inter);
-#pragma unroll 2
-    for (int c8 = lane; 8 * c8 < inter; c8 += 64) {
-      const uint4 w = ld16_nt(dr + 8 * c8);
-      const float4 h0 = hv[2 * c8], h1 = hv[2 * c8 + 1];
-      acc = fmaf(__uint_as_float(w.x << 16), h0.x, acc);
-      acc = fmaf(__uint_as_float(w.x & 0xFFFF0000u), h0.y, acc);
-      acc = fmaf(__uint_as_float(w.y << 16), h0.z, acc);
-      acc = fmaf(__uint_as_float(w.y & 0xFFFF0000u), h0.w, acc);
-      acc = fmaf(__uint_as_float(w.z << 16), h1.x, acc);
-      acc = fmaf(__uint_as_float(w.z & 0xFFFF0000u), h1.y, acc);
-      acc = fmaf(__uint_as_float(w.w << 16), h1.z, acc);
-      acc = fmaf(__uint_as_float(w.w & 0xFFFF0000u), h1.w, acc);
-    }
-  }
-  acc = lanes_sum(acc);
-  if (lane == 0) ys[r] = acc;
+  const float acc = shared_down_row(h, shared, n_shared, hidden, inter, r);
+  if ((threadIdx.x & 63) == 0) ys[r] = acc;
 }
 
 }  // namespace
