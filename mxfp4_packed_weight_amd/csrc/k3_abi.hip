@@ -89,11 +89,12 @@ PermWs perm_ws(size_t off, long long P) {
 }
 
 // Batched layer: logits, idx, w, counts, offsets, pair_token, pair_slot,
-// the permutation scratch, h [P][inter], yp [P][hidden].
+// the permutation scratch, h [P][inter] (fp32, the one-token path), the bf16
+// pieces of h hp [3][P][inter], yp [P][hidden].
 struct BatchWs {
   size_t logits, idx, w, counts, offsets, pair_token, pair_slot;
   PermWs perm;
-  size_t h, yp, sync, total;
+  size_t h, hp, yp, sync, total;
 };
 BatchWs batch_ws(int T, int n, int hidden, int inter, int k) {
   BatchWs B;
@@ -117,6 +118,8 @@ BatchWs batch_ws(int T, int n, int hidden, int inter, int k) {
   off = B.perm.total;
   B.h = off;
   off += align256((size_t)P * inter * sizeof(float));
+  B.hp = off;
+  off += align256((size_t)3 * P * inter * sizeof(uint16_t));
   B.yp = off;
   off += align256((size_t)P * hidden * sizeof(float));
   B.sync = off;  // the single-token path's arrival slots (T == 1)
@@ -842,7 +845,7 @@ k3_status k3_moe_permute(const int32_t *idx, int T, int k, int n_experts,
   K3_LAUNCH(fn, launch_permute(idx, T, k, n_experts,
                                perm_out(base, W, counts, offsets, pair_token,
                                         pair_slot),
-                               tok_batch(), stream));
+                               gate_up_mfma_tok(), stream));
   return K3_OK;
 }
 
@@ -904,9 +907,12 @@ static k3_status batched_common(const char *fn, const uint16_t *X,
     return K3_OK;
   }
   K3_LAUNCH(fn, launch_topk_f64(logits, bias, T, n_experts, k, ix, wt, stream));
-  K3_LAUNCH(fn, launch_permute(ix, T, k, n_experts, o, tok_batch(), stream));
-  K3_LAUNCH(fn, launch_gate_up_batched(X, experts, o, hidden, inter, h, stream));
-  K3_LAUNCH(fn, launch_down_batched(h, experts, o, hidden, inter, yp, stream));
+  K3_LAUNCH(fn, launch_permute(ix, T, k, n_experts, o, gate_up_mfma_tok(), stream));
+  const long long P = (long long)T * k;
+  const int max_items = (int)(std::min<long long>(n_experts, P) + P / gate_up_mfma_tok() + 1);
+  uint16_t *hp = reinterpret_cast<uint16_t *>(base + B.hp);
+  K3_LAUNCH(fn, launch_gate_up_mfma(X, experts, o, max_items, P, hidden, inter, hp, stream));
+  K3_LAUNCH(fn, launch_down_mfma(hp, experts, o, max_items, P, hidden, inter, yp, stream));
   K3_LAUNCH(fn, launch_combine_batched(yp, wt, o.pair_pos, T, k, hidden, Y,
                                        Y_f32, stream));
   return K3_OK;

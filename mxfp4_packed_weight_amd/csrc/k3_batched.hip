@@ -1,41 +1,17 @@
-// Batched decode: token->expert permutation, per-expert grouped GEMVs that
-// read each selected expert's packed bytes once for all of its tokens, and
-// the per-token weighted combine.
+// Batched decode and prefill: the token->expert permutation and the
+// per-token weighted combine. (The grouped products: k3_batched_mfma.hip for
+// decode batches, k3_prefill.hip for prefill.)
 //
 // The T*k routing pairs (t, j) are sorted by expert, stably by pair index
 // (token, then slot), so every expert's tokens form one contiguous run. A
-// run is cut into work items of at most kTokBatch tokens; the grouped
-// kernels stream an item's expert tiles exactly like the single-token
-// kernels and multiply every decoded group by each of the item's tokens.
+// run is cut into work items of at most item_tok tokens, the column count of
+// the kernels that multiply them.
 #include "k3_stream.h"
 
 namespace k3 {
 
 namespace {
 
-// Grouped kernels: small workgroups, several per compute unit. Their
-// activations reach the waves through scalar loads that miss the scalar
-// cache (each item brings new tokens), so a wave stalls on them; small
-// workgroups let the stalled waves' neighbours run instead of holding a
-// 16-wave barrier, and about 10 workgroups per CU keep ~40 waves' loads
-// queued. Measured at 64 tokens (Zipf routing): 1.9x faster down and 1.3x
-// faster gate/up than one 16-wave workgroup per CU.
-#ifndef K3_BATCH_NW
-#define K3_BATCH_NW 4
-#endif
-#ifndef K3_BATCH_WG_PER_CU
-#define K3_BATCH_WG_PER_CU 10
-#endif
-constexpr int kBatchNW = K3_BATCH_NW;  // waves per workgroup, grouped kernels
-constexpr int kThreads = kBatchNW * 64;
-#ifndef K3_TOK_BATCH
-#define K3_TOK_BATCH 4
-#endif
-constexpr int kTokBatch = K3_TOK_BATCH;  // tokens per work item (accumulators per lane)
-#ifndef K3_BATCH_TPW
-#define K3_BATCH_TPW 2
-#endif
-constexpr int kBatchTPW = K3_BATCH_TPW;  // tiles per chunk of the grouped kernels
 constexpr int kPermThreads = 1024;
 
 // Inclusive prefix sum over the block's 1024 threads (wave scans + LDS).
@@ -174,125 +150,29 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
       __syncthreads();
     }
   }
-  // work items: ceil(cnt/item_tok) per expert, in expert order
-  int li = 0;
-  for (int e = e0; e < e1; ++e) li += (cnt[e] + item_tok - 1) / item_tok;
-  int ibase = block_scan_incl(li, tmp) - li;
-  for (int e = e0; e < e1; ++e) {
-    const int off = offsets[e];
-    for (int s = 0; s < cnt[e]; s += item_tok) {
-      item_e[ibase] = e;
-      item_off[ibase] = off + s;
-      item_cnt[ibase] = min(item_tok, cnt[e] - s);
-      ++ibase;
+  // work items: ceil(cnt/tok) per expert, in expert order
+  auto cut = [&](int tok, int32_t *ie, int32_t *ioff, int32_t *icnt, int32_t *ni) {
+    int li = 0;
+    for (int e = e0; e < e1; ++e) li += (cnt[e] + tok - 1) / tok;
+    int ibase = block_scan_incl(li, tmp) - li;
+    for (int e = e0; e < e1; ++e) {
+      const int off = offsets[e];
+      for (int s = 0; s < cnt[e]; s += tok) {
+        ie[ibase] = e;
+        ioff[ibase] = off + s;
+        icnt[ibase] = min(tok, cnt[e] - s);
+        ++ibase;
+      }
     }
-  }
-  if (tid == kPermThreads - 1) *n_items = ibase;
+    if (tid == kPermThreads - 1) *ni = ibase;
+  };
+  cut(item_tok, item_e, item_off, item_cnt, n_items);
   if (tid == 0) *n_bad = bad;
 }
 
 struct Items {
   const int32_t *e, *off, *cnt, *n;
 };
-
-// Routing data of the tile being multiplied, refreshed when the tile
-// changes: the item's first sorted pair, its token count and one activation
-// row pointer per token (all wave-uniform, read with scalar loads).
-template <typename A>
-struct TileRows {
-  int t = -1, off = 0, cnt = 0;
-  const A *row[kTokBatch];
-};
-
-// h[q][inter] = SiLU(gate . x_tok) * (up . x_tok) for every placed pair q,
-// tok = pair_token[q]; tiles: item i's gate/up tile s is virtual tile
-// i*T + s.
-__global__ __launch_bounds__(kThreads) void gate_up_batched_kernel(
-    const uint16_t *__restrict__ X, const uint8_t *const *__restrict__ experts,
-    Items it, const int32_t *__restrict__ pair_token, int hidden, int inter,
-    float *__restrict__ h) {
-  __shared__ float part[kBatchTPW * kBatchNW * 64 * kTokBatch];
-  const ExpertLayout L = expert_layout(hidden, inter);
-  const int T = L.gu.ntiles;
-  const int total = ldc(it.n) * T;
-  int t0, t1;
-  wg_range(total, &t0, &t1);
-  const uint32_t *Xw = reinterpret_cast<const uint32_t *>(X);
-  const int xrow = hidden / 2;  // uint32 words per token row
-  TileRows<uint32_t> cr;        // consumer side
-  auto rows = [&](int t) {
-    if (t == cr.t) return;
-    cr.t = t;
-    const int i = t / T;
-    cr.off = ldc(it.off + i);
-    cr.cnt = ldc(it.cnt + i);
-#pragma unroll
-    for (int v = 0; v < kTokBatch; ++v) {
-      const int tok = v < cr.cnt ? ldc(pair_token + cr.off + v) : 0;
-      cr.row[v] = Xw + (size_t)tok * xrow;
-    }
-  };
-  run_rows_n<kTokBatch, kBatchTPW, kBatchNW>(
-      t0, t1, L.gu.G, L.gu.G4,
-      [&](int t) {
-        return ldc(experts + ldc(it.e + t / T)) + (size_t)(t % T) * L.gu.tile_bytes;
-      },
-      [&](int t) { return ldc(it.cnt + t / T); },
-      [&](u32x4 w, int g, int t, int n, float(&sub)[kTokBatch]) {
-        rows(t);
-        const GroupBf16 G = decode_bf16(w);
-#pragma unroll
-        for (int v = 0; v < kTokBatch; ++v)
-          sub[v] = v < n ? dot_decoded(G, cr.row[v] + (size_t)16 * g) : 0.f;
-      },
-      [&](int t, int v, int lane, float s) {
-        const float u = __shfl_down(s, 32);  // lane l<32: gate row; l+32: up row
-        int is_up, row;
-        gu_lane_row(t % T, lane, &is_up, &row);
-        const int q = ldc(it.off + t / T) + v;
-        if (lane < 32 && row < inter) h[(size_t)q * inter + row] = silu(s) * u;
-      },
-      part);
-}
-
-// yp[q][hidden] = W_down(e) h[q] for every placed pair q of expert e.
-__global__ __launch_bounds__(kThreads) void down_batched_kernel(
-    const float *__restrict__ h, const uint8_t *const *__restrict__ experts,
-    Items it, int hidden, int inter, float *__restrict__ yp) {
-  __shared__ float part[kBatchTPW * kBatchNW * 64 * kTokBatch];
-  const ExpertLayout L = expert_layout(hidden, inter);
-  const int T = L.down.ntiles;
-  const int total = ldc(it.n) * T;
-  int t0, t1;
-  wg_range(total, &t0, &t1);
-  int ct = -1;
-  const float *hrow[kTokBatch];  // activation rows of the consumer's tile
-  run_rows_n<kTokBatch, kBatchTPW, kBatchNW>(
-      t0, t1, L.down.G, L.down.G4,
-      [&](int t) {
-        return ldc(experts + ldc(it.e + t / T)) + L.down_offset +
-               (size_t)(t % T) * L.down.tile_bytes;
-      },
-      [&](int t) { return ldc(it.cnt + t / T); },
-      [&](u32x4 w, int g, int t, int n, float(&sub)[kTokBatch]) {
-        if (t != ct) {
-          ct = t;
-          const size_t coff = (size_t)ldc(it.off + t / T);
-#pragma unroll
-          for (int v = 0; v < kTokBatch; ++v) hrow[v] = h + (coff + v) * inter;
-        }
-        const GroupF32 G = decode_f32(w);
-#pragma unroll
-        for (int v = 0; v < kTokBatch; ++v)
-          sub[v] = v < n ? dot_decoded(G, hrow[v] + (size_t)32 * g) : 0.f;
-      },
-      [&](int t, int v, int lane, float s) {
-        const int row = (t % T) * kTileRows + lane;
-        const size_t q = (size_t)ldc(it.off + t / T) + v;
-        if (row < hidden) yp[q * hidden + row] = s;
-      },
-      part);
-}
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -336,11 +216,7 @@ __global__ __launch_bounds__(256) void combine_batched_kernel(
   }
 }
 
-unsigned persistent_grid() { return (unsigned)(num_cus() * K3_BATCH_WG_PER_CU); }
-
 }  // namespace
-
-int tok_batch() { return kTokBatch; }
 
 hipError_t launch_permute(const int32_t *idx, int T, int k, int n,
                           const PermOut &o, int item_tok, hipStream_t s) {
@@ -348,26 +224,6 @@ hipError_t launch_permute(const int32_t *idx, int T, int k, int n,
                      k, n, o.counts, o.offsets, o.pair_token, o.pair_slot,
                      o.pair_pos, o.item_e, o.item_off, o.item_cnt, o.n_items,
                      o.n_bad, item_tok);
-  return hipGetLastError();
-}
-
-hipError_t launch_gate_up_batched(const uint16_t *X,
-                                  const uint8_t *const *experts,
-                                  const PermOut &o, int hidden, int inter,
-                                  float *h, hipStream_t s) {
-  const Items it{o.item_e, o.item_off, o.item_cnt, o.n_items};
-  hipLaunchKernelGGL(gate_up_batched_kernel, dim3(persistent_grid()),
-                     dim3(kThreads), 0, s, X, experts, it, o.pair_token,
-                     hidden, inter, h);
-  return hipGetLastError();
-}
-
-hipError_t launch_down_batched(const float *h, const uint8_t *const *experts,
-                               const PermOut &o, int hidden, int inter,
-                               float *yp, hipStream_t s) {
-  const Items it{o.item_e, o.item_off, o.item_cnt, o.n_items};
-  hipLaunchKernelGGL(down_batched_kernel, dim3(persistent_grid()),
-                     dim3(kThreads), 0, s, h, experts, it, hidden, inter, yp);
   return hipGetLastError();
 }
 

@@ -111,16 +111,18 @@ struct PermOut {
   int32_t *counts, *offsets, *pair_token, *pair_slot, *pair_pos;
   int32_t *item_e, *item_off, *item_cnt, *n_items, *n_bad;
 };
-int tok_batch();
 hipError_t launch_permute(const int32_t *idx, int T, int k, int n,
                           const PermOut &o, int item_tok, hipStream_t s);
-hipError_t launch_gate_up_batched(const uint16_t *X,
-                                  const uint8_t *const *experts,
-                                  const PermOut &o, int hidden, int inter,
-                                  float *h, hipStream_t s);
-hipError_t launch_down_batched(const float *h, const uint8_t *const *experts,
-                               const PermOut &o, int hidden, int inter,
-                               float *yp, hipStream_t s);
+// Batched gate/up and down on the matrix unit, over items of at most
+// gate_up_mfma_tok() tokens; X 16-byte aligned. hp: the three bf16 pieces
+// of h, [3][P][inter]; yp [P][hidden] fp32.
+int gate_up_mfma_tok();
+hipError_t launch_gate_up_mfma(const uint16_t *X, const uint8_t *const *experts,
+                               const PermOut &o, int max_items, long long P, int hidden,
+                               int inter, uint16_t *hp, hipStream_t s);
+hipError_t launch_down_mfma(const uint16_t *hp, const uint8_t *const *experts, const PermOut &o,
+                            int max_items, long long P, int hidden, int inter, float *yp,
+                            hipStream_t s);
 hipError_t launch_combine_batched(const float *yp, const float *w,
                                   const int32_t *pair_pos, int T, int k,
                                   int hidden, uint16_t *Y, float *Y32,

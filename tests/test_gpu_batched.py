@@ -120,8 +120,11 @@ def check_tokens(out, X, logits, experts_of, k, hidden, inter, tokens):
     return max(errs)
 
 
+# hidden 800: 25 groups (a last quad of one group) and K long enough for the
+# matrix-unit gate/up's steady loop; inter 96: 3 gate/up tiles (a padding wave)
 @pytest.mark.parametrize("n,hidden,inter,k,T", [(24, 256, 128, 4, 10), (13, 96, 160, 13, 5),
-                                                (40, 512, 96, 16, 33), (9, 128, 64, 1, 70)])
+                                                (40, 512, 96, 16, 33), (9, 128, 64, 1, 70),
+                                                (12, 800, 96, 4, 40)])
 def test_batched_from_logits_small(n, hidden, inter, k, T):
     cfg, seed = 71, 4
     say(f"batched from logits n={n} hidden={hidden} inter={inter} k={k} T={T}")
@@ -133,6 +136,59 @@ def test_batched_from_logits_small(n, hidden, inter, k, T):
                        lambda e: W.expert_weights(seed, cfg, e, hidden, inter, 114, 120),
                        k, hidden, inter, range(T))
     say(f"batched small: max normwise {err:.3e}")
+
+
+def _edge_exponent_expert(seed, cfg, e, hidden, inter, xmax_col):
+    """An expert whose gate/up and down exponent bytes include 0, 1, 2 and
+    255 at random places, and gate rows 0, 1 and 2 with exponent bytes 253, 254 and
+    252 on a group holding a single code 0.5, at the column whose
+    activations are smallest (xmax_col: max |x| per column), so that every
+    product and sum stays finite in fp32."""
+    E = W.expert_weights(seed, cfg, e, hidden, inter, 114, 120)
+    rng = np.random.default_rng(1000 + e)
+    c = int(np.argmin(xmax_col))
+    g, j = c // 32, c % 32
+    for part in ("gate", "up"):
+        nib, sc = E[part]
+        nib, sc = nib.copy(), sc.copy()
+        rows, G = sc.shape
+        hit = rng.random((rows, G)) < 0.08
+        sc[hit] = rng.choice(np.array([0, 1, 2, 255], np.uint8), int(hit.sum()))
+        if part == "gate":
+            for r, ex in ((0, 253), (1, 254), (2, 252)):
+                nib[r, 16 * g:16 * g + 16] = 0
+                nib[r, 16 * g + j // 2] = 0x01 << (4 * (j % 2))  # element j: code 1 (0.5)
+                sc[r, g] = ex
+        E[part] = (nib, sc)
+    nib, sc = E["down"]
+    sc = sc.copy()
+    hit = rng.random(sc.shape) < 0.08
+    sc[hit] = rng.choice(np.array([0, 1, 2, 255], np.uint8), int(hit.sum()))
+    E["down"] = (nib, sc)
+    return E
+
+
+def test_batched_edge_exponents():
+    """Exponent bytes outside 2..252 (the matrix-unit stages' exact route)
+    and 255 (skipped groups), at a K that runs the steady loop."""
+    import torch
+    from mxfp4_packed_weight_amd.pool import ExpertPool
+    from tests import _independent as I
+    cfg, seed, n, hidden, inter, k, T = 74, 8, 6, 1024, 128, 3, 20
+    say(f"batched edge exponents n={n} hidden={hidden} inter={inter} k={k} T={T}")
+    X = W.tokens_bf16(seed, cfg, T, hidden)
+    xmax_col = np.abs(I.bf16_to_float_bits(X.reshape(-1)).reshape(T, hidden)).max(axis=0)
+    assert xmax_col.min() < 2.0  # 2^127 * 0.5 * max|x| stays below the fp32 maximum
+    pool = ExpertPool(n, hidden, inter)
+    ex = {e: _edge_exponent_expert(seed, cfg, e, hidden, inter, xmax_col) for e in range(n)}
+    for e in range(n):
+        pool.load(e, ex[e])
+    torch.cuda.synchronize()
+    logits = W.zipf_router_logits(seed, T, n, 1.1, cfg).astype(np.float64)
+    out = run_batched(pool, X, n, hidden, inter, k, logits=logits)
+    assert np.all(np.isfinite(out["Y32"]))
+    err = check_tokens(out, X, logits, lambda e: ex[e], k, hidden, inter, range(T))
+    say(f"batched edge exponents: max normwise {err:.3e}")
 
 
 def test_batched_router_path_small():
