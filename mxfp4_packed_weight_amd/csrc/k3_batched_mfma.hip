@@ -96,14 +96,19 @@ struct BmItems {
 // SiLU(gate . x_tok) * (up . x_tok) for the pairs q of every work item, tok =
 // pair_token[q]; tile rows 0..31 are gate rows, 32..63 the up rows of the
 // same 32 outputs. kDown = true: yp[q][hidden] = W_down(e) h[q], h read as
-// its pieces hp.
-template <bool kDown>
+// its pieces hp, by one of two launches: NP = 3 takes the items of more than
+// kPackTok pairs (one instruction per piece); NP = 1 the others, whose
+// (pair, piece) combinations fit the 16 columns of one instruction (column
+// p * cnt + t holds piece p of pair t), the pieces' sums added at the end.
+constexpr int kPackTok = 5;  // 3 * 5 <= 16 columns
+template <bool kDown, int NP>
 __global__ __launch_bounds__(kBmWaves * 64) void batched_mfma_kernel(
     const uint16_t *__restrict__ X, const int32_t *__restrict__ pair_token,
     const uint8_t *const *__restrict__ experts, BmItems it, int hidden, int inter,
     long long P, uint16_t *__restrict__ hp, float *__restrict__ yp) {
-  constexpr int NP = kDown ? kPieces : 1;              // B pieces
-  constexpr int kDepth = kDown ? 3 : 4;                // weight quads in flight per wave
+  static_assert(NP == 1 || (kDown && NP == kPieces), "B pieces per instruction");
+  constexpr bool kPacked = kDown && NP == 1;
+  constexpr int kDepth = NP == 1 ? 4 : 3;              // weight quads in flight per wave
   constexpr int LB = NP;                               // activation loads per quad
   __shared__ u32x4 bl[kBmBDepth][NP][kBmWaves][64];    // B of one quad: group w, lane order
   __shared__ __attribute__((aligned(16))) uint8_t ring[kBmWaves][kDepth][kQuadBytes];
@@ -116,16 +121,25 @@ __global__ __launch_bounds__(kBmWaves * 64) void batched_mfma_kernel(
   const int item = u / ngrp, s = kBmWaves * (u % ngrp) + wave;
   const bool active = s < Tt;  // else: streams tile Tt - 1, stores nothing
   const int e = ldc(it.e + item), off = ldc(it.off + item), cnt = ldc(it.cnt + item);
+  if (kDown && (cnt <= kPackTok) != kPacked) return;  // the other launch's item
   const uint8_t *tile = ldc(experts + e) + (kDown ? L.down_offset : 0) +
                         (size_t)(active ? s : Tt - 1) * M.tile_bytes;
   const int G = M.G, G4 = M.G4;
   const int lane = threadIdx.x & 63, col = lane & 15, kb = lane >> 4;
   // the activation row of this lane's column (a column past the item reads
   // the item's first row; its results are never stored): x of its token, or
-  // the first piece of its pair's h (piece p is p * P rows further)
-  const int c = off + (col < cnt ? col : 0);
-  const uint16_t *brow = kDown ? hp + (size_t)c * inter : X + (size_t)pair_token[c] * hidden;
+  // the first piece of its pair's h (piece p is p * P rows further); packed:
+  // column p * cnt + t is piece p of pair t
   const size_t pstride = (size_t)P * inter;
+  const uint16_t *brow;
+  if constexpr (kPacked) {
+    const bool used = col < kPieces * cnt;
+    const int t = used ? col % cnt : 0, pc = used ? col / cnt : 0;
+    brow = hp + pc * pstride + (size_t)(off + t) * inter;
+  } else {
+    const int c = off + (col < cnt ? col : 0);
+    brow = kDown ? hp + (size_t)c * inter : X + (size_t)pair_token[c] * hidden;
+  }
 
   u32x4 b[kBmBDepth][NP];
   auto load_a = [&](int slot, int q) __attribute__((always_inline)) {
@@ -315,6 +329,16 @@ __global__ __launch_bounds__(kBmWaves * 64) void batched_mfma_kernel(
     }
   }
 
+  if constexpr (kPacked) {  // column t += columns cnt + t and 2 cnt + t (same lane group)
+    const int src1 = min(lane + cnt, 63), src2 = min(lane + 2 * cnt, 63);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v1 = __shfl(acc[m][i], src1), v2 = __shfl(acc[m][i], src2);
+        acc[m][i] = (acc[m][i] + v1) + v2;
+      }
+  }
   if (!active || col >= cnt) return;  // padding wave, or a column past the item
   const size_t q = (size_t)(off + col);
   if constexpr (kDown) {
@@ -355,7 +379,7 @@ hipError_t launch_gate_up_mfma(const uint16_t *X, const uint8_t *const *experts,
   const ExpertLayout L = expert_layout(hidden, inter);
   const BmItems it{o.item_e, o.item_off, o.item_cnt, o.n_items};
   const long long ngrp = (L.gu.ntiles + kBmWaves - 1) / kBmWaves;
-  hipLaunchKernelGGL(batched_mfma_kernel<false>, dim3((unsigned)(max_items * ngrp)),
+  hipLaunchKernelGGL((batched_mfma_kernel<false, 1>), dim3((unsigned)(max_items * ngrp)),
                      dim3(kBmWaves * 64), 0, s, X, o.pair_token, experts, it, hidden, inter, P,
                      hp, nullptr);
   return hipGetLastError();
@@ -367,7 +391,13 @@ hipError_t launch_down_mfma(const uint16_t *hp, const uint8_t *const *experts, c
   const ExpertLayout L = expert_layout(hidden, inter);
   const BmItems it{o.item_e, o.item_off, o.item_cnt, o.n_items};
   const long long ngrp = (L.down.ntiles + kBmWaves - 1) / kBmWaves;
-  hipLaunchKernelGGL(batched_mfma_kernel<true>, dim3((unsigned)(max_items * ngrp)),
+  // items of at most kPackTok pairs, then the others
+  hipLaunchKernelGGL((batched_mfma_kernel<true, 1>), dim3((unsigned)(max_items * ngrp)),
+                     dim3(kBmWaves * 64), 0, s, nullptr, o.pair_token, experts, it, hidden, inter,
+                     P, const_cast<uint16_t *>(hp), yp);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((batched_mfma_kernel<true, kPieces>), dim3((unsigned)(max_items * ngrp)),
                      dim3(kBmWaves * 64), 0, s, nullptr, o.pair_token, experts, it, hidden, inter,
                      P, const_cast<uint16_t *>(hp), yp);
   return hipGetLastError();
