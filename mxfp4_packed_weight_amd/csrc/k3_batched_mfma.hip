@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kBmWaves * 64) void batched_mfma_kernel(
     long long P, uint16_t *__restrict__ hp, float *__restrict__ yp) {
   static_assert(NP == 1 || (kDown && NP == kPieces), "B pieces per instruction");
   constexpr bool kPacked = kDown && NP == 1;
-  constexpr int kDepth = NP == 1 ? 4 : 3;              // weight quads in flight per wave
+  constexpr int kDepth = NP == 1 ? 2 : 3;  // weight quads in flight per wave
   constexpr int LB = NP;                               // activation loads per quad
   __shared__ u32x4 bl[kBmBDepth][NP][kBmWaves][64];    // B of one quad: group w, lane order
   __shared__ __attribute__((aligned(16))) uint8_t ring[kBmWaves][kDepth][kQuadBytes];
