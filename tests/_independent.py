@@ -120,3 +120,30 @@ def read_census():
             tok = line.split()
             out[tok[0]] = float(tok[1])
     return out
+
+
+def bf16_nearest_even_bits(u32):
+    """bf16 bits nearest to the float32 with bits u32, ties to the even
+    pattern, by exact rational comparison of the two bf16 neighbours.
+    Overflow follows IEEE 754 round-to-nearest: the value past the largest
+    finite bf16 is taken as 2^128, so ties there go to the infinity (whose
+    mantissa is even). NaN inputs are not handled here."""
+    u32 = int(u32) & 0xFFFFFFFF
+    sign = u32 >> 31
+    mag_bits = u32 & 0x7FFFFFFF
+    if mag_bits == 0x7F800000:
+        return (sign << 15) | 0x7F80
+    v = abs(Fraction(float(np.array([mag_bits], np.uint32).view(np.float32)[0])))
+    lo = mag_bits >> 16                   # toward zero
+
+    def val(b):
+        if b >= 0x7F80:
+            return Fraction(2) ** 128
+        return abs(Fraction(float(np.array([b << 16], np.uint32).view(np.float32)[0])))
+
+    d_lo, d_hi = v - val(lo), val(lo + 1) - v
+    if d_lo < d_hi or (d_lo == d_hi and lo % 2 == 0):
+        out = lo
+    else:
+        out = lo + 1
+    return (sign << 15) | min(out, 0x7F80)

@@ -375,6 +375,78 @@ def check_permute(O, seed=17):
             assert idx[t, j] == e
 
 
+def _bits_to_f32(u):
+    return np.array(u, np.uint32).view(np.float32)
+
+
+def check_bf16_rne(O, seed=41):
+    """The fp32 -> bf16 cast of the layer's output is round to nearest, ties
+    to even. Pinned by exact rational comparison of the two bf16 neighbours
+    (tests/_independent.py) on hand-picked ties and their neighbours, signed
+    zeros, infinities, NaN and the overflow edge, and by torch's CPU bf16
+    conversion on random bit patterns."""
+    fixed = [0x3F808000, 0x3F818000, 0x3F808001, 0x3F807FFF, 0x3F818001, 0x3F817FFF,
+             0xBF808000, 0xBF818000, 0x00000000, 0x80000000, 0x7F800000, 0xFF800000,
+             0x7F7FFFFF, 0x7F7F8000, 0x7F7F7FFF, 0xFF7F8000, 0x7F7E8000, 0x00008000,
+             0x00018000, 0x00017FFF, 0x0000FFFF, 0x007F8000, 0x3F800000, 0x4B7FFF80]
+    rnd = gen.random_bytes(gen.key(seed, 87, gen.KIND_MATRIX), 4 * 6000).view(np.uint32)
+    ties = (rnd[:2000] & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    near = np.concatenate([ties + np.uint32(1), ties - np.uint32(1)])
+    pats = np.concatenate([np.array(fixed, np.uint32), ties, near, rnd[2000:]])
+    f = _bits_to_f32(pats)
+    finite = ~np.isnan(f)
+    got = O.f32_to_bf16(f).astype(np.uint32)
+    for u, g in zip(pats[:len(fixed) + 400], got[:len(fixed) + 400]):
+        if np.isnan(_bits_to_f32(u)):
+            continue
+        assert g == I.bf16_nearest_even_bits(int(u)), (hex(int(u)), hex(int(g)))
+    import torch
+    want = torch.from_numpy(f[finite].copy()).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(got[finite].astype(np.uint16), want.view(np.uint16))
+    # NaN stays NaN of the same sign
+    nan_in = _bits_to_f32(np.array([0x7FC00000, 0xFFC00001, 0x7F800001, 0x7FFFFFFF], np.uint32))
+    nb = O.f32_to_bf16(nan_in).astype(np.uint32)
+    for u, g in zip([0x7FC00000, 0xFFC00001, 0x7F800001, 0x7FFFFFFF], nb):
+        assert (g & 0x7F80) == 0x7F80 and (g & 0x7F) != 0, hex(int(g))
+        assert (g >> 15) == (u >> 31)
+
+
+def check_moe_from_logits(O, seed=34):
+    """The batched oracle: T tokens routed from given logits rows (with a
+    routing bias) equal T separate one-token calls bit for bit, and each
+    token equals an independent numpy route (key sigma(l) + b sorted by
+    Python, unbiased renormalised weights, experts expanded and multiplied
+    by numpy)."""
+    n, hidden, inter, k, T = 12, 128, 64, 3, 4
+    X = gen.normal_bf16(gen.key(seed, 86, gen.KIND_TOKENS), T * hidden).reshape(T, hidden)
+    L = gen.normal_f32(gen.key(seed, 86, gen.KIND_LOGITS), T * n).reshape(T, n).astype(np.float64)
+    L[2] = -L[1]               # makes tokens 1 and 2 pick different sets
+    bias = np.linspace(-0.2, 0.3, n)
+    experts = {e: gen.expert(seed, 86, e, hidden, inter, 114, 120) for e in range(n)}
+    Y, idx, w = O.moe_from_logits(X, L, experts, k, hidden, inter, bias=bias)
+    assert len({tuple(sorted(r)) for r in idx.tolist()}) >= 3, idx
+    for t in range(T):
+        y1, i1, w1 = O.moe_from_logits(X[t:t + 1], L[t:t + 1], experts, k, hidden, inter,
+                                       bias=bias)
+        assert np.array_equal(Y[t], y1[0]) and np.array_equal(idx[t], i1[0])
+        assert np.array_equal(w[t], w1[0])
+        key = [I.sigmoid(L[t, e]) + bias[e] for e in range(n)]
+        order = sorted(range(n), key=lambda e: (-key[e], e))[:k]
+        assert list(idx[t]) == order, (t, idx[t], order)
+        s = np.array([I.sigmoid(L[t, e]) for e in order])
+        wi = s / s.sum()
+        assert np.max(np.abs(w[t] - wi)) <= 1e-15
+        xf = I.bf16_to_float_bits(X[t])
+        yy = np.zeros(hidden)
+        for j, e in enumerate(order):
+            Ex = experts[e]
+            g = I.dequant_numpy(*Ex["gate"]) @ xf
+            u = I.dequant_numpy(*Ex["up"]) @ xf
+            h = np.array([I.silu_tanh_form(a) for a in g]) * u
+            yy += wi[j] * (I.dequant_numpy(*Ex["down"]) @ h)
+        assert np.max(np.abs(Y[t] - yy)) <= 1e-12 * np.max(np.abs(yy)), t
+
+
 ALL = [check_e2m1_table, check_e8m0, check_golden_nibble_order, check_bruteforce_4x32,
        check_all_scale_bytes, check_exact_rational, check_exact_dyadic, check_scale_shift,
        check_nan_containment, check_dequant_crosscheck, check_expert_crosscheck, check_silu,
@@ -382,4 +454,4 @@ ALL = [check_e2m1_table, check_e8m0, check_golden_nibble_order, check_bruteforce
        check_topk_bias_selects_only, check_combine, check_moe_layer_small,
        check_quant_ties_and_saturation, check_quant_invariants, check_quant_roundtrip,
        check_matmul, check_permute, check_shared_expert_crosscheck, check_shared_expert_by_hand,
-       check_layer_shared_adds]
+       check_layer_shared_adds, check_bf16_rne, check_moe_from_logits]

@@ -44,6 +44,12 @@ MUTANTS = {
                          "(void)ys;"),
     "combine_drops_rank0": ("for (int j = 0; j < k; j++) acc += w[j] * ye[(size_t)j * hidden + i];",
                             "for (int j = 1; j < k; j++) acc += w[j] * ye[(size_t)j * hidden + i];"),
+    "bf16_ties_away": ("if (lo > 0x8000u || (lo == 0x8000u && (hi & 1u))) r = hi + 1u;",
+                       "if (lo >= 0x8000u) r = hi + 1u;"),
+    "bf16_truncation": ("if (lo > 0x8000u || (lo == 0x8000u && (hi & 1u))) r = hi + 1u;",
+                        "(void)lo;"),
+    "logits_offset_ignored": ("logits + (size_t)t * n_experts, bias, experts,",
+                              "logits, bias, experts,"),
 }
 
 
