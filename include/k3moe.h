@@ -7,8 +7,14 @@
  * caller owns every buffer, including the workspace. Compute calls validate
  * all arguments on the host before anything is enqueued (on error nothing is
  * launched), then enqueue asynchronously on `stream` and never synchronise.
- * Calls on different streams with different outputs and workspaces may run
- * concurrently.
+ * Calls on different streams with different outputs and workspaces may be
+ * issued concurrently, from any host threads. The decode layer's expert
+ * launch (k3_moe_layer, _ex, _shared, _cached, and k3_moe_layer_from_logits
+ * with T = 1 and no bias) needs its whole grid resident at once, so the
+ * library orders those launches on one device: one issued on another stream
+ * than the device's previous one waits, on the device, for that previous
+ * launch to finish (an event recorded after every such launch). Every other
+ * launch may overlap with anything.
  *
  * Sources (web pages describing the kimi-k3-in-c engine), cited below as:
  *  [A176] "kimi-k3-in-c: A 176 KB Engine That Runs a 2.78T-Parameter MoE in
@@ -36,8 +42,10 @@
  * k3_last_error; nothing is defaulted, following the pages' config reader
  * that refuses to guess, [A176] "What byte-identical actually costs");
  * K3_ERR_MEMORY when the workspace is smaller than the call needs (the
- * message gives both sizes: a memory limit, not an engine ceiling, [A176]
- * "The interesting design decisions"); K3_ERR_DEVICE when the HIP runtime
+ * message gives both sizes, so the caller sees that more memory, not a
+ * different configuration, would serve the call; the pages report memory
+ * budgets the same way, [A176] "The interesting design decisions");
+ * K3_ERR_DEVICE when the HIP runtime
  * reports a launch or runtime error.
  */
 #ifndef K3MOE_H
@@ -214,10 +222,11 @@ k3_status k3_router_topk_f32(const float *logits, const float *bias, int T,
  * must not overlap). Its bits equal those of the stage-by-stage calls below
  * (k3_expert_gate_up_routed, k3_expert_down, k3_moe_combine), which are
  * what the layer runs while the stream is being captured into a graph or
- * for n_experts > 1024. Its internal waits are bounded: if the device
- * cannot run its whole grid at once for about a second (another kernel
- * holding compute units), it writes NaN to y_f32 and 0x7FC0 (bf16 NaN) to y
- * instead of hanging.
+ * for n_experts > 1024. Two such expert launches never overlap (see the top
+ * of this file). Its internal waits are bounded: if the device cannot run
+ * its whole grid at once for about a second (a kernel of another library,
+ * on another stream, holding compute units all that time), it writes NaN
+ * to y_f32 and 0x7FC0 (bf16 NaN) to y instead of hanging.
  * ---------------------------------------------------------------------- */
 size_t k3_moe_workspace_bytes(int T, int n_experts, int hidden, int inter,
                               int k);

@@ -278,7 +278,7 @@ const char *k3_strerror(k3_status s) {
     case K3_ERR_ARG: return "invalid argument (NULL or misaligned pointer)";
     case K3_ERR_CONFIG: return "unsupported or contradictory configuration";
     case K3_ERR_MEMORY:
-      return "workspace too small: a memory limit, not an engine ceiling";
+      return "insufficient memory: the workspace or the cache slots given are smaller than the call needs";
     case K3_ERR_DEVICE: return "HIP runtime error";
     default: return "unknown status";
   }
@@ -376,7 +376,7 @@ static k3_status need_ws(const char *fn, size_t have, size_t need) {
   if (have < need)
     return fail(K3_ERR_MEMORY,
                 "%s: workspace of %zu bytes is below the %zu bytes this call "
-                "needs; this is a memory limit, not an engine ceiling",
+                "needs (give a larger workspace; no size limit of the path is reached)",
                 fn, have, need);
   return K3_OK;
 }

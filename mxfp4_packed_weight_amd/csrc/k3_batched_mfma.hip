@@ -22,11 +22,13 @@
 // group (32 codes), so a group's exponent applies to whole A rows: the codes
 // are converted to bf16 with the group scale folded in (exact for exponent
 // bytes 2..252: the largest code times 2^125 and the smallest nonzero one
-// times 2^-125 are normal bf16), and exponent byte 255 zeroes the group, as
-// elsewhere ([A176] "What byte-identical actually costs"). A quad that holds
-// any other exponent byte (0, 1, 253 or 254) in this wave's tile takes the
-// exact route instead: each group's unscaled sum from its own instructions,
-// then scaled into the accumulator with ldexp, as the vector kernels do.
+// times 2^-125 are normal bf16). A quad that holds any other exponent byte
+// (0, 1, 253, 254 or 255) in this wave's tile takes the exact route instead:
+// each group's unscaled sum from its own instructions, then scaled into the
+// accumulator with ldexp, as the vector kernels do. There a group with byte
+// 255 is skipped, not multiplied by zero, so a NaN or infinite activation
+// inside it does not reach the row ([A176] "What byte-identical actually
+// costs").
 //
 // Gate/up multiplies bf16 x, which is exact in bf16. Down multiplies h, which
 // is fp32: the gate/up epilogue writes it as three bf16 pieces whose sum is
@@ -68,9 +70,12 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 }
 
 // The three bf16 pieces of v (their fp32 sum is v; a non-finite v is all in
-// the first piece).
+// the first piece). A finite v that rounds to a bf16 infinity (|v| within
+// half a bf16 step of FLT_MAX) takes its first piece rounded toward zero
+// instead, which keeps every piece finite and the residuals exact.
 __device__ __forceinline__ void split3(float v, uint16_t &p0, uint16_t &p1, uint16_t &p2) {
   p0 = f32_to_bf16_rne(v);
+  if (__builtin_isfinite(v) && (p0 & 0x7F80u) == 0x7F80u) p0 = (uint16_t)(__float_as_uint(v) >> 16);
   const float r1 = v - __uint_as_float((uint32_t)p0 << 16);
   p1 = f32_to_bf16_rne(r1);
   const float r2 = r1 - __uint_as_float((uint32_t)p1 << 16);
@@ -210,13 +215,13 @@ __global__ __launch_bounds__(kBmWaves * 64) void batched_mfma_kernel(
           : "memory");
     }
     // word of (m, g): aw[2m + g/2][g%2]
-    bool odd = false;  // an exponent byte the folded scale cannot take
+    bool odd = false;  // an exponent byte the folded scale cannot take, or 255
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const uint32_t ex = (sr[m] >> (8 * g)) & 255u;
-        odd |= ex - 2u > 250u && ex != 255u;
+        odd |= ex - 2u > 250u;
       }
     if (__ballot(odd) == 0) {
 #pragma unroll
@@ -224,9 +229,8 @@ __global__ __launch_bounds__(kBmWaves * 64) void batched_mfma_kernel(
         if (4 * q + g < G) {  // wave-uniform
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
-            const uint32_t ex = (sr[m] >> (8 * g)) & 255u;
-            const uint32_t w = ex == 255u ? 0u : aw[2 * m + g / 2][g % 2];
-            const v8bf a = decode8(w, __uint_as_float((ex == 255u ? 127u : ex) << 23));
+            const uint32_t ex = (sr[m] >> (8 * g)) & 255u;  // 2..252 here
+            const v8bf a = decode8(aw[2 * m + g / 2][g % 2], __uint_as_float(ex << 23));
 #pragma unroll
             for (int p = 0; p < NP; ++p)
               acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv[p][g], acc[m], 0, 0, 0);

@@ -331,7 +331,7 @@ k3_status k3_cache_fetch(k3_cache_t c, const int32_t *ids, int count,
   };
   if (!c->pol.plan(ids, count, done, &acts))
     return (set_error("%s: %d slots cannot hold this request beside the pinned "
-                      "experts; this is a memory limit, not an engine ceiling",
+                      "experts (a cache with more slots would serve it)",
                       fn, (int)c->pol.slots.size()),
             K3_ERR_MEMORY);
   hipError_t e = hipSuccess;

@@ -11,6 +11,8 @@
 // by one owner in one order, [SAT] "A floating-point contract, not a
 // convention"). The work is a memory-bound stream of packed bytes ("the wait
 // is for bytes to arrive", [SAT] "Reduction one").
+#include <mutex>
+
 #include "k3_stream.h"
 #include "k3_shared_row.h"
 #include "k3_sync.h"
@@ -361,12 +363,45 @@ hipError_t launch_gate_up_routed(const uint16_t *x, const double *logits,
 
 unsigned moe_experts_grid() { return (unsigned)num_cus(); }
 
+namespace {
+// Two of these launches must never run at the same time on one device: each
+// needs all of its workgroups resident (they wait for each other), and two
+// grids that each hold part of the compute units would both wait until
+// their polls run out. Calls on one stream are ordered by the stream; a call
+// on another stream than the device's previous one waits, on the device,
+// for an event recorded after that previous launch. The event is recorded
+// after every launch, on the stream the launch went to (a stream the caller
+// still owns at that point).
+struct FusedOrder {
+  std::mutex mu;
+  hipStream_t last = nullptr;
+  hipEvent_t done = nullptr;
+  bool any = false;
+};
+FusedOrder g_fused_order[kMaxDevices];
+}  // namespace
+
 hipError_t launch_moe_experts(const uint16_t *x, const double *logits,
                               const uint8_t *const *experts, int n, int k,
                               int hidden, int inter, float *h, float *yp,
                               uint64_t *slots, uint64_t val, int32_t *idx,
                               float *w, uint16_t *y, float *y_f32,
                               hipStream_t s, const float *add, const SharedStage *sh) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  FusedOrder &o = g_fused_order[dev];
+  std::lock_guard<std::mutex> lock(o.mu);
+  if (!o.done) {
+    const hipError_t e = hipEventCreateWithFlags(&o.done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      o.done = nullptr;
+      return e;
+    }
+  }
+  if (o.any && o.last != s) {
+    const hipError_t e = hipStreamWaitEvent(s, o.done, 0);
+    if (e != hipSuccess) return e;
+  }
   // one workgroup per compute unit: the whole grid fits at once
   if (sh)
     hipLaunchKernelGGL(moe_experts_kernel<true>, dim3(moe_experts_grid()), dim3(kThreads), 0,
@@ -376,7 +411,13 @@ hipError_t launch_moe_experts(const uint16_t *x, const double *logits,
     hipLaunchKernelGGL(moe_experts_kernel<false>, dim3(moe_experts_grid()), dim3(kThreads), 0,
                        s, x, logits, experts, n, k, hidden, inter, h, yp, slots, val, idx, w,
                        y, y_f32, add, nullptr, nullptr, 0, 0);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(o.done, s);
+  if (e != hipSuccess) return e;
+  o.last = s;
+  o.any = true;
+  return hipSuccess;
 }
 
 hipError_t launch_combine(const float *yp, const float *w, int k, int hidden,

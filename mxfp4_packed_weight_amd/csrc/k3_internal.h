@@ -192,6 +192,7 @@ hipError_t launch_shared_down(const float *h, const uint16_t *const *shared, int
 // (moe_experts_grid() <= kMaxSyncGrid workgroups); val: this call's value,
 // never reused in the process.
 constexpr int kMaxSyncGrid = 1024;
+constexpr int kMaxDevices = 64;  // per-device state of the library
 unsigned moe_experts_grid();
 // The shared experts' down stage taken inside the expert launch: hs [n][inter]
 // from an earlier launch, ys [hidden] written here and added by the combine.

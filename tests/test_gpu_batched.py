@@ -9,8 +9,10 @@
   per-token layer; bf16 output bit-exact against RNE of the GPU's own fp32;
   reruns bit-identical.
 - The C4 workload at full size: 64 tokens with Zipf(1.1)-skewed logits over
-  the 896-expert pool (15.7 GB resident). Every token's routing is checked,
-  and the outputs of sampled tokens are compared with the oracle.
+  the 896-expert pool (15.7 GB resident). Every token's routing and output is
+  compared with the oracle, and batch invariance is reported.
+- Edge exponent bytes on both the short and the steady K paths, and NaN or
+  infinite activations inside groups whose exponent byte is 255.
 """
 import numpy as np
 import pytest
@@ -191,6 +193,69 @@ def test_batched_edge_exponents():
     say(f"batched edge exponents: max normwise {err:.3e}")
 
 
+def test_batched_edge_exponents_steady_down():
+    """Edge exponent bytes (0, 1, 2, 253, 254, 255) with inter 768, so that
+    down's K (24 groups, six quads) runs the steady loop of both down
+    launches, and a batch whose experts get items of at most 5 pairs (the
+    packed launch) and of more (one instruction per piece); every token
+    against the oracle."""
+    import torch
+    from mxfp4_packed_weight_amd.pool import ExpertPool
+    from tests import _independent as I
+    cfg, seed, n, hidden, inter, k, T = 77, 9, 6, 1024, 768, 3, 40
+    say(f"batched edge exponents n={n} hidden={hidden} inter={inter} k={k} T={T}")
+    X = W.tokens_bf16(seed, cfg, T, hidden)
+    xmax_col = np.abs(I.bf16_to_float_bits(X.reshape(-1)).reshape(T, hidden)).max(axis=0)
+    assert xmax_col.min() < 2.0
+    pool = ExpertPool(n, hidden, inter)
+    ex = {e: _edge_exponent_expert(seed, cfg, e, hidden, inter, xmax_col) for e in range(n)}
+    for e in range(n):
+        pool.load(e, ex[e])
+    torch.cuda.synchronize()
+    logits = W.zipf_router_logits(seed, T, n, 1.1, cfg).astype(np.float64)
+    idx = np.stack([oracle.topk(logits[t], k)[0] for t in range(T)])
+    counts = np.bincount(idx.ravel(), minlength=n)
+    items = [min(16, c - i) for c in counts.tolist() if c for i in range(0, c, 16)]
+    assert min(items) <= 5 < max(items), items
+    out = run_batched(pool, X, n, hidden, inter, k, logits=logits)
+    assert np.all(np.isfinite(out["Y32"]))
+    err = check_tokens(out, X, logits, lambda e: ex[e], k, hidden, inter, range(T))
+    say(f"batched edge exponents (steady down): max normwise {err:.3e}")
+
+
+def test_batched_nonfinite_x_in_skipped_group():
+    """NaN and infinite activations inside a gate/up group whose exponent
+    byte is 255 in every row: the group is skipped, not multiplied by zero,
+    so the rows stay finite and match the oracle, which skips it ([A176]
+    "What byte-identical actually costs")."""
+    import torch
+    from mxfp4_packed_weight_amd.pool import ExpertPool
+    cfg, seed, n, hidden, inter, k, T = 78, 11, 8, 1024, 256, 3, 6
+    say(f"batched layer, NaN/Inf x inside 255 groups, T={T}")
+    X = W.tokens_bf16(seed, cfg, T, hidden).copy()
+    g0 = 9
+    X[:, 32 * g0 + 5] = 0x7F80            # +Inf
+    X[1::2, 32 * g0 + 17] = 0xFF80        # -Inf
+    X[::3, 32 * g0 + 30] = 0x7FC0         # NaN
+    pool = ExpertPool(n, hidden, inter)
+    ex = {}
+    for e in range(n):
+        E = W.expert_weights(seed, cfg, e, hidden, inter, 114, 120)
+        for part in ("gate", "up"):
+            nib, sc = E[part]
+            sc = sc.copy()
+            sc[:, g0] = 255
+            E[part] = (nib, sc)
+        ex[e] = E
+        pool.load(e, E)
+    torch.cuda.synchronize()
+    logits = W.zipf_router_logits(seed, T, n, 1.1, cfg).astype(np.float64)
+    out = run_batched(pool, X, n, hidden, inter, k, logits=logits)
+    assert np.all(np.isfinite(out["Y32"]))
+    err = check_tokens(out, X, logits, lambda e: ex[e], k, hidden, inter, range(T))
+    say(f"batched NaN/Inf in skipped groups: max normwise {err:.3e}")
+
+
 def test_batched_router_path_small():
     cfg, seed, n, hidden, inter, k, T = 72, 5, 30, 256, 128, 6, 12
     say("batched layer through the router")
@@ -213,7 +278,22 @@ def c4_pool():
     return D.build_expert_pool(0, W.C3, W.N_EXPERTS, log=say)
 
 
+def _cached(fn):
+    memo = {}
+
+    def get(e):
+        if e not in memo:
+            memo[e] = fn(e)
+        return memo[e]
+    return get
+
+
 def test_batched_c4_full_size(c4_pool):
+    """The C4 workload at full size, every one of its 64 tokens against the
+    oracle. Also reports (a printed fact, not a gate) whether the batched
+    path is batch-invariant: each token's fp32 output beside the same
+    token's single-token decode launch, bit for bit."""
+    import torch
     n, hidden, inter, k, T = W.N_EXPERTS, W.HIDDEN, W.INTER, W.TOPK, 64
     say("batched decode C4: 64 tokens, Zipf(1.1) logits, top-16 of 896")
     X = W.tokens_bf16(0, W.C4, T, hidden)
@@ -226,10 +306,25 @@ def test_batched_c4_full_size(c4_pool):
     distinct = int((counts > 0).sum())
     say(f"C4 distinct experts {distinct}, hottest expert on {int(counts.max())} tokens")
     assert 250 <= distinct <= 420
+    # both down launches run: items (runs cut at 16 tokens) of <= 5 and > 5 pairs
+    items = [min(16, c - i) for c in counts.tolist() if c for i in range(0, c, 16)]
+    assert min(items) <= 5 < max(items), items
     err = check_tokens(out, X, logits,
-                       lambda e: W.expert_weights(0, W.C3, e, hidden, inter),
-                       k, hidden, inter, [0, 31, 63])
-    say(f"C4 sampled tokens: max normwise {err:.3e}")
+                       _cached(lambda e: W.expert_weights(0, W.C3, e, hidden, inter)),
+                       k, hidden, inter, range(T))
+    say(f"C4 all 64 tokens: max normwise {err:.3e}")
+    # batch invariance (reported): the same token alone through the decode launch
+    ws1 = empty(K.k3_moe_batched_workspace_bytes(1, n, hidden, inter, k), torch.uint8)
+    same, worst = 0, 0.0
+    for t in range(T):
+        Y1 = empty((1, hidden), torch.float32)
+        K.k3_moe_layer_from_logits(up(X[t:t + 1]), up(logits[t:t + 1]), None, c4_pool.table,
+                                   n, hidden, inter, k, 1, None, ws1, Y_f32=Y1)
+        y1 = Y1.cpu().numpy()[0]
+        same += int(np.array_equal(y1.view(np.uint32), out["Y32"][t].view(np.uint32)))
+        worst = max(worst, normwise(out["Y32"][t], y1))
+    say(f"C4 batch invariance: {same} of {T} tokens bit-identical to their single-token "
+        f"decode launch; max normwise difference {worst:.3e}")
 
 
 def test_one_token_from_logits_takes_the_decode_launch(c4_pool):

@@ -31,7 +31,8 @@ import gen
 import mxfp4_packed_weight_amd as K
 from gen import device as D
 from gen import workloads as W
-from tests._gpu import empty, make_cache, pinned_copy, say, up
+import oracle
+from tests._gpu import TOL, empty, make_cache, normwise, pinned_copy, say, up
 
 pytestmark = pytest.mark.gpu
 
@@ -112,6 +113,14 @@ def test_cached_layer_matches_resident_layer(small_pool):
             for key in want:
                 assert np.array_equal(got[key], want[key]), (t, key)
             trace.extend(got["idx"].tolist())
+            if t in (0, tokens - 1):  # the cached layer against the oracle itself
+                R_h = R_d.cpu().numpy().view(np.uint16)
+                ex = {e: W.expert_weights(SEED, CFG, e, HIDDEN, INTER, 114, 120)
+                      for e in got["idx"].tolist()}
+                y_ref, idx_ref, w_ref = oracle.moe_layer(X[t], R_h, ex, KTOP, HIDDEN, INTER)
+                assert np.array_equal(got["idx"], idx_ref)
+                assert np.max(np.abs(got["w"].view(np.float32) - w_ref)) <= 1e-6
+                assert normwise(got["y32"].view(np.float32), y_ref) <= TOL, t
             tab = read_table(c, N)
             if slot_lo is None:
                 slot_lo = int(tab[got["idx"]].min())  # first token fills slots 0..k-1
@@ -252,8 +261,9 @@ def batched_outputs(fn, arg, X, L, T, ws):
 def test_batched_cached_layer_matches_resident(small_pool):
     """Batches of 4 tokens (top-8 of 48) through 36 slots: each batch fits,
     their union does not, so experts are evicted between batches. Every batch
-    gives the resident batched layer's bits; the counters equal the replay
-    with one request per batch."""
+    gives the resident batched layer's bits, and the last one is within 1e-5
+    of the oracle; the counters equal the replay with one request per
+    batch."""
     import torch
     pool, _, host = small_pool
     T, slots, nb = 4, 36, 6
@@ -272,6 +282,18 @@ def test_batched_cached_layer_matches_resident(small_pool):
             for key in want:
                 assert np.array_equal(got[key], want[key]), (b, key)
             trace.extend(got["idx"].ravel().tolist())
+            if b == nb - 1:  # the last batch (after evictions) against the oracle itself
+                Xh, Lh = X.cpu().numpy().view(np.uint16), L.cpu().numpy()
+                ex = {e: W.expert_weights(SEED, CFG, e, HIDDEN, INTER, 114, 120)
+                      for e in np.unique(got["idx"]).tolist()}
+                oracle.set_threads(16)
+                Y_ref, idx_ref, w_ref = oracle.moe_from_logits(Xh, Lh, ex, KTOP, HIDDEN, INTER)
+                assert np.array_equal(got["idx"], idx_ref)
+                assert np.max(np.abs(got["w"].view(np.float32) - w_ref)) <= 1e-6
+                for t in range(T):
+                    err = normwise(got["Y32"][t].view(np.float32), Y_ref[t])
+                    assert err <= TOL, (t, err)
+                say(f"batched cached layer, batch {b}: within {TOL} of the oracle")
         st = K.k3_cache_get_stats(c)
         ref = K.k3_cache_replay(np.array(trace, np.int32), N, slots, (), T * KTOP)
         ref["bytes_copied"] = st["misses"] * pool.expert_bytes

@@ -200,6 +200,62 @@ def test_layer_over_many_tokens_on_one_workspace():
             check_against_oracle(out, X[t], R, seed, cfg, n, hidden, inter, k, 114, 120)
 
 
+def test_layer_calls_on_two_streams(c3_pool):
+    """Layer calls issued on two streams with two workspaces, alternating
+    from one host thread and then from two host threads at once, with no
+    synchronisation between the streams: every output equals, bit for bit,
+    the same token's output from one stream alone, and is within 1e-5 of
+    the oracle (the library orders its whole-grid expert launches across
+    streams, so they never hold the device together)."""
+    import threading
+    import torch
+    pool, R, R_d = c3_pool
+    n, hidden, inter, k = W.N_EXPERTS, W.HIDDEN, W.INTER, W.TOPK
+    X = W.tokens_bf16(0, W.C3, 2, hidden, batch=11)
+    xs = [up(X[0]), up(X[1])]
+    ws = [empty(K.k3_moe_workspace_bytes(1, n, hidden, inter, k), torch.uint8) for _ in range(2)]
+    ref = [layer_outputs(pool, R_d, xs[i], n, hidden, inter, k, ws[0]) for i in range(2)]
+    for i in range(2):
+        err, _ = check_against_oracle(ref[i], X[i], R, 0, W.C3, n, hidden, inter, k, W.ELO, W.EHI)
+        say(f"two streams: token {i} normwise {err:.3e} against the oracle")
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    reps = 6
+    outs = [[empty(hidden, torch.float32) for _ in range(2 * reps)] for _ in range(2)]
+    torch.cuda.synchronize()
+
+    def issue(i, r):
+        K.k3_moe_layer_ex(xs[i], R_d, pool.table, n, hidden, inter, k, None, ws[i],
+                          y_f32=outs[i][r], stream=streams[i])
+
+    say("two streams: alternating calls from one thread")
+    for r in range(reps):
+        issue(0, r)
+        issue(1, r)
+    torch.cuda.synchronize()
+    say("two streams: two host threads at once")
+    errs = []
+
+    def worker(i):
+        try:
+            for r in range(reps, 2 * reps):
+                issue(i, r)
+        except Exception as e:  # reported by the main thread
+            errs.append(e)
+    th = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errs, errs
+    for i in range(2):
+        want = ref[i]["y32"].view(np.uint32)
+        for r in range(2 * reps):
+            got = outs[i][r].cpu().numpy().view(np.uint32)
+            assert np.array_equal(got, want), (i, r)
+    say(f"two streams: {2 * 2 * reps} calls bit-identical to the one-stream outputs")
+
+
 def test_layer_c3_tokens_in_a_row(c3_pool):
     """Eight C3 tokens back to back on one workspace, each bit-identical to the
     stage-by-stage calls (the full-size grid: 768 gate/up and 1792 down
@@ -219,8 +275,9 @@ def test_layer_c3_tokens_in_a_row(c3_pool):
 def test_cached_layer_c3_full_size(c3_pool):
     """The C3 layer with the 896 experts in pinned host memory behind a
     40-slot HBM cache: six tokens, each bit-identical (y, fp32 y, indices,
-    weights) to the layer on the resident pool, the cache's counters equal
-    to the host replay of its trace."""
+    weights) to the layer on the resident pool, the first and the last
+    within 1e-5 of the oracle, the cache's counters equal to the host replay
+    of its trace."""
     import torch
     pool, R, R_d = c3_pool
     n, hidden, inter, k = W.N_EXPERTS, W.HIDDEN, W.INTER, W.TOPK
@@ -245,6 +302,14 @@ def test_cached_layer_c3_full_size(c3_pool):
             assert np.array_equal(y32.cpu().numpy().view(np.uint32), want["y32"].view(np.uint32))
             assert np.array_equal(y.cpu().numpy().view(np.uint16), want["y"])
             trace.extend(want["idx"].tolist())
+            if t in (0, 5):  # the cached layer against the oracle itself
+                lg = empty(n, torch.float64)
+                K.k3_router(xd, R_d, 1, hidden, n, lg)
+                got = dict(y=y.cpu().numpy().view(np.uint16), y32=y32.cpu().numpy(),
+                           idx=idx.cpu().numpy(), w=w.cpu().numpy(), logits=lg.cpu().numpy())
+                err, _ = check_against_oracle(got, X[t], R, 0, W.C3, n, hidden, inter, k,
+                                              W.ELO, W.EHI)
+                say(f"cached layer C3 token {t}: normwise {err:.3e} against the oracle")
         st = K.k3_cache_get_stats(c)
         ref = K.k3_cache_replay(np.array(trace, np.int32), n, 40, (), k)
         ref["bytes_copied"] = st["misses"] * pool.expert_bytes

@@ -168,16 +168,72 @@ def c5_pool():
     return D.build_expert_pool(0, W.C3, W.N_EXPERTS, log=say)
 
 
+def test_prefill_weight_exponent_255():
+    """Weight groups with exponent byte 255 scattered through gate, up and
+    down contribute nothing ([A176] "What byte-identical actually costs";
+    [SAT] "Reduction one"), at K long enough for the steady path of both
+    GEMMs (hidden 1024, inter 768); every token staged against the oracle,
+    which skips those groups."""
+    import torch
+    from mxfp4_packed_weight_amd.pool import ExpertPool
+    cfg, seed, n, hidden, inter, k, T = 79, 12, 6, 1024, 768, 2, 60
+    say(f"prefill with weight exponent 255, n={n} hidden={hidden} inter={inter} T={T}")
+    pool = ExpertPool(n, hidden, inter)
+    ex = {}
+    rng = np.random.default_rng(255)
+    for e in range(n):
+        E = W.expert_weights(seed, cfg, e, hidden, inter, 114, 120)
+        for part in ("gate", "up", "down"):
+            nib, sc = E[part]
+            sc = sc.copy()
+            sc[rng.random(sc.shape) < 0.08] = 255
+            E[part] = (nib, sc)
+        ex[e] = E
+        pool.load(e, E)
+    torch.cuda.synchronize()
+    assert all(int((ex[e][p][1] == 255).sum()) > 0 for e in range(n) for p in ("gate", "up", "down"))
+    X = W.tokens_bf16(seed, cfg, T, hidden)
+    logits = W.uniform_router_logits(seed, T, n, cfg).astype(np.float64)
+    out = run_prefill(pool, X, logits, n, hidden, inter, k)
+    eh, ey = check_prefill(out, X, logits, lambda e: ex[e], k, hidden, inter, range(T))
+    say(f"prefill exponent 255: h {eh:.3e} y {ey:.3e}")
+
+
 def test_prefill_c5_full_size(c5_pool):
+    """The C5 workload at full size. Every pair of the most-loaded expert is
+    checked through stages 2 and 3 (one oracle product over all its tokens),
+    and whole tokens through stage 4: tokens 0, 1023, 2047 and the first,
+    middle and last token of the most-loaded expert (its first and last
+    tokens fall in different work items when it holds more than 64)."""
     n, hidden, inter, k, T = W.N_EXPERTS, W.HIDDEN, W.INTER, W.TOPK, 2048
     say("prefill C5: 2048 tokens, uniform logits, top-16 of 896")
     X = W.tokens_bf16(0, W.C5, T, hidden)
     logits = W.uniform_router_logits(0, T, n, W.C5).astype(np.float64)
     out = run_prefill(c5_pool, X, logits, n, hidden, inter, k)
-    counts, _, _, _ = oracle.permute(out["idx"], n)
+    counts, offsets, pt, ps = oracle.permute(out["idx"], n)
+    hot = int(np.argmax(counts))
     say(f"C5 experts used {int((counts > 0).sum())}, tokens per expert "
-        f"{counts.mean():.1f} (max {int(counts.max())})")
+        f"{counts.mean():.1f} (max {int(counts.max())}, expert {hot})")
+    # stages 2 and 3 on every pair of the most-loaded expert
+    oracle.set_threads(16)
+    E = W.expert_weights(0, W.C3, hot, hidden, inter)
+    qs = np.arange(offsets[hot], offsets[hot] + counts[hot])
+    toks = pt[qs]
+    xn, xs = oracle.mxfp4_quant(bf16_to_f64(X[toks]))
+    g = oracle.mxfp4_matmul(xn, xs, *E["gate"])
+    u = oracle.mxfp4_matmul(xn, xs, *E["up"])
+    silu = np.vectorize(oracle.silu)
+    with np.errstate(over="ignore"):
+        h_ref = silu(g) * u
+    worst = 0.0
+    for i, q in enumerate(qs):
+        worst = max(worst, normwise(out["h32"][q], h_ref[i]))
+        qn, qsc = oracle.mxfp4_quant(out["h32"][q].astype(np.float64))
+        assert np.array_equal(out["hn"][q], qn[0]) and np.array_equal(out["hs"][q], qsc[0]), q
+    assert worst <= TOL, worst
+    say(f"C5 most-loaded expert {hot}: {len(qs)} pairs, h within {worst:.3e}")
+    sample = sorted({0, 1023, 2047, int(toks[0]), int(toks[len(toks) // 2]), int(toks[-1])})
     eh, ey = check_prefill(out, X, logits,
                            lambda e: W.expert_weights(0, W.C3, e, hidden, inter),
-                           k, hidden, inter, [0, 1023, 2047])
-    say(f"C5 sampled tokens: h {eh:.3e} y {ey:.3e}")
+                           k, hidden, inter, sample)
+    say(f"C5 sampled tokens {sample}: h {eh:.3e} y {ey:.3e}")

@@ -132,7 +132,7 @@ def test_refusals_before_launch(L):
     assert need > 0
     rc = L.k3_moe_layer(_fake(1), _fake(2), _fake(3), 896, 7168, 1536, 16, _fake(4), _fake(5),
                         need - 1, s)
-    assert rc == K.K3_ERR_MEMORY and "memory limit, not an engine ceiling" in K.last_error()
+    assert rc == K.K3_ERR_MEMORY and "is below the" in K.last_error()
     rc = L.k3_moe_layer(_fake(1), _fake(2), _fake(3), 896, 7168, 1536, 0, _fake(4), _fake(5),
                         need, s)
     assert rc == K.K3_ERR_CONFIG
