@@ -241,6 +241,28 @@ k3_status k3_moe_layer_ex(const uint16_t *x, const uint16_t *router_w,
                           double *logits, void *ws, size_t ws_bytes,
                           k3_stream_t stream);
 
+/* ----------------------------------------------------------------------
+ * k3_moe_layer_noalloc: k3_moe_layer_ex without a workspace argument, for
+ * callers that cannot allocate device memory (code under graph capture,
+ * serving loops, harnesses that forbid allocation). Same arguments, outputs,
+ * kernels and bits as k3_moe_layer_ex. Its scratch is a static device array
+ * of K3_NOALLOC_SCRATCH_BYTES inside the library, one per device, held until
+ * the process ends; the call allocates nothing. Shapes whose scratch
+ * (k3_moe_workspace_bytes(1, n_experts, hidden, inter, k)) exceeds it are
+ * refused with K3_ERR_MEMORY (the 896-expert, 7168/1536, top-16 layer needs
+ * about 0.58 MB). Every call on one device shares that device's array:
+ * calls that overlap on one device (on different streams, or a call on
+ * another stream before an earlier one finished) race on it and must be
+ * ordered by the caller. Nothing in it needs clearing between calls (its
+ * arrival slots carry a per-call value).
+ * ---------------------------------------------------------------------- */
+#define K3_NOALLOC_SCRATCH_BYTES (2u << 20)
+k3_status k3_moe_layer_noalloc(const uint16_t *x, const uint16_t *router_w,
+                               const uint8_t *const *experts, int n_experts,
+                               int hidden, int inter, int k, uint16_t *y,
+                               float *y_f32, int32_t *idx, float *w,
+                               double *logits, k3_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * Batched decode: T tokens, each routed to k of n_experts experts; every
  * selected expert's packed bytes are read once for all of its tokens.

@@ -59,6 +59,8 @@ SIGNATURES = [
     ("k3_moe_layer", _i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
     ("k3_moe_layer_ex", _i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
                              _vp, _sz, _vp]),
+    ("k3_moe_layer_noalloc", _i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
+                                  _vp]),
     ("k3_moe_permute_workspace_bytes", _sz, [_i, _i]),
     ("k3_moe_permute", _i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     ("k3_moe_batched_workspace_bytes", _sz, [_i, _i, _i, _i, _i]),
@@ -271,6 +273,15 @@ def k3_moe_layer_ex(x, router_w, experts, n_experts, hidden, inter, k, y, ws, y_
     _call("k3_moe_layer_ex", _dp(x), _dp(router_w), _dp(experts), n_experts, hidden, inter,
           k, _dp(y), _dp(y_f32), _dp(idx), _dp(w), _dp(logits), _dp(ws), _nbytes(ws),
           _stream(stream))
+
+
+def k3_moe_layer_noalloc(x, router_w, experts, n_experts, hidden, inter, k, y, y_f32=None,
+                         idx=None, w=None, logits=None, stream=None):
+    _call("k3_moe_layer_noalloc", _dp(x), _dp(router_w), _dp(experts), n_experts, hidden,
+          inter, k, _dp(y), _dp(y_f32), _dp(idx), _dp(w), _dp(logits), _stream(stream))
+
+
+K3_NOALLOC_SCRATCH_BYTES = 2 << 20
 
 
 # ---- batched decode -------------------------------------------------------

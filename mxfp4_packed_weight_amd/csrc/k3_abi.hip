@@ -12,6 +12,7 @@
 #include <algorithm>
 #include <atomic>
 #include <chrono>
+#include <mutex>
 
 #include "k3_internal.h"
 
@@ -652,6 +653,65 @@ k3_status k3_moe_layer_ex(const uint16_t *x, const uint16_t *router_w,
   return layer_launches(fn, x, router_w, experts, n_experts, hidden, inter, k, y,
                         y_f32, idx, w, logits, static_cast<uint8_t *>(ws), L,
                         nullptr, stream);
+}
+
+// ---- the decode layer without a caller workspace --------------------------
+// For callers that cannot allocate device memory: the layer's scratch (logits,
+// selection, h, down partials, arrival slots) lives in this file-scope array,
+// one copy per device, held until the process ends. Its device address is
+// looked up once per device with that device current; host code passes that
+// address, never the array's own name (a host-side stand-in).
+static __device__ __align__(256) uint8_t scratch[K3_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+uint8_t *g_scratch_at[kMaxDevices];
+}  // namespace
+
+static k3_status scratch_address(const char *fn, uint8_t **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_status(e, fn);
+  K3_NEED(fn, dev >= 0 && dev < kMaxDevices, "%s: device %d beyond the %d this library serves",
+          fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_at[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return device_status(e, fn);
+    if (!p) return fail(K3_ERR_DEVICE, "%s: no device address for the static scratch", fn);
+    g_scratch_at[dev] = static_cast<uint8_t *>(p);
+  }
+  *out = g_scratch_at[dev];
+  return K3_OK;
+}
+
+k3_status k3_moe_layer_noalloc(const uint16_t *x, const uint16_t *router_w,
+                               const uint8_t *const *experts, int n_experts,
+                               int hidden, int inter, int k, uint16_t *y,
+                               float *y_f32, int32_t *idx, float *w,
+                               double *logits, k3_stream_t stream) {
+  const char *fn = "k3_moe_layer_noalloc";
+  K3_NEED_PTR(fn, x);
+  K3_NEED_PTR(fn, router_w);
+  K3_NEED_PTR(fn, experts);
+  K3_NEED_PTR(fn, y);
+  if ((y_f32 && !aligned16(y_f32)) || (idx && !aligned16(idx)) ||
+      (w && !aligned16(w)) || (logits && !aligned16(logits)))
+    return fail(K3_ERR_ARG, "%s: an optional output is not 16-byte aligned",
+                fn);
+  if (k3_status s = check_routing(fn, 1, n_experts, k)) return s;
+  if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
+  const WsLayout L = ws_layout(1, n_experts, hidden, inter, k);
+  if (L.total > (size_t)K3_NOALLOC_SCRATCH_BYTES)
+    return fail(K3_ERR_MEMORY,
+                "%s: this shape needs %zu bytes of scratch, above the %zu-byte "
+                "static scratch of the call (use k3_moe_layer_ex with a workspace)",
+                fn, L.total, (size_t)K3_NOALLOC_SCRATCH_BYTES);
+  uint8_t *base = nullptr;
+  if (k3_status s = scratch_address(fn, &base)) return s;
+  return layer_launches(fn, x, router_w, experts, n_experts, hidden, inter, k, y,
+                        y_f32, idx, w, logits, base, L, nullptr, stream);
 }
 
 size_t k3_shared_expert_bytes(int hidden, int inter) {
