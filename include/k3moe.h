@@ -11,10 +11,12 @@
  * issued concurrently, from any host threads. The decode layer's expert
  * launch (k3_moe_layer, _ex, _shared, _cached, and k3_moe_layer_from_logits
  * with T = 1 and no bias) needs its whole grid resident at once, so the
- * library orders those launches on one device: one issued on another stream
- * than the device's previous one waits, on the device, for that previous
- * launch to finish (an event recorded after every such launch). Every other
- * launch may overlap with anything.
+ * library orders those launches on one device. While they all go to one
+ * stream, the stream orders them. The first one issued on a second stream
+ * blocks the calling thread until the device is idle; from then on an event
+ * is recorded after each of them, and one issued on another stream than
+ * the previous one waits for it on the device. Every other launch may
+ * overlap with anything.
  *
  * Sources (web pages describing the kimi-k3-in-c engine), cited below as:
  *  [A176] "kimi-k3-in-c: A 176 KB Engine That Runs a 2.78T-Parameter MoE in

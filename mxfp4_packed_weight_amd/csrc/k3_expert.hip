@@ -367,16 +367,20 @@ namespace {
 // Two of these launches must never run at the same time on one device: each
 // needs all of its workgroups resident (they wait for each other), and two
 // grids that each hold part of the compute units would both wait until
-// their polls run out. Calls on one stream are ordered by the stream; a call
-// on another stream than the device's previous one waits, on the device,
-// for an event recorded after that previous launch. The event is recorded
-// after every launch, on the stream the launch went to (a stream the caller
-// still owns at that point).
+// their polls run out. Calls on one stream are ordered by the stream. While
+// every launch on a device has gone to one stream nothing more is done (an
+// event per launch costs a few microseconds of the layer). The first launch
+// on a second stream waits on the host until the device is idle, so the
+// previous stream's launches are finished without touching that stream (it
+// may no longer exist); from then on an event is recorded after every
+// launch, and a launch on another stream than the previous one waits for
+// it on the device.
 struct FusedOrder {
   std::mutex mu;
   hipStream_t last = nullptr;
   hipEvent_t done = nullptr;
-  bool any = false;
+  bool any = false;    // a launch went out on this device
+  bool multi = false;  // launches went to more than one stream
 };
 FusedOrder g_fused_order[kMaxDevices];
 }  // namespace
@@ -391,16 +395,20 @@ hipError_t launch_moe_experts(const uint16_t *x, const double *logits,
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   FusedOrder &o = g_fused_order[dev];
   std::lock_guard<std::mutex> lock(o.mu);
-  if (!o.done) {
-    const hipError_t e = hipEventCreateWithFlags(&o.done, hipEventDisableTiming);
-    if (e != hipSuccess) {
-      o.done = nullptr;
-      return e;
-    }
-  }
   if (o.any && o.last != s) {
-    const hipError_t e = hipStreamWaitEvent(s, o.done, 0);
-    if (e != hipSuccess) return e;
+    if (!o.multi) {  // first switch of stream: finish everything queued so far
+      hipError_t e = hipEventCreateWithFlags(&o.done, hipEventDisableTiming);
+      if (e != hipSuccess) {
+        o.done = nullptr;
+        return e;
+      }
+      e = hipDeviceSynchronize();
+      if (e != hipSuccess) return e;
+      o.multi = true;
+    } else {
+      const hipError_t e = hipStreamWaitEvent(s, o.done, 0);
+      if (e != hipSuccess) return e;
+    }
   }
   // one workgroup per compute unit: the whole grid fits at once
   if (sh)
@@ -413,8 +421,10 @@ hipError_t launch_moe_experts(const uint16_t *x, const double *logits,
                        y, y_f32, add, nullptr, nullptr, 0, 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = hipEventRecord(o.done, s);
-  if (e != hipSuccess) return e;
+  if (o.multi) {
+    e = hipEventRecord(o.done, s);
+    if (e != hipSuccess) return e;
+  }
   o.last = s;
   o.any = true;
   return hipSuccess;

@@ -145,7 +145,10 @@ def _edge_exponent_expert(seed, cfg, e, hidden, inter, xmax_col):
     255 at random places, and gate rows 0, 1 and 2 with exponent bytes 253, 254 and
     252 on a group holding a single code 0.5, at the column whose
     activations are smallest (xmax_col: max |x| per column), so that every
-    product and sum stays finite in fp32."""
+    product and sum stays finite in fp32. Those gate rows reach about 1e38;
+    their up rows take exponent byte 60 (weights near 1e-20), so that h, and
+    down's unscaled group sums of up to 32 * 6 * |h| (the group's exponent
+    is applied after its sum), stay far inside the fp32 range."""
     E = W.expert_weights(seed, cfg, e, hidden, inter, 114, 120)
     rng = np.random.default_rng(1000 + e)
     c = int(np.argmin(xmax_col))
@@ -161,6 +164,8 @@ def _edge_exponent_expert(seed, cfg, e, hidden, inter, xmax_col):
                 nib[r, 16 * g:16 * g + 16] = 0
                 nib[r, 16 * g + j // 2] = 0x01 << (4 * (j % 2))  # element j: code 1 (0.5)
                 sc[r, g] = ex
+        else:
+            sc[0:3, :] = 60
         E[part] = (nib, sc)
     nib, sc = E["down"]
     sc = sc.copy()

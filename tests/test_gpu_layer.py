@@ -221,10 +221,11 @@ def test_layer_calls_on_two_streams(c3_pool):
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     reps = 6
     outs = [[empty(hidden, torch.float32) for _ in range(2 * reps)] for _ in range(2)]
+    ybf = [[empty(hidden, torch.int16) for _ in range(2 * reps)] for _ in range(2)]
     torch.cuda.synchronize()
 
     def issue(i, r):
-        K.k3_moe_layer_ex(xs[i], R_d, pool.table, n, hidden, inter, k, None, ws[i],
+        K.k3_moe_layer_ex(xs[i], R_d, pool.table, n, hidden, inter, k, ybf[i][r], ws[i],
                           y_f32=outs[i][r], stream=streams[i])
 
     say("two streams: alternating calls from one thread")
@@ -253,6 +254,7 @@ def test_layer_calls_on_two_streams(c3_pool):
         for r in range(2 * reps):
             got = outs[i][r].cpu().numpy().view(np.uint32)
             assert np.array_equal(got, want), (i, r)
+            assert np.array_equal(ybf[i][r].cpu().numpy().view(np.uint16), ref[i]["y"]), (i, r)
     say(f"two streams: {2 * 2 * reps} calls bit-identical to the one-stream outputs")
 
 
