@@ -392,10 +392,20 @@ def bench_c1_c2(args):
         x = D.to_device(W.tokens_bf16(0, W.C2, 1)[0].view(np.int16), dev)
         y = torch.empty(hidden, dtype=torch.float32, device=dev)
         h = torch.empty(inter, dtype=torch.float32, device=dev)
-        single = timed(lambda i: K.k3_expert_swiglu(x, pool.expert_view(0), hidden, inter, y, h,
-                                                    stream), args.steps)
-        rot = timed(lambda i: K.k3_expert_swiglu(x, pool.expert_view(i % ne), hidden, inter, y, h,
-                                                 stream), args.steps)
+        ws = torch.empty(K.k3_expert_swiglu_workspace_bytes(hidden, inter), dtype=torch.uint8,
+                         device=dev)
+        # the one-launch entry point (gate/up split along K over every compute unit)
+        single = timed(lambda i: K.k3_expert_swiglu_ws(x, pool.expert_view(0), hidden, inter, y,
+                                                       ws, stream=stream), args.steps)
+        rot = timed(lambda i: K.k3_expert_swiglu_ws(x, pool.expert_view(i % ne), hidden, inter,
+                                                    y, ws, stream=stream), args.steps)
+        # beside it: the two-launch entry point (tile-split gate/up, then down)
+        two_single = timed(lambda i: K.k3_expert_swiglu(x, pool.expert_view(0), hidden, inter, y,
+                                                        h, stream), args.steps)
+        two_rot = timed(lambda i: K.k3_expert_swiglu(x, pool.expert_view(i % ne), hidden, inter,
+                                                     y, h, stream), args.steps)
+        log(f"C2 two launches (k3_expert_swiglu): single {two_single:.2f} us, rotating "
+            f"{two_rot:.2f} us")
         nbytes, name = BYTES_PER_EXPERT, "one routed SwiGLU expert, hidden 7168, inter 1536, x bf16"
         E = W.expert_weights(0, W.C2, 0)
         xf = oracle.bf16_to_f64(W.tokens_bf16(0, W.C2, 1)[0])
@@ -417,9 +427,12 @@ def bench_c1_c2(args):
                    "rotation": "4096 copies (570 MB)" if args.workload == "c1"
                    else "64 experts (1.12 GB)"},
         "single_call_us": round(single, 3), "rotating_call_us": round(rot, 3),
+        **({} if args.workload == "c1" else
+           {"two_launch_single_call_us": round(two_single, 3),
+            "two_launch_rotating_call_us": round(two_rot, 3)}),
         "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "roofline": {"kernel": "gemv_f32_kernel" if args.workload == "c1"
-                     else "gate_up_kernel + down_kernel (k3_expert_swiglu)",
+                     else "expert_one_kernel (k3_expert_swiglu_ws, one launch)",
                      "bound": "hbm", "achieved": round(value, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(value / PEAK_HBM_GBS, 4), "traffic": None,
                      "algorithmic_bytes_per_launch": nbytes},

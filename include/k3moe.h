@@ -9,9 +9,10 @@
  * launched), then enqueue asynchronously on `stream` and never synchronise.
  * Calls on different streams with different outputs and workspaces may be
  * issued concurrently, from any host threads. The decode layer's expert
- * launch (k3_moe_layer, _ex, _shared, _cached, and k3_moe_layer_from_logits
- * with T = 1 and no bias) needs its whole grid resident at once, so the
- * library orders those launches on one device. While they all go to one
+ * launch (k3_moe_layer, _ex, _noalloc, _shared, _cached, and
+ * k3_moe_layer_from_logits with T = 1 and no bias) and k3_expert_swiglu_ws
+ * need their whole grid resident at once, so the library orders those
+ * launches on one device. While they all go to one
  * stream, the stream orders them. The first one issued on a second stream
  * blocks the calling thread until the device is idle; from then on an event
  * is recorded after each of them, and one issued on another stream than
@@ -151,6 +152,25 @@ k3_status k3_mxfp4_gemv(const float *x, const uint8_t *tiles, int rows,
 k3_status k3_expert_swiglu(const uint16_t *x, const uint8_t *expert,
                            int hidden, int inter, float *y, float *h,
                            k3_stream_t stream);
+
+/* The same expert in one launch over every compute unit, for a lone expert
+ * (the two launches above occupy only as many compute units as the matrix
+ * has 64-row tiles). The gate/up tiles are cut along K into chunks, one per
+ * workgroup; their row partials go to the workspace, and the workgroups that
+ * own down tiles (whose first bytes they load before the gate/up work) sum
+ * each row's partials in chunk order, form h and multiply their tile by it.
+ * Summation order differs from k3_expert_swiglu's, so the two differ in the
+ * last bits; each is bit-identical from run to run on one device. h fp32
+ * [inter] is optional (NULL: not written). ws: at least
+ * k3_expert_swiglu_workspace_bytes(hidden, inter) bytes; calls sharing a
+ * workspace must not overlap. The launch needs its whole grid resident; it
+ * is ordered with the decode layer's expert launch across streams (top of
+ * this file). While the stream is being captured it runs the two launches
+ * of k3_expert_swiglu instead (same bits as those). */
+size_t k3_expert_swiglu_workspace_bytes(int hidden, int inter);
+k3_status k3_expert_swiglu_ws(const uint16_t *x, const uint8_t *expert,
+                              int hidden, int inter, float *y, float *h,
+                              void *ws, size_t ws_bytes, k3_stream_t stream);
 
 /* The two stages of k3_expert_swiglu over k routing slots of one token, and
  * the weighted combine, as separate calls (k3_moe_layer runs exactly these):

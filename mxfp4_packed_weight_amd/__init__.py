@@ -48,6 +48,8 @@ SIGNATURES = [
     ("k3_expert_pack", _i, [_vp] * 6 + [_i, _i, _vp, _vp]),
     ("k3_mxfp4_gemv", _i, [_vp, _vp, _i, _i, _vp, _vp]),
     ("k3_expert_swiglu", _i, [_vp, _vp, _i, _i, _vp, _vp, _vp]),
+    ("k3_expert_swiglu_workspace_bytes", _sz, [_i, _i]),
+    ("k3_expert_swiglu_ws", _i, [_vp, _vp, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     ("k3_expert_gate_up", _i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
     ("k3_expert_gate_up_routed", _i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
     ("k3_expert_down", _i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
@@ -222,6 +224,15 @@ def k3_mxfp4_gemv(x, tiles, rows, cols, y, stream=None):
 def k3_expert_swiglu(x, expert, hidden, inter, y, h, stream=None):
     _call("k3_expert_swiglu", _dp(x), _dp(expert), hidden, inter, _dp(y), _dp(h),
           _stream(stream))
+
+
+def k3_expert_swiglu_workspace_bytes(hidden, inter):
+    return lib().k3_expert_swiglu_workspace_bytes(hidden, inter)
+
+
+def k3_expert_swiglu_ws(x, expert, hidden, inter, y, ws, h=None, stream=None):
+    _call("k3_expert_swiglu_ws", _dp(x), _dp(expert), hidden, inter, _dp(y), _dp(h), _dp(ws),
+          _nbytes(ws), _stream(stream))
 
 
 def k3_expert_gate_up(x, experts, idx, k, hidden, inter, h, stream=None):

@@ -409,6 +409,37 @@ k3_status k3_expert_swiglu(const uint16_t *x, const uint8_t *expert,
   return K3_OK;
 }
 
+size_t k3_expert_swiglu_workspace_bytes(int hidden, int inter) {
+  if (check_expert_dims("k3_expert_swiglu_workspace_bytes", hidden, inter) != K3_OK) return 0;
+  return align256(expert_one_workspace_bytes(hidden, inter));
+}
+
+k3_status k3_expert_swiglu_ws(const uint16_t *x, const uint8_t *expert, int hidden,
+                              int inter, float *y, float *h, void *ws, size_t ws_bytes,
+                              k3_stream_t stream) {
+  const char *fn = "k3_expert_swiglu_ws";
+  K3_NEED_PTR(fn, x);
+  K3_NEED_PTR(fn, expert);
+  K3_NEED_PTR(fn, y);
+  K3_NEED_PTR(fn, ws);
+  if (h && !aligned16(h)) return fail(K3_ERR_ARG, "%s: h is not 16-byte aligned", fn);
+  if (k3_status s = check_expert_dims(fn, hidden, inter)) return s;
+  if (k3_status s = need_ws(fn, ws_bytes, k3_expert_swiglu_workspace_bytes(hidden, inter)))
+    return s;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (moe_experts_grid() <= (unsigned)kMaxSyncGrid &&
+      hipStreamIsCapturing(stream, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone) {
+    K3_LAUNCH(fn, launch_expert_one(x, expert, hidden, inter, y, h, ws, next_layer_seq(),
+                                    stream));
+    return K3_OK;
+  }
+  // captured (a per-call value would be frozen in the graph): the two stages
+  float *hh = h ? h : static_cast<float *>(ws);  // the partial area holds inter floats
+  K3_LAUNCH(fn, launch_gate_up(x, nullptr, nullptr, expert, 1, hidden, inter, hh, stream));
+  K3_LAUNCH(fn, launch_down(hh, nullptr, nullptr, expert, 1, hidden, inter, y, stream));
+  return K3_OK;
+}
+
 k3_status k3_expert_gate_up(const uint16_t *x, const uint8_t *const *experts,
                             const int32_t *idx, int k, int hidden, int inter,
                             float *h, k3_stream_t stream) {

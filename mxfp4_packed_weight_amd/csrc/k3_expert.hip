@@ -11,6 +11,7 @@
 // by one owner in one order, [SAT] "A floating-point contract, not a
 // convention"). The work is a memory-bound stream of packed bytes ("the wait
 // is for bytes to arrive", [SAT] "Reduction one").
+#include <functional>
 #include <mutex>
 
 #include "k3_stream.h"
@@ -364,17 +365,17 @@ hipError_t launch_gate_up_routed(const uint16_t *x, const double *logits,
 unsigned moe_experts_grid() { return (unsigned)num_cus(); }
 
 namespace {
-// Two of these launches must never run at the same time on one device: each
-// needs all of its workgroups resident (they wait for each other), and two
-// grids that each hold part of the compute units would both wait until
-// their polls run out. Calls on one stream are ordered by the stream. While
-// every launch on a device has gone to one stream nothing more is done (an
-// event per launch costs a few microseconds of the layer). The first launch
-// on a second stream waits on the host until the device is idle, so the
-// previous stream's launches are finished without touching that stream (it
-// may no longer exist); from then on an event is recorded after every
-// launch, and a launch on another stream than the previous one waits for
-// it on the device.
+// Two launches whose workgroups wait for each other (this file's expert
+// launch, the one-expert launch) must never run at the same time on one
+// device: each needs all of its workgroups resident, and two grids that each
+// hold part of the compute units would both wait until their polls run out.
+// Calls on one stream are ordered by the stream. While every such launch on
+// a device has gone to one stream nothing more is done (an event per launch
+// costs a few microseconds of the layer). The first launch on a second
+// stream waits on the host until the device is idle, so the previous
+// stream's launches are finished without touching that stream (it may no
+// longer exist); from then on an event is recorded after every launch, and a
+// launch on another stream than the previous one waits for it on the device.
 struct FusedOrder {
   std::mutex mu;
   hipStream_t last = nullptr;
@@ -385,12 +386,7 @@ struct FusedOrder {
 FusedOrder g_fused_order[kMaxDevices];
 }  // namespace
 
-hipError_t launch_moe_experts(const uint16_t *x, const double *logits,
-                              const uint8_t *const *experts, int n, int k,
-                              int hidden, int inter, float *h, float *yp,
-                              uint64_t *slots, uint64_t val, int32_t *idx,
-                              float *w, uint16_t *y, float *y_f32,
-                              hipStream_t s, const float *add, const SharedStage *sh) {
+hipError_t grid_sync_launch(hipStream_t s, const std::function<hipError_t()> &launch) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   FusedOrder &o = g_fused_order[dev];
@@ -410,16 +406,7 @@ hipError_t launch_moe_experts(const uint16_t *x, const double *logits,
       if (e != hipSuccess) return e;
     }
   }
-  // one workgroup per compute unit: the whole grid fits at once
-  if (sh)
-    hipLaunchKernelGGL(moe_experts_kernel<true>, dim3(moe_experts_grid()), dim3(kThreads), 0,
-                       s, x, logits, experts, n, k, hidden, inter, h, yp, slots, val, idx, w,
-                       y, y_f32, sh->ys, sh->hs, sh->shared, sh->n_shared, sh->inter);
-  else
-    hipLaunchKernelGGL(moe_experts_kernel<false>, dim3(moe_experts_grid()), dim3(kThreads), 0,
-                       s, x, logits, experts, n, k, hidden, inter, h, yp, slots, val, idx, w,
-                       y, y_f32, add, nullptr, nullptr, 0, 0);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch();
   if (e != hipSuccess) return e;
   if (o.multi) {
     e = hipEventRecord(o.done, s);
@@ -428,6 +415,26 @@ hipError_t launch_moe_experts(const uint16_t *x, const double *logits,
   o.last = s;
   o.any = true;
   return hipSuccess;
+}
+
+hipError_t launch_moe_experts(const uint16_t *x, const double *logits,
+                              const uint8_t *const *experts, int n, int k,
+                              int hidden, int inter, float *h, float *yp,
+                              uint64_t *slots, uint64_t val, int32_t *idx,
+                              float *w, uint16_t *y, float *y_f32,
+                              hipStream_t s, const float *add, const SharedStage *sh) {
+  // one workgroup per compute unit: the whole grid fits at once
+  return grid_sync_launch(s, [&]() {
+    if (sh)
+      hipLaunchKernelGGL(moe_experts_kernel<true>, dim3(moe_experts_grid()), dim3(kThreads), 0,
+                         s, x, logits, experts, n, k, hidden, inter, h, yp, slots, val, idx, w,
+                         y, y_f32, sh->ys, sh->hs, sh->shared, sh->n_shared, sh->inter);
+    else
+      hipLaunchKernelGGL(moe_experts_kernel<false>, dim3(moe_experts_grid()), dim3(kThreads), 0,
+                         s, x, logits, experts, n, k, hidden, inter, h, yp, slots, val, idx, w,
+                         y, y_f32, add, nullptr, nullptr, 0, 0);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_combine(const float *yp, const float *w, int k, int hidden,

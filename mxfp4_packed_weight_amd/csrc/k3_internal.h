@@ -10,6 +10,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <functional>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -193,6 +195,10 @@ hipError_t launch_shared_down(const float *h, const uint16_t *const *shared, int
 // never reused in the process.
 constexpr int kMaxSyncGrid = 1024;
 constexpr int kMaxDevices = 64;  // per-device state of the library
+// Runs `launch` (which enqueues one grid whose workgroups wait for each
+// other, on stream s) so that no two such grids overlap on the device
+// (k3_expert.hip).
+hipError_t grid_sync_launch(hipStream_t s, const std::function<hipError_t()> &launch);
 unsigned moe_experts_grid();
 // The shared experts' down stage taken inside the expert launch: hs [n][inter]
 // from an earlier launch, ys [hidden] written here and added by the combine.
@@ -209,6 +215,15 @@ hipError_t launch_moe_experts(const uint16_t *x, const double *logits,
                               float *w, uint16_t *y, float *y_f32,
                               hipStream_t s, const float *add = nullptr,
                               const SharedStage *sh = nullptr);
+// One expert in one launch over every compute unit (k3_expert_one.hip):
+// gate/up split along K into expert_one_split() chunks per tile, one
+// hand-off, then down. ws: expert_one_workspace_bytes() (partials, then
+// kMaxSyncGrid arrival words);
+// val: a per-call value.
+int expert_one_split(int hidden, int inter);
+size_t expert_one_workspace_bytes(int hidden, int inter);
+hipError_t launch_expert_one(const uint16_t *x, const uint8_t *expert, int hidden, int inter,
+                             float *y, float *h, void *ws, uint64_t val, hipStream_t s);
 // Calibration read of `bytes` (a multiple of 16) at `buf` (k3_probe.hip).
 hipError_t launch_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s);
 // Pinned host buffer of at least n ints owned by an expert cache

@@ -185,6 +185,82 @@ def test_expert_small_ragged():
     assert normwise(h, h_ref) <= TOL and normwise(y, y_ref) <= TOL
 
 
+def _expert_one_launch(E, x_bf16, hidden, inter):
+    """k3_expert_swiglu_ws (one launch, gate/up split along K): y and h,
+    checked bit-identical over a rerun on the same workspace."""
+    import torch
+    blob = up(K.k3_expert_pack_host(E, hidden, inter))
+    xd = up(x_bf16)
+    ws = empty(K.k3_expert_swiglu_workspace_bytes(hidden, inter), torch.uint8)
+    y = empty(hidden, torch.float32)
+    h = empty(inter, torch.float32)
+    K.k3_expert_swiglu_ws(xd, blob, hidden, inter, y, ws, h=h)
+    y1, h1 = y.cpu().numpy().copy(), h.cpu().numpy().copy()
+    y2 = empty(hidden, torch.float32)
+    K.k3_expert_swiglu_ws(xd, blob, hidden, inter, y2, ws)  # h optional
+    assert np.array_equal(y1.view(np.uint32), y2.cpu().numpy().view(np.uint32)), "rerun differs"
+    return y1, h1
+
+
+# C2 in both exponent ranges; a ragged gate/up tile with G % 4 != 0; the
+# largest hidden with one gate/up tile (chunks of one quad); the largest
+# inter with a one-quad K (one chunk per tile, 128 tiles)
+@pytest.mark.parametrize("hidden,inter,elo,ehi", [(7168, 1536, 120, 134), (7168, 1536, 114, 120),
+                                                  (96, 160, 114, 120), (16384, 32, 114, 120),
+                                                  (128, 4096, 114, 120), (800, 224, 114, 120)])
+def test_expert_one_launch_parity(hidden, inter, elo, ehi):
+    say(f"expert in one launch hidden={hidden} inter={inter} e=[{elo},{ehi}]")
+    E = gen.expert(10, 68, 0, hidden, inter, elo, ehi)
+    x = gen.normal_bf16(gen.key(10, 68, gen.KIND_TOKENS), hidden)
+    y, h = _expert_one_launch(E, x, hidden, inter)
+    oracle.set_threads(16)
+    y_ref, h_ref = oracle.expert_swiglu(E, I.bf16_to_float_bits(x))
+    eh, ey = normwise(h, h_ref), normwise(y, y_ref)
+    say(f"expert in one launch: normwise h {eh:.3e} y {ey:.3e}")
+    assert eh <= TOL and ey <= TOL
+
+
+def test_expert_one_launch_nonfinite_x_in_skipped_group():
+    hidden, inter = 1024, 256
+    say("expert in one launch with NaN/Inf activations inside 255 groups")
+    E = gen.expert(9, 69, 0, hidden, inter, 114, 120)
+    x = gen.normal_bf16(gen.key(9, 69, gen.KIND_TOKENS), hidden).copy()
+    E["gate"][1][:, 3] = 255
+    E["up"][1][:, 3] = 255
+    x[100] = 0x7F80
+    x[101] = 0x7FC0
+    y, h = _expert_one_launch(E, x, hidden, inter)
+    y_ref, h_ref = oracle.expert_swiglu(E, I.bf16_to_float_bits(x))
+    assert np.all(np.isfinite(h)) and np.all(np.isfinite(y))
+    assert normwise(h, h_ref) <= TOL and normwise(y, y_ref) <= TOL
+
+
+def test_expert_one_launch_captured_graph_takes_the_two_launches():
+    """Under stream capture the call records k3_expert_swiglu's two launches:
+    every replay gives their bits."""
+    import torch
+    hidden, inter = 512, 256
+    E = gen.expert(11, 70, 0, hidden, inter, 114, 120)
+    x = gen.normal_bf16(gen.key(11, 70, gen.KIND_TOKENS), hidden)
+    blob = up(K.k3_expert_pack_host(E, hidden, inter))
+    xd = up(x)
+    ws = empty(K.k3_expert_swiglu_workspace_bytes(hidden, inter), torch.uint8)
+    y = empty(hidden, torch.float32)
+    yw, hw = empty(hidden, torch.float32), empty(inter, torch.float32)
+    K.k3_expert_swiglu(xd, blob, hidden, inter, yw, hw)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        K.k3_expert_swiglu_ws(xd, blob, hidden, inter, y, ws, stream=s)
+    for _ in range(3):
+        y.fill_(0.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), yw.cpu().numpy().view(np.uint32))
+
+
 def test_router_logits_and_topk():
     import torch
     n, hidden, T, k = W.N_EXPERTS, W.HIDDEN, 3, W.TOPK
