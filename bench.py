@@ -137,12 +137,13 @@ def main():
                          "(the known-size kernel the HBM byte counters are scaled by)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
-                         "WRITE_SIZE) of a --calib run into profiles/experts_c3_traffic.json")
+                         "WRITE_SIZE) of a --calib run of --workload (c1..c5) into that "
+                         "workload's traffic file under profiles/")
     args = ap.parse_args()
     if args.cache_slots is None:
         args.cache_slots = 640 if args.workload == "c4-cached" else 128
     if args.traffic_summary:
-        traffic_summary(*args.traffic_summary)
+        traffic_summary(*args.traffic_summary, workload=args.workload)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -247,21 +248,9 @@ def main():
     log(f"calibrated read {cal:.1f} GB/s; layer steps p10/p50/p90 "
         f"{spread['p10']:.2f}/{spread['p50']:.2f}/{spread['p90']:.2f} us")
 
-    traffic = None
-    tpath = os.path.join(ROOT, "profiles", TRAFFIC_JSON)
-    if os.path.exists(tpath):
-        with open(tpath) as f:
-            tr = json.load(f)
-        if tr.get("kernel_source_hash") == _kernel_hash():
-            traffic = tr.get("bytes_per_launch")
-
+    traffic = measured_traffic("c3")
     if args.calib:
-        src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copies(dev)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
@@ -381,10 +370,10 @@ def bench_c1_c2(args):
         nbytes, name = mb, "one MXFP4 GEMV, W 256x1024 (139,264 B packed), x fp32"
         xh = W.c1_inputs(0)[2].astype(np.float64)
         t0, n = time.perf_counter(), 0
-        while n < 1000 and time.perf_counter() - t0 < 10:
+        while n < (0 if args.no_cpu_baseline else 1000) and time.perf_counter() - t0 < 10:
             oracle.gemv(*mats[n % nbase], xh)
             n += 1
-        cpu_s = (time.perf_counter() - t0) / n
+        cpu_s = (time.perf_counter() - t0) / max(n, 1)
         cpu_sample = f"{n} oracle GEMVs (fp64, {threads} threads)"
     else:
         hidden, inter, ne = W.HIDDEN, W.INTER, 64
@@ -410,14 +399,16 @@ def bench_c1_c2(args):
         E = W.expert_weights(0, W.C2, 0)
         xf = oracle.bf16_to_f64(W.tokens_bf16(0, W.C2, 1)[0])
         t0, n = time.perf_counter(), 0
-        while n < 10 and time.perf_counter() - t0 < 15:
+        while n < (0 if args.no_cpu_baseline else 10) and time.perf_counter() - t0 < 15:
             oracle.expert_swiglu(E, xf)
             n += 1
-        cpu_s = (time.perf_counter() - t0) / n
+        cpu_s = (time.perf_counter() - t0) / max(n, 1)
         cpu_sample = f"{n} oracle experts (fp64, {threads} threads)"
     value = nbytes / rot / 1e3
     log(f"{args.workload.upper()}: single call {single:.2f} us, rotating {rot:.2f} us "
         f"({value:.1f} GB/s)")
+    if args.calib:
+        calibration_copies(dev)
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(rot / 1e3, 6),
@@ -434,11 +425,12 @@ def bench_c1_c2(args):
         "roofline": {"kernel": "gemv_f32_kernel" if args.workload == "c1"
                      else "expert_one_kernel (k3_expert_swiglu_ws, one launch)",
                      "bound": "hbm", "achieved": round(value, 2), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(value / PEAK_HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(value / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(args.workload),
                      "algorithmic_bytes_per_launch": nbytes},
-        "cpu_baseline": {"value": round(nbytes / cpu_s / 1e9, 4), "unit": "GB/s",
-                         "cores": threads, "kind": "oracle", "host": host_info(),
-                         "sample": cpu_sample},
+        "cpu_baseline": None if args.no_cpu_baseline else {
+            "value": round(nbytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "host": host_info(), "sample": cpu_sample},
     }
     print(json.dumps(with_speedup(out)))
 
@@ -494,6 +486,8 @@ def bench_c4(args):
     value = nbytes / (ms * 1e-3) / 1e9
     log(f"C4 layer: {ms * 1e3:.1f} us/batch, {mean_distinct:.1f} distinct experts, "
         f"{value:.1f} GB/s")
+    if args.calib:
+        calibration_copies(dev)
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
@@ -510,7 +504,7 @@ def bench_c4(args):
         "step_us": spread,
         "roofline": {"kernel": "whole batched layer (k3_moe_layer_from_logits)", "bound": "hbm",
                      "achieved": round(value, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(value / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(value / PEAK_HBM_GBS, 4), "traffic": measured_traffic("c4"),
                      "algorithmic_bytes_per_launch": int(nbytes)},
         "cpu_baseline": None,
     }
@@ -926,6 +920,8 @@ def bench_c5(args):
     flop = 2.0 * T * k * 3 * hidden * inter
     tflops = flop / (ms * 1e-3) / 1e12
     log(f"C5 prefill: {ms:.3f} ms/batch, {value:.1f} GB/s, {tflops:.1f} TFLOP/s")
+    if args.calib:
+        calibration_copies(dev)
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
@@ -943,7 +939,7 @@ def bench_c5(args):
         "mfma_util": round(tflops / PEAK_FP4_TFLOPS, 5),
         "roofline": {"kernel": "whole prefill layer (k3_moe_prefill)", "bound": "hbm",
                      "achieved": round(value, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(value / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(value / PEAK_HBM_GBS, 4), "traffic": measured_traffic("c5"),
                      "algorithmic_bytes_per_launch": int(nbytes),
                      "fp4_tflops": round(tflops, 2), "fp4_peak_tflops": PEAK_FP4_TFLOPS},
         "cpu_baseline": None,
@@ -957,6 +953,38 @@ def bench_c5(args):
 CALIB_BYTES = 1 << 30
 DOMINANT_KERNEL = "moe_experts_kernel"
 TRAFFIC_JSON = "experts_c3_traffic.json"
+
+# Per workload: the kernels of one step (a label and a substring of the
+# kernel's name in a rocprofv3 trace), the kernel that runs once per step
+# (the anchor: every other kernel's dispatch count is taken relative to
+# it), the traffic file under profiles/ and the sources whose hash it was
+# measured at.
+TRAFFIC = {
+    "c1": {"json": "gemv_c1_traffic.json", "anchor": "gemv_f32_kernel",
+           "kernels": {"GEMV": "gemv_f32_kernel"},
+           "sources": ("k3_decode.h", "k3_stream.h", "k3_expert.hip")},
+    "c2": {"json": "expert_one_c2_traffic.json", "anchor": "expert_one_kernel",
+           "kernels": {"one-launch expert": "expert_one_kernel"},
+           "sources": ("k3_decode.h", "k3_stream.h", "k3_sync.h", "k3_expert_one.hip")},
+    "c3": {"json": TRAFFIC_JSON, "anchor": DOMINANT_KERNEL,
+           "kernels": {"expert launch": DOMINANT_KERNEL},
+           "sources": ("k3_decode.h", "k3_stream.h", "k3_topk.h", "k3_sync.h", "k3_expert.hip")},
+    "c4": {"json": "batched_decode_c4_traffic.json", "anchor": "batched_mfma_kernel<false",
+           "kernels": {"top-k": "topk_kernel", "permutation": "permute_kernel",
+                       "gate/up (matrix unit)": "batched_mfma_kernel<false",
+                       "down, items <= 5 pairs": "batched_mfma_kernel<true, 1>",
+                       "down, larger items": "batched_mfma_kernel<true, 3>",
+                       "combine": "combine_batched_kernel"},
+           "sources": ("k3_decode.h", "k3_stream.h", "k3_topk.h", "k3_router.hip",
+                       "k3_batched.hip", "k3_batched_mfma.hip")},
+    "c5": {"json": "prefill_c5_traffic.json", "anchor": "prefill_gemm_kernel<true>",
+           "kernels": {"top-k": "topk_kernel", "permutation": "permute_kernel",
+                       "x quantiser": "quant_kernel", "gate/up GEMM": "prefill_gemm_kernel<true>",
+                       "down GEMM": "prefill_gemm_kernel<false>",
+                       "combine": "combine_batched_kernel"},
+           "sources": ("k3_decode.h", "k3_stream.h", "k3_topk.h", "k3_router.hip",
+                       "k3_batched.hip", "k3_prefill.hip")},
+}
 
 
 def _pmc_rows(path, counter):
@@ -973,36 +1001,81 @@ def _pmc_rows(path, counter):
     return rows
 
 
-def traffic_summary(fetch_csv, write_csv):
-    """HBM bytes per expert launch from FETCH_SIZE and WRITE_SIZE (KiB per
-    dispatch), each scaled by what the counter reads for the 1 GiB calibration
-    copy (CALIB_BYTES read and CALIB_BYTES written)."""
-    out = {"kernel": DOMINANT_KERNEL, "kernel_source_hash": _kernel_hash(),
-           "calibration": f"device-to-device copy of {CALIB_BYTES} bytes",
-           "algorithmic_bytes_per_launch": 16 * BYTES_PER_EXPERT}
+def traffic_summary(fetch_csv, write_csv, workload="c3"):
+    """HBM bytes per step of a workload's kernels from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by what the counter reads for
+    the 1 GiB calibration copy (CALIB_BYTES read and CALIB_BYTES written).
+    Per kernel: mean KiB per dispatch x dispatches per anchor dispatch."""
+    spec = TRAFFIC[workload]
+    out = {"workload": workload, "anchor_kernel": spec["anchor"],
+           "kernel_source_hash": _kernel_hash(workload),
+           "calibration": f"device-to-device copy of {CALIB_BYTES} bytes", "kernels": {}}
+    if workload == "c3":
+        out["kernel"] = DOMINANT_KERNEL
+        out["algorithmic_bytes_per_launch"] = 16 * BYTES_PER_EXPERT
+    total = 0.0
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _pmc_rows(path, name)
-        gu = [v for k, g, v in rows if DOMINANT_KERNEL in k]
-        calib = [v for k, g, v in rows if "copy" in k.lower()]
-        calib = sorted(calib)[-3:]  # the three largest copies are the calibration
-        if not gu or not calib:
-            raise SystemExit(f"{path}: no {DOMINANT_KERNEL} or calibration dispatches")
+        calib = sorted(v for k, g, v in rows if "copy" in k.lower())[-3:]
+        anchor = [v for k, g, v in rows if spec["anchor"] in k]
+        if not anchor or not calib:
+            raise SystemExit(f"{path}: no {spec['anchor']} or calibration dispatches")
         factor = (sum(calib) / len(calib)) * 1024.0 / CALIB_BYTES
-        out[name] = {"kernel_kib_mean": sum(gu) / len(gu), "dispatches": len(gu),
-                     "calib_kib_mean": sum(calib) / len(calib), "scale": factor,
-                     "bytes_per_launch": sum(gu) / len(gu) * 1024.0 / factor}
-    out["bytes_per_launch"] = out["FETCH_SIZE"]["bytes_per_launch"] + \
-        out["WRITE_SIZE"]["bytes_per_launch"]
-    path = os.path.join(ROOT, "profiles", TRAFFIC_JSON)
+        per = {}
+        for label, sub in spec["kernels"].items():
+            vals = [v for k, g, v in rows if sub in k]
+            if not vals:
+                continue
+            mult = len(vals) / len(anchor)
+            bpd = sum(vals) / len(vals) * 1024.0 / factor
+            per[label] = {"kernel_kib_mean": sum(vals) / len(vals), "dispatches": len(vals),
+                          "dispatches_per_step": round(mult, 4),
+                          "bytes_per_dispatch": bpd, "bytes_per_step": bpd * mult}
+            out["kernels"].setdefault(label, {})[name] = per[label]
+        step = sum(v["bytes_per_step"] for v in per.values())
+        out[name] = {"calib_kib_mean": sum(calib) / len(calib), "scale": factor,
+                     "bytes_per_step": step}
+        if workload == "c3":
+            out[name]["bytes_per_launch"] = step
+        total += step
+    out["bytes_per_step"] = total
+    if workload == "c3":
+        out["bytes_per_launch"] = total
+    path = os.path.join(ROOT, "profiles", spec["json"])
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
 
 
-def _kernel_hash():
+def measured_traffic(workload):
+    """Bytes per step from the workload's traffic file, while the kernel
+    sources still hash to the value it was measured at; else None."""
+    path = os.path.join(ROOT, "profiles", TRAFFIC[workload]["json"])
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tr = json.load(f)
+    if tr.get("kernel_source_hash") != _kernel_hash(workload):
+        return None
+    return tr.get("bytes_per_step", tr.get("bytes_per_launch"))
+
+
+def calibration_copies(dev):
+    """Three 1 GiB device-to-device copies: the known-size kernel the HBM
+    byte counters are scaled by."""
+    import torch
+    src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def _kernel_hash(workload="c3"):
     import hashlib
     hsh = hashlib.sha256()
-    for f in ("k3_decode.h", "k3_stream.h", "k3_topk.h", "k3_sync.h", "k3_expert.hip"):
+    for f in TRAFFIC[workload]["sources"]:
         with open(os.path.join(ROOT, "mxfp4_packed_weight_amd", "csrc", f), "rb") as fh:
             hsh.update(fh.read())
     return hsh.hexdigest()[:16]
