@@ -221,6 +221,16 @@ k3_status k3_router_topk(const double *logits, const float *bias, int T,
 k3_status k3_router_topk_f32(const float *logits, const float *bias, int T,
                              int n_experts, int k, int32_t *idx, float *w,
                              k3_stream_t stream);
+/* k3_router_topk with the renormalised weights multiplied by routed_scale:
+ * w_j = fp32((s_j / sum s) * routed_scale), the product in fp64. The pages
+ * name the routing bias but no scale on the routed weights ([ZOR] "How is
+ * the C engine actually built?", invariant 3), so the layer calls use 1; a
+ * model with a routed scaling factor takes these weights into the
+ * stage-by-stage calls (k3_expert_gate_up, k3_expert_down, k3_moe_combine).
+ * routed_scale must be positive and finite (K3_ERR_CONFIG otherwise). */
+k3_status k3_router_topk_scaled(const double *logits, const float *bias, int T,
+                                int n_experts, int k, double routed_scale,
+                                int32_t *idx, float *w, k3_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Whole decode MoE layer for one token: router GEMV -> sigmoid top-k ->

@@ -57,6 +57,7 @@ SIGNATURES = [
     ("k3_router", _i, [_vp, _vp, _i, _i, _i, _vp, _vp]),
     ("k3_router_topk", _i, [_vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
     ("k3_router_topk_f32", _i, [_vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
+    ("k3_router_topk_scaled", _i, [_vp, _vp, _i, _i, _i, ctypes.c_double, _vp, _vp, _vp]),
     ("k3_moe_workspace_bytes", _sz, [_i, _i, _i, _i, _i]),
     ("k3_moe_layer", _i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
     ("k3_moe_layer_ex", _i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
@@ -268,6 +269,11 @@ def k3_router_topk(logits, bias, T, n_experts, k, idx, w, stream=None):
 def k3_router_topk_f32(logits, bias, T, n_experts, k, idx, w, stream=None):
     _call("k3_router_topk_f32", _dp(logits), _dp(bias), T, n_experts, k, _dp(idx), _dp(w),
           _stream(stream))
+
+
+def k3_router_topk_scaled(logits, bias, T, n_experts, k, routed_scale, idx, w, stream=None):
+    _call("k3_router_topk_scaled", _dp(logits), _dp(bias), T, n_experts, k, float(routed_scale),
+          _dp(idx), _dp(w), _stream(stream))
 
 
 def k3_moe_workspace_bytes(T, n_experts, hidden, inter, k):

@@ -585,6 +585,23 @@ k3_status k3_router_topk(const double *logits, const float *bias, int T,
   return K3_OK;
 }
 
+k3_status k3_router_topk_scaled(const double *logits, const float *bias, int T,
+                                int n_experts, int k, double routed_scale,
+                                int32_t *idx, float *w, k3_stream_t stream) {
+  const char *fn = "k3_router_topk_scaled";
+  K3_NEED_PTR(fn, logits);
+  K3_NEED_PTR(fn, idx);
+  K3_NEED_PTR(fn, w);
+  if (bias && !aligned16(bias))
+    return fail(K3_ERR_ARG, "%s: bias is not 16-byte aligned", fn);
+  K3_NEED(fn, routed_scale > 0.0 && routed_scale < 1e30,
+          "%s: routed_scale=%g is not a positive finite factor", fn, routed_scale);
+  if (k3_status s = check_routing(fn, T, n_experts, k)) return s;
+  K3_LAUNCH(fn, launch_topk_f64(logits, bias, T, n_experts, k, idx, w, stream,
+                                routed_scale));
+  return K3_OK;
+}
+
 k3_status k3_router_topk_f32(const float *logits, const float *bias, int T,
                              int n_experts, int k, int32_t *idx, float *w,
                              k3_stream_t stream) {

@@ -232,9 +232,10 @@ hipError_t launch_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipS
 int32_t *cache_selection_buffer(k3_cache_t c, size_t n);
 hipError_t launch_router(const uint16_t *x, const uint16_t *R, int T,
                          int hidden, int n, double *logits, hipStream_t s);
+// scale multiplies the renormalised weights (1: none).
 hipError_t launch_topk_f64(const double *logits, const float *bias, int T,
                            int n, int k, int32_t *idx, float *w,
-                           hipStream_t s);
+                           hipStream_t s, double scale = 1.0);
 hipError_t launch_topk_f32(const float *logits, const float *bias, int T,
                            int n, int k, int32_t *idx, float *w,
                            hipStream_t s);

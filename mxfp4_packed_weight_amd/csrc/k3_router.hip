@@ -41,13 +41,13 @@ __global__ __launch_bounds__(64) void topk_kernel(const LT *__restrict__ logits,
                                                   const float *__restrict__ bias,
                                                   int n, int k,
                                                   int32_t *__restrict__ idx,
-                                                  float *__restrict__ w) {
+                                                  float *__restrict__ w, double scale) {
   __shared__ TopkLds tk;
   const int lane = threadIdx.x;
   const int t = blockIdx.x;
   int sel;
   float wt;
-  topk_wave<KPL, LT>(logits + (size_t)t * n, bias, n, k, tk, &sel, &wt);
+  topk_wave<KPL, LT>(logits + (size_t)t * n, bias, n, k, tk, &sel, &wt, scale);
   if (lane < k) {
     idx[(size_t)t * k + lane] = sel;
     w[(size_t)t * k + lane] = wt;
@@ -56,12 +56,13 @@ __global__ __launch_bounds__(64) void topk_kernel(const LT *__restrict__ logits,
 
 template <typename LT>
 hipError_t launch_topk(const LT *logits, const float *bias, int T, int n,
-                       int k, int32_t *idx, float *w, hipStream_t s) {
+                       int k, int32_t *idx, float *w, hipStream_t s,
+                       double scale = 1.0) {
   const int kpl = (n + 63) / 64;
 #define K3_TOPK_CASE(KPL)                                                      \
   if (kpl <= KPL) {                                                            \
     hipLaunchKernelGGL((topk_kernel<KPL, LT>), dim3(T), dim3(64), 0, s,       \
-                       logits, bias, n, k, idx, w);                            \
+                       logits, bias, n, k, idx, w, scale);                     \
     return hipGetLastError();                                                  \
   }
   K3_TOPK_CASE(1)
@@ -90,8 +91,8 @@ hipError_t launch_router(const uint16_t *x, const uint16_t *R, int T,
 
 hipError_t launch_topk_f64(const double *logits, const float *bias, int T,
                            int n, int k, int32_t *idx, float *w,
-                           hipStream_t s) {
-  return launch_topk(logits, bias, T, n, k, idx, w, s);
+                           hipStream_t s, double scale) {
+  return launch_topk(logits, bias, T, n, k, idx, w, s, scale);
 }
 
 hipError_t launch_topk_f32(const float *logits, const float *bias, int T,

@@ -116,13 +116,15 @@ __device__ __forceinline__ void wave_lds_sync() {
 // Top-k of one token's n logits held in registers by one wave: raw[i] is the
 // logit of expert lane + 64 i (entries at or past n are ignored). On return
 // lanes < k hold the j-th selection in *sel_out and its renormalised weight
-// in *wt_out (rank order). `tk` is the wave's LDS scratch; with a bias,
-// logit_of(e) returns expert e's logit (the weights use unbiased scores).
+// times `scale` in *wt_out (rank order). `tk` is the wave's LDS scratch; with
+// a bias, logit_of(e) returns expert e's logit (the weights use unbiased
+// scores).
 template <int KPL, typename LT, class LogitOf>
 __device__ __forceinline__ void topk_core(const LT (&raw)[KPL],
                                           const float *__restrict__ bias, int n,
                                           int k, TopkLds &tk, LogitOf logit_of,
-                                          int *sel_out, float *wt_out) {
+                                          int *sel_out, float *wt_out,
+                                          double scale = 1.0) {
   const int lane = threadIdx.x & 63;
   float b[KPL];
   if (bias) {
@@ -209,7 +211,7 @@ __device__ __forceinline__ void topk_core(const LT (&raw)[KPL],
   double sum = 0.0;
   for (int j = 0; j < k; ++j) sum += tk.ranked[j];
   *sel_out = sel;
-  *wt_out = (float)(s / sum);
+  *wt_out = (float)((s / sum) * scale);
 }
 
 // The same with the logits read from memory (L[e], e < n).
@@ -217,13 +219,13 @@ template <int KPL, typename LT>
 __device__ __forceinline__ void topk_wave(const LT *__restrict__ L,
                                           const float *__restrict__ bias, int n,
                                           int k, TopkLds &tk, int *sel_out,
-                                          float *wt_out) {
+                                          float *wt_out, double scale = 1.0) {
   const int lane = threadIdx.x & 63;
   LT raw[KPL];
 #pragma unroll
   for (int i = 0; i < KPL; ++i) raw[i] = L[min(lane + 64 * i, n - 1)];
   topk_core<KPL, LT>(raw, bias, n, k, tk, [&](int e) { return (double)L[e]; },
-                     sel_out, wt_out);
+                     sel_out, wt_out, scale);
 }
 
 // Top-k of one token's n <= blockDim logits by a whole workgroup (16 waves),

@@ -330,6 +330,31 @@ def test_topk_cases(case):
         assert np.max(np.abs(w_h[t] - ww)) <= 1e-6
 
 
+@pytest.mark.parametrize("scale", [1.0, 2.5, 0.125])
+def test_topk_routed_scale(scale):
+    """k3_router_topk_scaled: the same selection as k3_router_topk (bias
+    included), weights = the oracle's renormalised weights times the scale;
+    scale 1 gives k3_router_topk's bits."""
+    import torch
+    T, n, k = 5, 896, 16
+    L = gen.normal_f32(gen.key(3, 71, gen.KIND_LOGITS), T * n).reshape(T, n).astype(np.float64)
+    bias = W.routing_bias(3, n, 0.5).astype(np.float32)
+    idx = empty((T, k), torch.int32)
+    w = empty((T, k), torch.float32)
+    K.k3_router_topk_scaled(up(L), up(bias), T, n, k, scale, idx, w)
+    idx0 = empty((T, k), torch.int32)
+    w0 = empty((T, k), torch.float32)
+    K.k3_router_topk(up(L), up(bias), T, n, k, idx0, w0)
+    gi, gw = idx.cpu().numpy(), w.cpu().numpy()
+    assert np.array_equal(gi, idx0.cpu().numpy())
+    if scale == 1.0:
+        assert np.array_equal(gw.view(np.uint32), w0.cpu().numpy().view(np.uint32))
+    for t in range(T):
+        ri, rw = oracle.topk(L[t], k, bias.astype(np.float64))
+        assert np.array_equal(gi[t], ri)
+        assert np.max(np.abs(gw[t] - scale * rw)) <= 1e-6 * scale
+
+
 def test_hbm_read_probe_runs_and_refuses():
     """The calibration read streams a buffer and leaves the sink alone
     (ordinary data does not fold to its magic value); bad sizes are refused."""

@@ -166,3 +166,13 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(K, "_lib", None)
     with pytest.raises(K.K3LibraryMissing):
         K.k3_mxfp4_packed_bytes(64, 64)
+
+
+def test_routed_scale_refusals(L):
+    """k3_router_topk_scaled refuses a scale that is not a positive finite
+    factor before any launch."""
+    s = ctypes.c_void_p(0)
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        rc = L.k3_router_topk_scaled(_fake(1), None, 2, 896, 16, bad, _fake(2), _fake(3), s)
+        assert rc == K.K3_ERR_CONFIG, (bad, rc)
+        assert "routed_scale" in K.last_error()
