@@ -133,14 +133,21 @@ k3_status k3_expert_pack(const uint8_t *gate_nib_d, const uint8_t *gate_sc_d,
 
 /* ------------------------------------------------------------------------
  * y[rows] = W[rows][cols] . x[cols] read straight from the packed bytes,
- * never expanded to floats in memory ([SAT] "Reduction one"): the codes of a
- * group are converted in registers, multiplied by x with fp32 accumulation,
- * and the group's exponent is applied once to the group's sum; exponent 255
- * contributes nothing. fp32 accumulation in a fixed order: each row is
- * reduced by one workgroup along a fixed tree, so results are bit-identical
- * from run to run on one device (the pages' fixed-order rule, [SAT] "A
- * floating-point contract, not a convention"). x fp32 [cols], tiles from
- * k3_mxfp4_pack, y fp32 [rows]. No workspace.
+ * never expanded to floats in memory ([SAT] "Reduction one"). The codes go
+ * to gfx950's block-scaled matrix instruction as they are stored (E2M1, each
+ * group's exponent byte as its block scale), against x cut into six 4-bit
+ * fixed-point digits per value below the largest exponent of its group of
+ * 32: a bf16 value within 2^-16 of its group's largest is carried exactly,
+ * any other value to within half an fp32 ulp of the group's largest. Every
+ * block sum is exact and the sums accumulate in fp32; exponent 255
+ * contributes nothing. A workgroup whose x groups hold a non-finite value
+ * or a largest value outside [2^-87, 2^122) multiplies on the vector ALU
+ * instead: the group's codes converted in registers, multiplied by x in
+ * fp32, the exponent applied once to the group's sum. fp32 accumulation in
+ * a fixed order: each row is reduced by one workgroup along a fixed tree,
+ * so results are bit-identical from run to run on one device (the pages'
+ * fixed-order rule, [SAT] "A floating-point contract, not a convention").
+ * x fp32 [cols], tiles from k3_mxfp4_pack, y fp32 [rows]. No workspace.
  * ---------------------------------------------------------------------- */
 k3_status k3_mxfp4_gemv(const float *x, const uint8_t *tiles, int rows,
                         int cols, float *y, k3_stream_t stream);
@@ -159,8 +166,10 @@ k3_status k3_expert_swiglu(const uint16_t *x, const uint8_t *expert,
  * workgroup; their row partials go to the workspace, and the workgroups that
  * own down tiles (whose first bytes they load before the gate/up work) sum
  * each row's partials in chunk order, form h and multiply their tile by it.
- * Summation order differs from k3_expert_swiglu's, so the two differ in the
- * last bits; each is bit-identical from run to run on one device. h fp32
+ * The products are the vector-ALU form described at k3_mxfp4_gemv (one
+ * expert is bound by its chain of memory round trips, not by arithmetic),
+ * and the summation order differs from k3_expert_swiglu's, so the two differ
+ * in the last bits; each is bit-identical from run to run on one device. h fp32
  * [inter] is optional (NULL: not written). ws: at least
  * k3_expert_swiglu_workspace_bytes(hidden, inter) bytes; calls sharing a
  * workspace must not overlap. The launch needs its whole grid resident; it

@@ -4,9 +4,9 @@
 // The matrix kernels are CU-persistent: the grid has one workgroup of kNW
 // waves per compute unit, each workgroup owns a contiguous range of 64-row
 // tiles (of one matrix, or of the k selected experts back to back) and
-// streams it through run_rows (k3_stream.h), which converts the codes in
-// registers and multiplies them by wave-uniform activations on the vector
-// ALU. Each row's sum has one fixed order that depends on the shape and grid
+// streams it through run_rows (k3_stream.h), which multiplies the packed
+// codes on the matrix unit against the activations' digits, built by the
+// workgroup in LDS while its first loads are in flight (k3_digits.h). Each row's sum has one fixed order that depends on the shape and grid
 // only, so reruns are bit-identical (the pages' rule that every row is summed
 // by one owner in one order, [SAT] "A floating-point contract, not a
 // convention"). The work is a memory-bound stream of packed bytes ("the wait
@@ -25,22 +25,83 @@ namespace {
 
 constexpr int kThreads = kNW * 64;
 
+// LDS digits of the activation vectors of slots [s_lo, s_hi], as many as
+// fit (n); `all` if every slot fits.
+struct SlotDigits {
+  lds_u8 *buf;
+  int s_lo, n, stride;
+  bool all;
+  __device__ const lds_u8 *at(int s) const { return buf + (s - s_lo) * stride; }
+};
+
+// The slots of tiles [t0, t1) of a stack of T tiles per slot.
+__device__ __forceinline__ SlotDigits slot_digits(uint8_t *buf, int t0, int t1, int T, int G4) {
+  SlotDigits d;
+  d.buf = (lds_u8 *)buf;
+  d.stride = digit_bytes(G4);
+  d.s_lo = t0 / T;
+  const int want = t0 < t1 ? (t1 - 1) / T - d.s_lo + 1 : 0;
+  d.n = min(want, kDigitLds / d.stride);
+  d.all = d.n == want;
+  return d;
+}
+
+// Builds every slot's digits (load(s, i) = element i of slot s's vector) and
+// returns, the same in every thread, whether the matrix route may run: every
+// slot fits and no group is flagged.
+template <class Load>
+__device__ __forceinline__ bool build_slot_digits(const SlotDigits &d, int G, int G4, Load load) {
+  bool flagged = false;
+  for (int i = 0; i < d.n; ++i)
+    flagged |= build_digits([&](int k) { return load(d.s_lo + i, k); }, G, G4, d.buf + i * d.stride);
+  return __syncthreads_or(flagged) == 0 && d.all;
+}
+
+// The bf16 activation vector x (hidden values) of the gate/up stages: its
+// bytes go to LDS behind the digits by direct copies when both fit (true),
+// for the digits to be computed there later.
+__device__ __forceinline__ bool stage_x(const uint16_t *x, int hidden, const SlotDigits &d) {
+  const int at = d.stride, bytes = 2 * hidden;
+  if (d.n < 1 || at + bytes > kDigitLds) return false;
+  dma_to_lds(reinterpret_cast<const uint8_t *>(x), d.buf + at, bytes);
+  return true;
+}
+
+// x's digits into D's one vector (from the LDS copy when staged, else from
+// device memory); whether the matrix route may run (as build_slot_digits).
+__device__ __forceinline__ bool x_ready(const uint16_t *x, bool staged, int G, int G4,
+                                        const SlotDigits &d) {
+  if (staged) {
+    const bool flagged = compute_digits_bf16(d.buf + d.stride, G, G4, d.buf);
+    return __syncthreads_or(flagged) == 0 && d.all;
+  }
+  return build_slot_digits(d, G, G4,
+                           [&](int, int i) { return __uint_as_float((uint32_t)x[i] << 16); });
+}
+
 __global__ __launch_bounds__(kThreads) void gemv_f32_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ tiles, int rows,
     int cols, float *__restrict__ y) {
   __shared__ float part[kPartFloats];
+  __shared__ __attribute__((aligned(16))) uint8_t dig[kDigitLds];
   const MatLayout m = mat_layout(rows, cols);
   int t0, t1;
   wg_range(m.ntiles, &t0, &t1);
-  run_rows(
+  // one vector for every tile (wider than the buffer: the vector-ALU route)
+  const SlotDigits D = slot_digits(dig, 0, 1, 1, m.G4);
+  bool mx = false;
+  stream_tiles(
       t0, t1, m.G, m.G4,
       [&](int t) { return tiles + (size_t)t * m.tile_bytes; },
+      [&](int) { return D.at(0); },
       [&](u32x4 w, int g, int) { return group_dot_f32(w, x + (size_t)32 * g); },
       [&](int t, int lane, float s) {
         const int row = t * kTileRows + lane;
         if (row < rows) y[row] = s;
       },
-      part);
+      part, NoPre(), NoPre(),
+      [&]() { mx = build_slot_digits(D, m.G, m.G4, [&](int, int i) { return x[i]; }); },
+      [&]() { return mx; });
 }
 
 __device__ __forceinline__ const uint8_t *expert_base(
@@ -56,17 +117,21 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(
     const int32_t *__restrict__ idx, const uint8_t *__restrict__ single,
     int nslots, int hidden, int inter, float *__restrict__ h) {
   __shared__ float part[kPartFloats];
+  __shared__ __attribute__((aligned(16))) uint8_t dig[kDigitLds];
   const ExpertLayout L = expert_layout(hidden, inter);
   const int T = L.gu.ntiles;
   const uint32_t *xp = reinterpret_cast<const uint32_t *>(x);
   int t0, t1;
   wg_range(nslots * T, &t0, &t1);
-  run_rows(
+  const SlotDigits D = slot_digits(dig, 0, 1, 1, L.gu.G4);  // x, shared by every slot
+  bool mx = false;
+  stream_tiles(
       t0, t1, L.gu.G, L.gu.G4,
       [&](int t) {
         return expert_base(experts, idx, single, t / T) +
                (size_t)(t % T) * L.gu.tile_bytes;
       },
+      [&](int) { return D.at(0); },
       [&](u32x4 w, int g, int) { return group_dot_bf16(w, xp + (size_t)16 * g); },
       [&](int t, int lane, float s) {
         const float u = __shfl_down(s, 32);  // lane l<32: gate row; l+32: up row
@@ -74,7 +139,8 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(
         gu_lane_row(t % T, lane, &is_up, &row);
         if (lane < 32 && row < inter) h[(size_t)(t / T) * inter + row] = silu(s) * u;
       },
-      part);
+      part, NoPre(), NoPre(), [&]() { mx = x_ready(x, false, L.gu.G, L.gu.G4, D); },
+      [&]() { return mx; });
 }
 
 // yp[j][r] = W_down(e_j)[r] . h[j], tiles of the k slots back to back (a
@@ -85,16 +151,20 @@ __global__ __launch_bounds__(kThreads) void down_kernel(
     const int32_t *__restrict__ idx, const uint8_t *__restrict__ single,
     int nslots, int hidden, int inter, float *__restrict__ yp) {
   __shared__ float part[kPartFloats];
+  __shared__ __attribute__((aligned(16))) uint8_t dig[kDigitLds];
   const ExpertLayout L = expert_layout(hidden, inter);
   const int T = L.down.ntiles;
   int t0, t1;
   wg_range(nslots * T, &t0, &t1);
-  run_rows(
+  const SlotDigits D = slot_digits(dig, t0, t1, T, L.down.G4);
+  bool mx = false;
+  stream_tiles(
       t0, t1, L.down.G, L.down.G4,
       [&](int t) {
         return expert_base(experts, idx, single, t / T) + L.down_offset +
                (size_t)(t % T) * L.down.tile_bytes;
       },
+      [&](int t) { return D.at(t / T); },
       [&](u32x4 w, int g, int t) {
         return group_dot_f32(w, h + (size_t)(t / T) * inter + (size_t)32 * g);
       },
@@ -102,7 +172,12 @@ __global__ __launch_bounds__(kThreads) void down_kernel(
         const int row = (t % T) * kTileRows + lane;
         if (row < hidden) yp[(size_t)(t / T) * hidden + row] = s;
       },
-      part);
+      part, NoPre(), NoPre(),
+      [&]() {
+        mx = build_slot_digits(D, L.down.G, L.down.G4,
+                               [&](int sl, int i) { return h[(size_t)sl * inter + i]; });
+      },
+      [&]() { return mx; });
 }
 
 // The decode layer's first expert stage with the selection folded in:
@@ -117,23 +192,30 @@ __global__ __launch_bounds__(kThreads) void gate_up_routed_kernel(
     int inter, float *__restrict__ h, int32_t *__restrict__ idx_out,
     float *__restrict__ w_out) {
   __shared__ float part[kPartFloats];
+  __shared__ __attribute__((aligned(16))) uint8_t dig[kDigitLds];
   __shared__ TopkWgLds tk;
+  const ExpertLayout L = expert_layout(hidden, inter);
+  const SlotDigits D = slot_digits(dig, 0, 1, 1, L.gu.G4);
+  const bool staged = stage_x(x, hidden, D);  // x's bytes on their way to LDS
   topk_wg<kNW>(logits, n, k, tk);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's copies are in
+  __syncthreads();
   if (blockIdx.x == 0 && (int)threadIdx.x < k) {
     idx_out[threadIdx.x] = tk.sel[threadIdx.x];
     w_out[threadIdx.x] = tk.wt[threadIdx.x];
   }
-  const ExpertLayout L = expert_layout(hidden, inter);
   const int T = L.gu.ntiles;
   const uint32_t *xp = reinterpret_cast<const uint32_t *>(x);
   int t0, t1;
   wg_range(k * T, &t0, &t1);
-  run_rows(
+  bool mx = false;
+  stream_tiles(
       t0, t1, L.gu.G, L.gu.G4,
       [&](int t) {
         const int e = __builtin_amdgcn_readfirstlane(tk.sel[t / T]);
         return ldc(experts + e) + (size_t)(t % T) * L.gu.tile_bytes;
       },
+      [&](int) { return D.at(0); },
       [&](u32x4 w, int g, int) { return group_dot_bf16(w, xp + (size_t)16 * g); },
       [&](int t, int lane, float s) {
         const float u = __shfl_down(s, 32);  // lane l<32: gate row; l+32: up row
@@ -141,7 +223,8 @@ __global__ __launch_bounds__(kThreads) void gate_up_routed_kernel(
         gu_lane_row(t % T, lane, &is_up, &row);
         if (lane < 32 && row < inter) h[(size_t)(t / T) * inter + row] = silu(s) * u;
       },
-      part);
+      part, NoPre(), NoPre(), [&]() { mx = x_ready(x, staged, L.gu.G, L.gu.G4, D); },
+      [&]() { return mx; });
 }
 
 // The decode layer's expert work in one launch, after the router: top-k
@@ -179,27 +262,34 @@ __global__ __launch_bounds__(kThreads) void moe_experts_kernel(
     const float *add, const float *__restrict__ hs,
     const uint16_t *const *__restrict__ shared, int n_shared, int inter_s) {
   __shared__ float part[kPartFloats];
+  __shared__ __attribute__((aligned(16))) uint8_t dig[kDigitLds];  // x's, then h's
   __shared__ TopkWgLds tk;
   __shared__ int bad;
   if (threadIdx.x == 0) bad = 0;
+  const ExpertLayout L = expert_layout(hidden, inter);
+  const SlotDigits D = slot_digits(dig, 0, 1, 1, L.gu.G4);
+  const bool staged = stage_x(x, hidden, D);  // x's bytes on their way to LDS
   topk_wg<kNW>(logits, n, k, tk);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's copies are in
+  __syncthreads();
   if (blockIdx.x == 0 && (int)threadIdx.x < k) {
     idx_out[threadIdx.x] = tk.sel[threadIdx.x];
     w_out[threadIdx.x] = tk.wt[threadIdx.x];
   }
   const int G = gridDim.x, lane = threadIdx.x & 63;
-  const ExpertLayout L = expert_layout(hidden, inter);
   const uint32_t *xp = reinterpret_cast<const uint32_t *>(x);
   const int Tg = L.gu.ntiles, total_gu = k * Tg;
   {
     int t0, t1;
     wg_range(total_gu, &t0, &t1);
-    run_rows(
+    bool mx = false;
+    stream_tiles(
         t0, t1, L.gu.G, L.gu.G4,
         [&](int t) {
           const int e = __builtin_amdgcn_readfirstlane(tk.sel[t / Tg]);
           return ldc(experts + e) + (size_t)(t % Tg) * L.gu.tile_bytes;
         },
+        [&](int) { return D.at(0); },
         [&](u32x4 w, int g, int) { return group_dot_bf16(w, xp + (size_t)16 * g); },
         [&](int t, int ln, float s) {
           const float u = __shfl_down(s, 32);  // lane l<32: gate row; l+32: up row
@@ -208,7 +298,8 @@ __global__ __launch_bounds__(kThreads) void moe_experts_kernel(
           if (ln < 32 && row < inter)
             st_dev(h + (size_t)(t / Tg) * inter + row, silu(s) * u);
         },
-        part);
+        part, NoPre(), NoPre(), [&]() { mx = x_ready(x, staged, L.gu.G, L.gu.G4, D); },
+        [&]() { return mx; });
   }
   arrive(slots, val);
   if constexpr (kShared) {
@@ -224,12 +315,15 @@ __global__ __launch_bounds__(kThreads) void moe_experts_kernel(
   int t0, t1;
   wg_range(total, &t0, &t1);
   const float *hb = h;
-  run_rows(
+  const SlotDigits Dd = slot_digits(dig, t0, t1, Td, L.down.G4);
+  bool mxd = false;
+  stream_tiles(
       t0, t1, L.down.G, L.down.G4,
       [&](int t) {
         const int e = __builtin_amdgcn_readfirstlane(tk.sel[t / Td]);
         return ldc(experts + e) + L.down_offset + (size_t)(t % Td) * L.down.tile_bytes;
       },
+      [&](int t) { return Dd.at(t / Td); },
       [&](u32x4 w, int g, int t) {
         return group_dot_f32(w, hb + (size_t)(t / Td) * inter + (size_t)32 * g);
       },
@@ -246,7 +340,13 @@ __global__ __launch_bounds__(kThreads) void moe_experts_kernel(
         }
         __syncthreads();
         hb = after_wait(hb);
-      });
+      },
+      NoPre(),
+      [&]() {  // h of this workgroup's slots, device-coherent, into digits
+        mxd = build_slot_digits(Dd, L.down.G, L.down.G4,
+                                [&](int sl, int i) { return ld_dev(hb + (size_t)sl * inter + i); });
+      },
+      [&]() { return mxd; });
   uint64_t *done = slots + kMaxSyncGrid;
   arrive(done, val);
 
