@@ -131,6 +131,48 @@ def test_gemv_nan_scale_contains_nonfinite_x():
     assert normwise(y, ref) <= TOL
 
 
+def test_gemv_activation_groups_outside_digit_range():
+    """Activation groups whose largest value is below 2^-87 or at least 2^122
+    (beyond the exponents of the matrix unit's activation digits) send the
+    workgroups to the vector-ALU products; results still match the oracle.
+    That route sums a group's unscaled products in fp32, so the large group
+    has one non-zero code per row (a finite group sum); weights scaled by
+    2^-27 keep every product finite."""
+    say("gemv activation groups of 2^-100 and 2^123")
+    rows, cols = 200, 512
+    nib, sc = gen.mxfp4_matrix(12, 71, rows, cols, 98, 102)
+    nib = nib.copy()
+    nib[:, 64:80] = 0  # group 4 (elements 128..159): only element 128's code stays
+    nib[:, 64] = gen.mxfp4_matrix(12, 73, rows, 32)[0][:, 0] & 0x0F
+    x = gen.normal_f32(gen.key(12, 71, gen.KIND_TOKENS), cols).astype(np.float64)
+    x[32:64] *= 2.0 ** -100  # group 1: largest value far below 2^-87
+    x[128] = 1.5 * 2.0 ** 123  # group 4: largest value above 2^122
+    x = x.astype(np.float32)
+    y = gpu_gemv(nib, sc, x)
+    ref = oracle.gemv(nib, sc, x.astype(np.float64))
+    assert np.all(np.isfinite(y))
+    assert normwise(y, ref) <= TOL
+
+
+def test_gemv_extreme_exponent_bytes_on_the_matrix_unit():
+    """Exponent bytes 0, 1, 2, 126..128, 252, 253, 254 mixed in every row, with
+    activations around 2^-58 (inside the digits' range, so the matrix unit
+    multiplies): each group scaled by the instruction's E8M0 scale, results
+    within fp32 range of the oracle."""
+    say("gemv exponent bytes 0..2, 126..128, 252..254 on the matrix unit")
+    rows, cols = 192, 1024
+    nib, _ = gen.mxfp4_matrix(13, 72, rows, cols)
+    rng = np.random.default_rng(1372)
+    sc = rng.choice(np.array([0, 1, 2, 126, 127, 128, 252, 253, 254], np.uint8),
+                    size=(rows, cols // 32))
+    x = (gen.normal_f32(gen.key(13, 72, gen.KIND_TOKENS), cols).astype(np.float64) *
+         2.0 ** -58).astype(np.float32)
+    y = gpu_gemv(nib, sc, x)
+    ref = oracle.gemv(nib, sc, x.astype(np.float64))
+    assert np.all(np.isfinite(y))
+    assert normwise(y, ref) <= TOL
+
+
 def _expert_on_gpu(E, x_bf16, hidden, inter):
     import torch
     blob = up(K.k3_expert_pack_host(E, hidden, inter))
