@@ -962,13 +962,14 @@ TRAFFIC_JSON = "experts_c3_traffic.json"
 TRAFFIC = {
     "c1": {"json": "gemv_c1_traffic.json", "anchor": "gemv_f32_kernel",
            "kernels": {"GEMV": "gemv_f32_kernel"},
-           "sources": ("k3_decode.h", "k3_stream.h", "k3_expert.hip")},
+           "sources": ("k3_decode.h", "k3_digits.h", "k3_stream.h", "k3_expert.hip")},
     "c2": {"json": "expert_one_c2_traffic.json", "anchor": "expert_one_kernel",
            "kernels": {"one-launch expert": "expert_one_kernel"},
            "sources": ("k3_decode.h", "k3_stream.h", "k3_sync.h", "k3_expert_one.hip")},
     "c3": {"json": TRAFFIC_JSON, "anchor": DOMINANT_KERNEL,
            "kernels": {"expert launch": DOMINANT_KERNEL},
-           "sources": ("k3_decode.h", "k3_stream.h", "k3_topk.h", "k3_sync.h", "k3_expert.hip")},
+           "sources": ("k3_decode.h", "k3_digits.h", "k3_stream.h", "k3_topk.h", "k3_sync.h",
+                       "k3_expert.hip")},
     "c4": {"json": "batched_decode_c4_traffic.json", "anchor": "batched_mfma_kernel<false",
            "kernels": {"top-k": "topk_kernel", "permutation": "permute_kernel",
                        "gate/up (matrix unit)": "batched_mfma_kernel<false",
