@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void gemv_f32_kernel(
   const SlotDigits D = slot_digits(dig, 0, 1, 1, m.G4);
   bool mx = false;
   stream_tiles(
-      t0, t1, m.G, m.G4,
+      matrix_stream(m.ntiles, m.G4), t0, t1, m.G, m.G4,
       [&](int t) { return tiles + (size_t)t * m.tile_bytes; },
       [&](int) { return D.at(0); },
       [&](u32x4 w, int g, int) { return group_dot_f32(w, x + (size_t)32 * g); },
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(
   const SlotDigits D = slot_digits(dig, 0, 1, 1, L.gu.G4);  // x, shared by every slot
   bool mx = false;
   stream_tiles(
-      t0, t1, L.gu.G, L.gu.G4,
+      matrix_stream(nslots * T, L.gu.G4), t0, t1, L.gu.G, L.gu.G4,
       [&](int t) {
         return expert_base(experts, idx, single, t / T) +
                (size_t)(t % T) * L.gu.tile_bytes;
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void down_kernel(
   const SlotDigits D = slot_digits(dig, t0, t1, T, L.down.G4);
   bool mx = false;
   stream_tiles(
-      t0, t1, L.down.G, L.down.G4,
+      matrix_stream(nslots * T, L.down.G4), t0, t1, L.down.G, L.down.G4,
       [&](int t) {
         return expert_base(experts, idx, single, t / T) + L.down_offset +
                (size_t)(t % T) * L.down.tile_bytes;
@@ -196,7 +196,8 @@ __global__ __launch_bounds__(kThreads) void gate_up_routed_kernel(
   __shared__ TopkWgLds tk;
   const ExpertLayout L = expert_layout(hidden, inter);
   const SlotDigits D = slot_digits(dig, 0, 1, 1, L.gu.G4);
-  const bool staged = stage_x(x, hidden, D);  // x's bytes on their way to LDS
+  // x's bytes on their way to LDS, when the gate/up tiles take the matrix route
+  const bool staged = matrix_stream(k * L.gu.ntiles, L.gu.G4) && stage_x(x, hidden, D);
   topk_wg<kNW>(logits, n, k, tk);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's copies are in
   __syncthreads();
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_routed_kernel(
   wg_range(k * T, &t0, &t1);
   bool mx = false;
   stream_tiles(
-      t0, t1, L.gu.G, L.gu.G4,
+      matrix_stream(k * T, L.gu.G4), t0, t1, L.gu.G, L.gu.G4,
       [&](int t) {
         const int e = __builtin_amdgcn_readfirstlane(tk.sel[t / T]);
         return ldc(experts + e) + (size_t)(t % T) * L.gu.tile_bytes;
@@ -268,7 +269,8 @@ __global__ __launch_bounds__(kThreads) void moe_experts_kernel(
   if (threadIdx.x == 0) bad = 0;
   const ExpertLayout L = expert_layout(hidden, inter);
   const SlotDigits D = slot_digits(dig, 0, 1, 1, L.gu.G4);
-  const bool staged = stage_x(x, hidden, D);  // x's bytes on their way to LDS
+  // x's bytes on their way to LDS, when the gate/up tiles take the matrix route
+  const bool staged = matrix_stream(k * L.gu.ntiles, L.gu.G4) && stage_x(x, hidden, D);
   topk_wg<kNW>(logits, n, k, tk);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's copies are in
   __syncthreads();
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void moe_experts_kernel(
     wg_range(total_gu, &t0, &t1);
     bool mx = false;
     stream_tiles(
-        t0, t1, L.gu.G, L.gu.G4,
+        matrix_stream(total_gu, L.gu.G4), t0, t1, L.gu.G, L.gu.G4,
         [&](int t) {
           const int e = __builtin_amdgcn_readfirstlane(tk.sel[t / Tg]);
           return ldc(experts + e) + (size_t)(t % Tg) * L.gu.tile_bytes;
@@ -318,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void moe_experts_kernel(
   const SlotDigits Dd = slot_digits(dig, t0, t1, Td, L.down.G4);
   bool mxd = false;
   stream_tiles(
-      t0, t1, L.down.G, L.down.G4,
+      matrix_stream(total, L.down.G4), t0, t1, L.down.G, L.down.G4,
       [&](int t) {
         const int e = __builtin_amdgcn_readfirstlane(tk.sel[t / Td]);
         return ldc(experts + e) + L.down_offset + (size_t)(t % Td) * L.down.tile_bytes;

@@ -232,15 +232,28 @@ __device__ __forceinline__ bool run_rows(int t_begin, int t_end, int G, int G4, 
   return true;
 }
 
-// One stack of tiles: on the matrix unit when ok() after ready(), else on
-// the vector ALU (pre() is then called again; fetch(), ready() and ok() are
-// not).
+// Whether a stack's tiles are long enough per workgroup for the matrix
+// route: at least kMinMatrixQuads quads (the ceiling of tiles / grid,
+// times G4). A shorter stream would spend longer building the activation
+// digits than the matrix unit saves. The answer depends on the shape and
+// the grid only, so a fused launch and the separate launches of the same
+// stage (grid min(tiles, compute units) against compute units) agree.
+constexpr int kMinMatrixQuads = 64;
+__device__ __forceinline__ bool matrix_stream(int tiles, int G4) {
+  const int per_wg = (tiles + (int)gridDim.x - 1) / (int)gridDim.x;
+  return per_wg * G4 >= kMinMatrixQuads;
+}
+
+// One stack of tiles: on the matrix unit when `matrix` and ok() after
+// ready(), else on the vector ALU (after a refusal pre() is called again;
+// fetch(), ready() and ok() are not).
 template <class Base, class Dig, class Dot, class Epi, class Pre, class Fetch, class Ready,
           class Ok>
-__device__ __forceinline__ void stream_tiles(int t_begin, int t_end, int G, int G4, Base base,
-                                             Dig dig, Dot dot, Epi epi, float *part, Pre pre,
-                                             Fetch fetch, Ready ready, Ok ok) {
-  if (!run_rows<true>(t_begin, t_end, G, G4, base, dig, dot, epi, part, pre, fetch, ready, ok))
+__device__ __forceinline__ void stream_tiles(bool matrix, int t_begin, int t_end, int G, int G4,
+                                             Base base, Dig dig, Dot dot, Epi epi, float *part,
+                                             Pre pre, Fetch fetch, Ready ready, Ok ok) {
+  if (!matrix ||
+      !run_rows<true>(t_begin, t_end, G, G4, base, dig, dot, epi, part, pre, fetch, ready, ok))
     run_rows<false>(t_begin, t_end, G, G4, base, dig, dot, epi, part, pre, NoPre(), NoPre(),
                     []() { return true; });
 }

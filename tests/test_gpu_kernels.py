@@ -87,9 +87,13 @@ def test_gemv_c1_parity():
     assert err <= TOL
 
 
+# K of 8192 and more: 64 or more quads per workgroup, the matrix-unit products;
+# the shorter ones: the vector ALU
 @pytest.mark.parametrize("rows,cols,elo,ehi", [(100, 224, 120, 134), (63, 96, 10, 20),
                                                (65, 160, 230, 240), (1, 32, 127, 127),
-                                               (300, 7168, 120, 134), (129, 1536, 114, 120)])
+                                               (300, 7168, 120, 134), (129, 1536, 114, 120),
+                                               (130, 8192, 120, 134), (64, 16384, 114, 120),
+                                               (65, 8224, 10, 20)])
 def test_gemv_shapes_and_exponent_range(rows, cols, elo, ehi):
     say(f"gemv rows={rows} cols={cols} e=[{elo},{ehi}]")
     nib, sc = gen.mxfp4_matrix(5, 62, rows, cols, elo, ehi)
@@ -99,10 +103,12 @@ def test_gemv_shapes_and_exponent_range(rows, cols, elo, ehi):
     assert normwise(y, ref) <= TOL
 
 
-def test_gemv_nan_scale_finite_x():
-    """Exponent 255 with finite activations (the matrix-unit path)."""
-    say("gemv exponent 255, finite activations")
-    rows, cols = 130, 384
+@pytest.mark.parametrize("cols", [384, 8192])
+def test_gemv_nan_scale_finite_x(cols):
+    """Exponent 255 with finite activations (K = 8192: the matrix-unit
+    products, whose 255 groups are zeroed in the registers)."""
+    say(f"gemv exponent 255, finite activations, cols={cols}")
+    rows = 130
     nib, sc = gen.mxfp4_matrix(8, 66, rows, cols)
     sc = sc.copy()
     sc[:, 3] = 255
@@ -139,7 +145,7 @@ def test_gemv_activation_groups_outside_digit_range():
     has one non-zero code per row (a finite group sum); weights scaled by
     2^-27 keep every product finite."""
     say("gemv activation groups of 2^-100 and 2^123")
-    rows, cols = 200, 512
+    rows, cols = 200, 8192  # 64 quads per workgroup: the matrix route is tried first
     nib, sc = gen.mxfp4_matrix(12, 71, rows, cols, 98, 102)
     nib = nib.copy()
     nib[:, 64:80] = 0  # group 4 (elements 128..159): only element 128's code stays
@@ -160,7 +166,7 @@ def test_gemv_extreme_exponent_bytes_on_the_matrix_unit():
     multiplies): each group scaled by the instruction's E8M0 scale, results
     within fp32 range of the oracle."""
     say("gemv exponent bytes 0..2, 126..128, 252..254 on the matrix unit")
-    rows, cols = 192, 1024
+    rows, cols = 192, 8192
     nib, _ = gen.mxfp4_matrix(13, 72, rows, cols)
     rng = np.random.default_rng(1372)
     sc = rng.choice(np.array([0, 1, 2, 126, 127, 128, 252, 253, 254], np.uint8),
