@@ -54,7 +54,7 @@ __device__ __forceinline__ bool build_slot_digits(const SlotDigits &d, int G, in
   bool flagged = false;
   for (int i = 0; i < d.n; ++i)
     flagged |= build_digits([&](int k) { return load(d.s_lo + i, k); }, G, G4, d.buf + i * d.stride);
-  return __syncthreads_or(flagged) == 0 && d.all;
+  return !wg_any(flagged) && d.all;
 }
 
 // The bf16 activation vector x (hidden values) of the gate/up stages: its
@@ -73,7 +73,7 @@ __device__ __forceinline__ bool x_ready(const uint16_t *x, bool staged, int G, i
                                         const SlotDigits &d) {
   if (staged) {
     const bool flagged = compute_digits_bf16(d.buf + d.stride, G, G4, d.buf);
-    return __syncthreads_or(flagged) == 0 && d.all;
+    return !wg_any(flagged) && d.all;
   }
   return build_slot_digits(d, G, G4,
                            [&](int, int i) { return __uint_as_float((uint32_t)x[i] << 16); });
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void moe_experts_kernel(
           const int c_hi = tile_owner(((t1 - 1) / Td + 1) * Tg - 1, total_gu, G);
           if (!wave_wait_range(slots, c_lo, c_hi - c_lo + 1, val) && lane == 0) bad = 1;
         }
-        __syncthreads();
+        lds_barrier();  // wave 0's poll has returned; the quads stay in flight
         hb = after_wait(hb);
       },
       NoPre(),

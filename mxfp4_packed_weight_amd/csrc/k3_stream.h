@@ -44,6 +44,32 @@ constexpr int kPartFloats = kMaxTPW * kNW * 64;  // per-wave row partials
 // encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int kWaitVmcnt0 = 0x0F70;
 
+// A workgroup barrier that orders LDS accesses only. __syncthreads() also
+// waits for every global load the wave has in flight (vmcnt(0)), which would
+// drain the quads of the ring issued just before it, and make every wave wait
+// for the slowest wave's quads.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Whether v holds in any thread of the workgroup, the same answer in every
+// thread, through LDS behind lds_barrier(). (__syncthreads_or reads the
+// workgroup size from the dispatch's argument block with vector loads and
+// waits for them, and with them for every load in flight.) The flags are
+// reused: two calls are separated by a barrier.
+__device__ __forceinline__ bool wg_any(bool v) {
+  __shared__ uint32_t any_flag[kNW];
+  const bool w = __ballot(v) != 0ull;
+  if ((threadIdx.x & 63) == 0) any_flag[wave_id()] = w ? 1u : 0u;
+  lds_barrier();
+  uint32_t a = 0u;
+#pragma unroll
+  for (int i = 0; i < kNW; ++i) a |= any_flag[i];
+  return a != 0u;
+}
+
 struct NoPre {
   __device__ void operator()() const {}
 };
