@@ -92,64 +92,69 @@ __device__ __forceinline__ float digit_unit(uint32_t emax) {
   return __uint_as_float((277u - emax) << 23);
 }
 
-// Group state of one activation group: its largest exponent field and
-// whether any value is non-zero, from per-lane partial values, reduced over
-// W consecutive lanes (W = 8 or 32).
-template <int W>
-__device__ __forceinline__ uint32_t group_max(uint32_t v) {
+// Largest of v over the four lanes of this lane's DPP quad: the four lanes
+// that hold one activation group.
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
   v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));  // lane ^ 1
   v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));  // lane ^ 2
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false)); // other half of 8
-  if constexpr (W == 32) {
-    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));  // other half of 16
-    const auto w = __builtin_amdgcn_permlane16_swap(v, v, false, false);  // rows 2i <-> 2i+1
-    v = max(v, max((uint32_t)w[0], (uint32_t)w[1]));
-  }
   return v;
 }
 
-// The slice exponent bytes, flag and zero of a group: flagged if a value is
-// non-finite or the non-zero group's largest exponent field is outside
-// [40, 248].
-__device__ __forceinline__ void group_meta(uint32_t emax, uint32_t nz, uint32_t &lo4,
-                                           uint32_t &hi4) {
-  const bool flag = emax > 248u || (nz != 0u && emax < 40u);
-  if (flag || nz == 0u) {
-    lo4 = 0x7F7F7F7Fu;
-    hi4 = 0x7F7Fu | (flag ? 0x10000u : 0u);
-    return;
-  }
-  const uint32_t e0 = emax + 6u;  // slice p: (Emax - 3 - 4p + 9) + 127
-  lo4 = e0 | ((e0 - 4u) << 8) | ((e0 - 8u) << 16) | ((e0 - 12u) << 24);
-  hi4 = (e0 - 16u) | ((e0 - 20u) << 8);
+// The eight meta bytes of a group from m, the fp32 bits of its largest
+// magnitude (its largest exponent field is m >> 23, as magnitudes order like
+// their bits): the slice exponent bytes (Emax - 3 - 4p + 9) + 127 =
+// emax + 6 - 4p for p = 0..5, a flag byte, 0. Flagged: a non-finite value,
+// or a non-zero group whose emax is outside [40, 248]. A flagged or all-zero
+// group gets exponent bytes 127.
+__device__ __forceinline__ void group_meta(uint32_t m, uint32_t &lo4, uint32_t &hi4) {
+  const uint32_t emax = m >> 23;
+  const bool flag = emax > 248u || (m != 0u && emax < 40u);
+  const bool live = !flag && m != 0u;
+  // emax + 6 in all four bytes; no byte borrows below, as emax + 6 >= 46
+  const uint32_t e4 = __builtin_amdgcn_perm(0u, emax + 6u, 0u);
+  lo4 = live ? e4 - 0x0C080400u : 0x7F7F7F7Fu;
+  hi4 = live ? (e4 & 0xFFFFu) - 0x1410u : (flag ? 0x17F7Fu : 0x7F7Fu);
 }
 
 // Building the digits of one activation vector of G groups (G4 quads in the
-// buffer; groups past G are zero digits with finite exponents) is cut in two
-// so that the loads can be issued early and the arithmetic done while other
-// loads are in flight. Eight threads per group, four values each: task t of
-// the vector is values [4t, 4t + 4), thread i takes tasks i, i + blockDim.x,
-// ... Every thread of the workgroup (kNW waves) takes part in both steps.
-constexpr int kDigitTasks = (kMaxDigitQuads * 32 + kNW * 64 - 1) / (kNW * 64);
+// buffer; groups past G get zero digits and finite exponents). Four lanes
+// per group (one DPP quad), eight values each: task t of the vector is
+// values [8t, 8t + 8), quarter t & 3 of group t >> 2; thread i takes tasks
+// i, i + kDigitThreads, ... Every thread of the workgroup (kNW waves) takes
+// part. The loads are a step of their own so that a caller can issue them
+// early and do the arithmetic while other loads are in flight.
+constexpr int kDigitThreads = kNW * 64;
+constexpr int kDigitTasks = (kMaxDigitQuads * 16 + kDigitThreads - 1) / kDigitThreads;
 
-// Values of this thread's tasks as loaded: four fp32 (W = 4) or four bf16
-// packed in pairs (W = 2, fewer registers to hold while other loads fly).
+// This thread's tasks as loaded: eight fp32 (W = 8) or eight bf16 packed in
+// pairs, the lower half first (W = 4).
 template <int W>
 struct DigitFetch {
   uint32_t r[kDigitTasks][W];
-  __device__ __forceinline__ uint32_t bits(int k, int i) const {  // fp32 bits of value i
-    if constexpr (W == 4) return r[k][i];
+  // fp32 bits of value i of pass k
+  __device__ __forceinline__ uint32_t bits(int k, int i) const {
+    if constexpr (W == 8) return r[k][i];
     return (i & 1) ? (r[k][i >> 1] & 0xFFFF0000u) : (r[k][i >> 1] << 16);
+  }
+  // sign bits of values 4h..4h+3 of pass k, in bit 7 of bytes 0..3
+  __device__ __forceinline__ uint32_t signs(int k, int h) const {
+    uint32_t s;
+    if constexpr (W == 8)
+      s = __builtin_amdgcn_perm(r[k][4 * h + 1], r[k][4 * h], 0x0C0C0703u) |
+          __builtin_amdgcn_perm(r[k][4 * h + 3], r[k][4 * h + 2], 0x07030C0Cu);
+    else
+      s = __builtin_amdgcn_perm(r[k][2 * h + 1], r[k][2 * h], 0x07050301u);
+    return s & 0x80808080u;
   }
 };
 
-// Step one: load(t, r) fills r[0..W) with task t's values (t < 8 G).
+// Step one: load(t, r) fills r[0..W) with task t's values (t < 4 G).
 template <int W, class Load>
-__device__ __forceinline__ void fetch_digits(Load load, int G, int G4, DigitFetch<W> &f) {
+__device__ __forceinline__ void fetch_digits(Load load, int G, DigitFetch<W> &f) {
 #pragma unroll
   for (int k = 0; k < kDigitTasks; ++k) {
-    const int task = (int)threadIdx.x + k * (int)blockDim.x;
-    if (task < 8 * G) {
+    const int task = (int)threadIdx.x + k * kDigitThreads;
+    if (task < 4 * G) {
       load(task, f.r[k]);
     } else {
 #pragma unroll
@@ -160,44 +165,52 @@ __device__ __forceinline__ void fetch_digits(Load load, int G, int G4, DigitFetc
 
 // Step two: the digits into dst. Returns (per thread) whether this thread
 // wrote a flagged group; the caller synchronises before the digits are read.
+// A flagged group's digit bytes are left undefined: its workgroup streams
+// on the vector ALU and never reads them.
 template <int W>
 __device__ __forceinline__ bool compute_digits(const DigitFetch<W> &f, int G4, lds_u8 *dst) {
-  const int n = 32 * G4;
+  const int n = 16 * G4;  // tasks, those of the padding groups included
   bool flagged = false;
 #pragma unroll
   for (int k = 0; k < kDigitTasks; ++k) {
-    if (k * (int)blockDim.x >= n) break;  // uniform
-    const int task = (int)threadIdx.x + k * (int)blockDim.x, gi = task >> 3, a = task & 7;
-    uint32_t u[4], ev = 0u, mag = 0u;
+    if (k * kDigitThreads >= n) break;  // uniform
+    const int task = (int)threadIdx.x + k * kDigitThreads, gi = task >> 2, a = task & 3;
+    uint32_t u[8], m = 0u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
       u[i] = f.bits(k, i);
-      ev = max(ev, (u[i] >> 23) & 255u);
-      mag = max(mag, u[i] & 0x7FFFFFFFu);
+      m = max(m, u[i] & 0x7FFFFFFFu);
     }
-    // the group's eight threads are eight consecutive lanes of one wave
-    const uint32_t emax = group_max<8>(ev), nz = group_max<8>(mag);
+    m = quad_max(m);
     if (task >= n) continue;
     uint32_t lo4, hi4;
-    group_meta(emax, nz, lo4, hi4);  // a group past G reads as all zero
-    const bool live = (hi4 >> 16) == 0u && nz != 0u;
-    const float unit = digit_unit(live ? emax : 127u);
-    uint32_t F[4], sgn = 0u;
+    group_meta(m, lo4, hi4);  // a group past G reads as all zero
+    // finite for every group that is not flagged; a zero group's values
+    // give zero digits with it
+    const float unit = digit_unit(m >> 23);
+    uint32_t F[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      F[i] = live ? digit_mag(u[i], unit) : 0u;
-      sgn |= (u[i] >> 31) << (8 * i + 7);
-    }
+    for (int i = 0; i < 8; ++i) F[i] = digit_mag(u[i], unit);
     const int q = gi >> 2, j = gi & 3;
-    lds_u8 *sl = dst + q * kSliceQuadBytes + 32 * j + 4 * a;
+    lds_u8 *sl = dst + q * kSliceQuadBytes + 32 * j + 8 * a;
+    uint32_t S[kDigits][2];  // slice p, values 4h..4h+3
 #pragma unroll
-    for (int kb = 2; kb >= 0; --kb) {  // byte kb of the 24 bits: slices 4 - 2kb, 5 - 2kb
-      const uint32_t sel = (uint32_t)kb | ((uint32_t)(4 + kb) << 8) | 0x0C0C0000u;
-      const uint32_t Bk = __builtin_amdgcn_perm(F[1], F[0], sel) |
-                          (__builtin_amdgcn_perm(F[3], F[2], sel) << 16);
-      const int p = 4 - 2 * kb;
-      *(lds_u32 *)(sl + p * 128) = ((Bk >> 4) & 0x0F0F0F0Fu) | sgn;
-      *(lds_u32 *)(sl + (p + 1) * 128) = (Bk & 0x0F0F0F0Fu) | sgn;
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t sgn = f.signs(k, h);
+#pragma unroll
+      for (int kb = 2; kb >= 0; --kb) {  // byte kb of the 24 bits: slices 4 - 2kb, 5 - 2kb
+        const uint32_t sel = (uint32_t)kb | ((uint32_t)(4 + kb) << 8) | 0x0C0C0000u;
+        const uint32_t Bk = __builtin_amdgcn_perm(F[4 * h + 1], F[4 * h], sel) |
+                            (__builtin_amdgcn_perm(F[4 * h + 3], F[4 * h + 2], sel) << 16);
+        S[4 - 2 * kb][h] = ((Bk >> 4) & 0x0F0F0F0Fu) | sgn;
+        S[5 - 2 * kb][h] = (Bk & 0x0F0F0F0Fu) | sgn;
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < kDigits; ++p) {
+      lds_u32 *d = (lds_u32 *)(sl + p * 128);
+      d[0] = S[p][0];
+      d[1] = S[p][1];
     }
     if (a == 0) {
       lds_u32 *meta = (lds_u32 *)(dst + digit_meta_off(G4) + kGroupMeta * gi);
@@ -213,13 +226,13 @@ __device__ __forceinline__ bool compute_digits(const DigitFetch<W> &f, int G4, l
 // element i as an exact fp32 value.
 template <class Load>
 __device__ __forceinline__ bool build_digits(Load load, int G, int G4, lds_u8 *dst) {
-  DigitFetch<4> f;
-  fetch_digits<4>(
-      [&](int t, uint32_t(&r)[4]) {
+  DigitFetch<8> f;
+  fetch_digits<8>(
+      [&](int t, uint32_t(&r)[8]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) r[i] = __float_as_uint(load(4 * t + i));
+        for (int i = 0; i < 8; ++i) r[i] = __float_as_uint(load(8 * t + i));
       },
-      G, G4, f);
+      G, f);
   return compute_digits(f, G4, dst);
 }
 
@@ -239,23 +252,20 @@ __device__ __forceinline__ void dma_to_lds(const uint8_t *src, lds_u8 *dst, int 
 }
 
 // Digits of a bf16 vector of G groups already copied to LDS (xs, 2 bytes
-// per value) into dst; as compute_digits.
+// per value, 16-byte aligned) into dst; as compute_digits.
 __device__ __forceinline__ bool compute_digits_bf16(const lds_u8 *xs, int G, int G4,
                                                     lds_u8 *dst) {
-  DigitFetch<2> f;
-  fetch_digits<2>(
-      [&](int t, uint32_t(&r)[2]) {
-        r[0] = ((const lds_u32 *)xs)[2 * t];
-        r[1] = ((const lds_u32 *)xs)[2 * t + 1];
+  DigitFetch<4> f;
+  fetch_digits<4>(
+      [&](int t, uint32_t(&r)[4]) {
+        const u32x4 v = ((const lds_u4 *)xs)[t];
+        r[0] = v[0];
+        r[1] = v[1];
+        r[2] = v[2];
+        r[3] = v[3];
       },
-      G, G4, f);
+      G, f);
   return compute_digits(f, G4, dst);
-}
-
-// Loader of four consecutive bf16 values, packed in pairs.
-__device__ __forceinline__ void load4_bf16(const uint16_t *x, int t, uint32_t (&r)[2]) {
-  r[0] = reinterpret_cast<const uint32_t *>(x)[2 * t];
-  r[1] = reinterpret_cast<const uint32_t *>(x)[2 * t + 1];
 }
 
 // 4 x 4 transpose of (register, 16-lane row): afterwards register m of lane
