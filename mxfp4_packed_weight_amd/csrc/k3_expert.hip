@@ -271,13 +271,9 @@ __global__ __launch_bounds__(kThreads) void moe_experts_kernel(
   const SlotDigits D = slot_digits(dig, 0, 1, 1, L.gu.G4);
   // x's bytes on their way to LDS, when the gate/up tiles take the matrix route
   const bool staged = matrix_stream(k * L.gu.ntiles, L.gu.G4) && stage_x(x, hidden, D);
-  topk_wg<kNW>(logits, n, k, tk);
+  topk_wg<kNW, false>(logits, n, k, tk);  // the weights come during the wait for h
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's copies are in
   __syncthreads();
-  if (blockIdx.x == 0 && (int)threadIdx.x < k) {
-    idx_out[threadIdx.x] = tk.sel[threadIdx.x];
-    w_out[threadIdx.x] = tk.wt[threadIdx.x];
-  }
   const int G = gridDim.x, lane = threadIdx.x & 63;
   const uint32_t *xp = reinterpret_cast<const uint32_t *>(x);
   const int Tg = L.gu.ntiles, total_gu = k * Tg;
@@ -354,6 +350,15 @@ __global__ __launch_bounds__(kThreads) void moe_experts_kernel(
 
   const int last = (k - 1) * Td;
   const int r_lo = max(t0 - last, 0), r_hi = min(t1 - last, Td);
+  // The routing weights (lane j < k: rank j's), in the registers of each wave
+  // that needs them: here they are off the path to the experts' loads, and
+  // a combining wave usually waits for other workgroups' partials anyway.
+  const bool publish = blockIdx.x == 0 && wave_id() == kNW - 1;
+  const float wl = r_lo + wave_id() < r_hi || publish ? topk_wg_weight_lane(tk, k) : 0.f;
+  if (publish && lane < k) {
+    idx_out[lane] = tk.sel[lane];
+    w_out[lane] = wl;
+  }
   for (int r = r_lo + wave_id(); r < r_hi; r += kNW) {
     const int owner = lane < k ? tile_owner(lane * Td + r, total, G) : 0;
     if (!wave_wait_owners(done, owner, k, val) && lane == 0) bad = 1;
@@ -372,7 +377,9 @@ __global__ __launch_bounds__(kThreads) void moe_experts_kernel(
           v[j] = j0 + j < k ? ld_dev(yp + (size_t)(j0 + j) * hidden + row) : 0.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          if (j0 + j < k) acc = fmaf(tk.wt[j0 + j], v[j], acc);
+          if (j0 + j < k)
+            acc = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j0 + j)),
+                       v[j], acc);
       }
       if (kShared)
         acc += ld_dev(add + row);  // the shared experts' output, from this launch

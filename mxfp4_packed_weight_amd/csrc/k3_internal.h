@@ -160,7 +160,8 @@ struct TopkWgLds {
   double sel_key[K3_MAX_TOPK], ranked[K3_MAX_TOPK];
   int sel[K3_MAX_TOPK];
   float wt[K3_MAX_TOPK];
-  TopkLds tk;  // the single-wave fallback
+  int wt_later;  // the weights are left to topk_wg_weights
+  TopkLds tk;    // the single-wave fallback
 };
 // The decode layer's first expert stage with top-k folded in (k3_expert.hip).
 hipError_t launch_gate_up_routed(const uint16_t *x, const double *logits,

@@ -228,6 +228,19 @@ __device__ __forceinline__ void topk_wave(const LT *__restrict__ L,
                      sel_out, wt_out, scale);
 }
 
+// Weights of a ranked selection (s.sel_key, rank order) in one wave: the
+// scores renormalised, summed in rank order (as topk_core without a bias:
+// the key is the logit).
+__device__ __forceinline__ void topk_wg_weights_wave(TopkWgLds &s, int k) {
+  const int lane = threadIdx.x & 63;
+  const double sc = lane < k ? sigmoid_d(s.sel_key[lane]) : 0.0;
+  if (lane < k) s.ranked[lane] = sc;
+  wave_lds_sync();
+  double sum = 0.0;
+  for (int j = 0; j < k; ++j) sum += s.ranked[j];
+  if (lane < k) s.wt[lane] = (float)(sc / sum);
+}
+
 // Top-k of one token's n <= blockDim logits by a whole workgroup (16 waves),
 // one expert per thread: the selection and weights of topk_core, with the
 // three steps spread over the waves so that no single wave walks the keys.
@@ -240,8 +253,10 @@ __device__ __forceinline__ void topk_wave(const LT *__restrict__ L,
 //   3. each wave ranks every candidate against 4 others; the counts add up
 //      in LDS to the exact (key desc, index asc) rank.
 // More than 64 candidates (many equal keys) take topk_core on wave 0.
-// Result in s.sel / s.wt (rank order, lanes < k) after a barrier.
-template <int NWAVES>
+// Result in s.sel / s.wt (rank order, lanes < k) after a barrier. With
+// kWeights false the weights may be left to topk_wg_weights, so that a
+// caller can start on the selected experts first.
+template <int NWAVES, bool kWeights = true>
 __device__ void topk_wg(const double *__restrict__ L, int n, int k, TopkWgLds &s) {
   static_assert(NWAVES * 4 >= 64, "each wave compares against 4 columns");
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -323,14 +338,8 @@ __device__ void topk_wg(const double *__restrict__ L, int n, int k, TopkWgLds &s
         }
       }
       wave_lds_sync();
-      // weights from the scores, renormalised, summed in rank order (as
-      // topk_core without a bias: the key is the logit)
-      const double sc = lane < k ? sigmoid_d(s.sel_key[lane]) : 0.0;
-      if (lane < k) s.ranked[lane] = sc;
-      wave_lds_sync();
-      double sum = 0.0;
-      for (int j = 0; j < k; ++j) sum += s.ranked[j];
-      if (lane < k) s.wt[lane] = (float)(sc / sum);
+      if constexpr (kWeights) topk_wg_weights_wave(s, k);
+      if (lane == 0) s.wt_later = kWeights ? 0 : 1;
     }
   } else if (w == 0) {
     int e;
@@ -340,8 +349,22 @@ __device__ void topk_wg(const double *__restrict__ L, int n, int k, TopkWgLds &s
       s.sel[lane] = e;
       s.wt[lane] = wt;
     }
+    if (lane == 0) s.wt_later = 0;
   }
   __syncthreads();
+}
+
+// The weights of topk_wg's selection in the calling wave's registers: lane
+// j < k returns rank j's weight, computed here when topk_wg left them (the
+// same operations and order as topk_wg_weights_wave), else read from s.wt.
+// Any wave, any time after topk_wg returned; LDS is only read.
+__device__ __forceinline__ float topk_wg_weight_lane(const TopkWgLds &s, int k) {
+  const int lane = threadIdx.x & 63;
+  if (!s.wt_later) return lane < k ? s.wt[lane] : 0.f;
+  const double sc = lane < k ? sigmoid_d(s.sel_key[lane]) : 0.0;
+  double sum = 0.0;
+  for (int j = 0; j < k; ++j) sum += readlane_d(sc, j);
+  return lane < k ? (float)(sc / sum) : 0.f;
 }
 
 }  // namespace k3
