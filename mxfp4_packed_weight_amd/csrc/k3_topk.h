@@ -257,7 +257,7 @@ __device__ __forceinline__ void topk_wg_weights_wave(TopkWgLds &s, int k) {
 // kWeights false the weights may be left to topk_wg_weights, so that a
 // caller can start on the selected experts first.
 template <int NWAVES, bool kWeights = true>
-__device__ void topk_wg(const double *__restrict__ L, int n, int k, TopkWgLds &s) {
+__device__ __forceinline__ void topk_wg(const double *__restrict__ L, int n, int k, TopkWgLds &s) {
   static_assert(NWAVES * 4 >= 64, "each wave compares against 4 columns");
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   double key = -INFINITY;
