@@ -273,9 +273,13 @@ __device__ __forceinline__ void topk_wg(const double *__restrict__ L, int n, int
   }
   __syncthreads();
   // 1. column maxima (each wave, redundantly), then 4 comparisons per lane.
+  uint32_t col[NWAVES];
+#pragma unroll
+  for (int i = 0; i < NWAVES; ++i) col[i] = s.okey[lane + 64 * i];
+  __builtin_amdgcn_sched_barrier(0);  // every read in flight before the first use
   uint32_t um = 0;
 #pragma unroll
-  for (int i = 0; i < NWAVES; ++i) um = max(um, s.okey[lane + 64 * i]);
+  for (int i = 0; i < NWAVES; ++i) um = max(um, col[i]);
   {
     int gt = 0, ge = 0;
 #pragma unroll
@@ -316,16 +320,18 @@ __device__ __forceinline__ void topk_wg(const double *__restrict__ L, int n, int
     if (lane < C) {
       const double ck = s.cand_key[lane];
       const int ci = s.cand_idx[lane];
+      double kq[4];
+      int iq[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {  // slots past C hold stale bytes, never used
+        kq[j] = s.cand_key[min(4 * w + j, 63)];
+        iq[j] = s.cand_idx[min(4 * w + j, 63)];
+      }
+      __builtin_amdgcn_sched_barrier(0);  // every read in flight before the first use
       int r = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int q = 4 * w + j;
-        if (q < C) {
-          const double kq = s.cand_key[q];
-          const int iq = s.cand_idx[q];
-          r += (kq > ck || (kq == ck && iq < ci)) ? 1 : 0;
-        }
-      }
+      for (int j = 0; j < 4; ++j)
+        if (4 * w + j < C) r += (kq[j] > ck || (kq[j] == ck && iq[j] < ci)) ? 1 : 0;
       if (r) atomicAdd(&s.rank[lane], r);
     }
     __syncthreads();
