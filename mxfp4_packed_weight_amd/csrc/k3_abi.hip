@@ -953,7 +953,7 @@ k3_status k3_moe_permute(const int32_t *idx, int T, int k, int n_experts,
   K3_LAUNCH(fn, launch_permute(idx, T, k, n_experts,
                                perm_out(base, W, counts, offsets, pair_token,
                                         pair_slot),
-                               gate_up_mfma_tok(), stream));
+                               gate_up_mfma_tok(), gate_up_mfma_tok(), stream));
   return K3_OK;
 }
 
@@ -1015,7 +1015,8 @@ static k3_status batched_common(const char *fn, const uint16_t *X,
     return K3_OK;
   }
   K3_LAUNCH(fn, launch_topk_f64(logits, bias, T, n_experts, k, ix, wt, stream));
-  K3_LAUNCH(fn, launch_permute(ix, T, k, n_experts, o, gate_up_mfma_tok(), stream));
+  K3_LAUNCH(fn, launch_permute(ix, T, k, n_experts, o, gate_up_mfma_tok(), down_mfma_pack_tok(),
+                               stream));
   const long long P = (long long)T * k;
   const int max_items = (int)(std::min<long long>(n_experts, P) + P / gate_up_mfma_tok() + 1);
   uint16_t *hp = reinterpret_cast<uint16_t *>(base + B.hp);
@@ -1165,7 +1166,8 @@ k3_status k3_moe_prefill(const uint16_t *X, const double *logits,
   const int max_items =
       (int)(std::min<long long>(n_experts, P) + P / prefill_tok_batch() + 1);
   K3_LAUNCH(fn, launch_topk_f64(logits, bias, T, n_experts, k, ix, wt, stream));
-  K3_LAUNCH(fn, launch_permute(ix, T, k, n_experts, o, prefill_tok_batch(), stream));
+  K3_LAUNCH(fn, launch_permute(ix, T, k, n_experts, o, prefill_tok_batch(), prefill_tok_batch(),
+                               stream));
   K3_LAUNCH(fn, launch_quant_bf16(X, T, hidden, base + B.xq, base + B.xsc, stream));
   K3_LAUNCH(fn, launch_prefill_gate_up(base + B.xq, base + B.xsc, experts, o,
                                        max_items, hidden, inter, hq, hsc, h_f32,

@@ -49,13 +49,13 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     int32_t *__restrict__ pair_token, int32_t *__restrict__ pair_slot,
     int32_t *__restrict__ pair_pos, int32_t *__restrict__ item_e,
     int32_t *__restrict__ item_off, int32_t *__restrict__ item_cnt,
-    int32_t *__restrict__ n_items, int32_t *__restrict__ n_bad, int item_tok) {
+    int32_t *__restrict__ n_items, int32_t *__restrict__ n_bad, int item_tok, int pack_tok) {
   __shared__ int cnt[K3_MAX_EXPERTS];
   __shared__ int start[K3_MAX_EXPERTS];  // offsets, then running fill base
   __shared__ unsigned long long mask[K3_MAX_EXPERTS];
   __shared__ int chunk_e[kPermThreads];
   __shared__ int tmp[kPermThreads / 64];
-  __shared__ int bad, chunk_slow;
+  __shared__ int bad, chunk_slow, n_large;
   const int tid = threadIdx.x;
   const int P = T * k;
   for (int e = tid; e < n; e += kPermThreads) cnt[e] = 0;
@@ -150,23 +150,34 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
       __syncthreads();
     }
   }
-  // work items: ceil(cnt/tok) per expert, in expert order
-  auto cut = [&](int tok, int32_t *ie, int32_t *ioff, int32_t *icnt, int32_t *ni) {
-    int li = 0;
-    for (int e = e0; e < e1; ++e) li += (cnt[e] + tok - 1) / tok;
-    int ibase = block_scan_incl(li, tmp) - li;
+  // work items: ceil(cnt/tok) per expert; those of more than pack pairs
+  // first, then the others, each class in expert order. ni[0] = all items,
+  // ni[1] = the first class's.
+  auto cut = [&](int tok, int pack, int32_t *ie, int32_t *ioff, int32_t *icnt, int32_t *ni) {
+    int nl = 0, ns = 0;
+    for (int e = e0; e < e1; ++e)
+      for (int s = 0; s < cnt[e]; s += tok) (min(tok, cnt[e] - s) > pack ? nl : ns) += 1;
+    const int lb = block_scan_incl(nl, tmp) - nl;
+    const int sb = block_scan_incl(ns, tmp) - ns;
+    if (tid == kPermThreads - 1) n_large = lb + nl;
+    __syncthreads();
+    int il = lb, is = n_large + sb;
     for (int e = e0; e < e1; ++e) {
       const int off = offsets[e];
       for (int s = 0; s < cnt[e]; s += tok) {
-        ie[ibase] = e;
-        ioff[ibase] = off + s;
-        icnt[ibase] = min(tok, cnt[e] - s);
-        ++ibase;
+        const int c = min(tok, cnt[e] - s);
+        const int at = c > pack ? il++ : is++;
+        ie[at] = e;
+        ioff[at] = off + s;
+        icnt[at] = c;
       }
     }
-    if (tid == kPermThreads - 1) *ni = ibase;
+    if (tid == kPermThreads - 1) {
+      ni[0] = is;
+      ni[1] = n_large;
+    }
   };
-  cut(item_tok, item_e, item_off, item_cnt, n_items);
+  cut(item_tok, pack_tok, item_e, item_off, item_cnt, n_items);
   if (tid == 0) *n_bad = bad;
 }
 
@@ -219,11 +230,11 @@ __global__ __launch_bounds__(256) void combine_batched_kernel(
 }  // namespace
 
 hipError_t launch_permute(const int32_t *idx, int T, int k, int n,
-                          const PermOut &o, int item_tok, hipStream_t s) {
+                          const PermOut &o, int item_tok, int pack_tok, hipStream_t s) {
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, s, idx, T,
                      k, n, o.counts, o.offsets, o.pair_token, o.pair_slot,
                      o.pair_pos, o.item_e, o.item_off, o.item_cnt, o.n_items,
-                     o.n_bad, item_tok);
+                     o.n_bad, item_tok, pack_tok);
   return hipGetLastError();
 }
 

@@ -120,13 +120,17 @@ __global__ __launch_bounds__(kBmWaves * 64) void batched_mfma_kernel(
   const ExpertLayout L = expert_layout(hidden, inter);
   const MatLayout &M = kDown ? L.down : L.gu;
   const int Tt = M.ntiles, ngrp = (Tt + kBmWaves - 1) / kBmWaves;
+  // this launch's items: gate/up all of them; down the first it.n[1] (more
+  // than kPackTok pairs) for NP = 3, the others for NP = 1
   const int u = blockIdx.x;
-  if (u >= ldc(it.n) * ngrp) return;  // the whole workgroup leaves together
+  const int i_lo = kPacked ? ldc(it.n + 1) : 0, i_hi = kDown && !kPacked ? ldc(it.n + 1) : ldc(it.n);
+  const int item = i_lo + u / ngrp;
+  if (item >= i_hi) return;  // the whole workgroup leaves together
   const int wave = wave_id();
-  const int item = u / ngrp, s = kBmWaves * (u % ngrp) + wave;
+  const int s = kBmWaves * (u % ngrp) + wave;
   const bool active = s < Tt;  // else: streams tile Tt - 1, stores nothing
   const int e = ldc(it.e + item), off = ldc(it.off + item), cnt = ldc(it.cnt + item);
-  if (kDown && (cnt <= kPackTok) != kPacked) return;  // the other launch's item
+  if (kDown && (cnt <= kPackTok) != kPacked) return;  // not this launch's (never, when ordered)
   const uint8_t *tile = ldc(experts + e) + (kDown ? L.down_offset : 0) +
                         (size_t)(active ? s : Tt - 1) * M.tile_bytes;
   const int G = M.G, G4 = M.G4;
@@ -375,6 +379,7 @@ __global__ __launch_bounds__(kBmWaves * 64) void batched_mfma_kernel(
 }  // namespace
 
 int gate_up_mfma_tok() { return kBmTok; }
+int down_mfma_pack_tok() { return kPackTok; }
 
 // max_items: an upper bound of the work items the permutation can make.
 hipError_t launch_gate_up_mfma(const uint16_t *X, const uint8_t *const *experts,
@@ -395,13 +400,17 @@ hipError_t launch_down_mfma(const uint16_t *hp, const uint8_t *const *experts, c
   const ExpertLayout L = expert_layout(hidden, inter);
   const BmItems it{o.item_e, o.item_off, o.item_cnt, o.n_items};
   const long long ngrp = (L.down.ntiles + kBmWaves - 1) / kBmWaves;
-  // items of at most kPackTok pairs, then the others
+  // the items of at most kPackTok pairs (after the others in the item
+  // order), then the others
   hipLaunchKernelGGL((batched_mfma_kernel<true, 1>), dim3((unsigned)(max_items * ngrp)),
                      dim3(kBmWaves * 64), 0, s, nullptr, o.pair_token, experts, it, hidden, inter,
                      P, const_cast<uint16_t *>(hp), yp);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((batched_mfma_kernel<true, kPieces>), dim3((unsigned)(max_items * ngrp)),
+  // the first class holds at most P / (kPackTok + 1) items
+  const long long n_large = std::min<long long>(max_items, P / (kPackTok + 1));
+  if (n_large < 1) return hipSuccess;
+  hipLaunchKernelGGL((batched_mfma_kernel<true, kPieces>), dim3((unsigned)(n_large * ngrp)),
                      dim3(kBmWaves * 64), 0, s, nullptr, o.pair_token, experts, it, hidden, inter,
                      P, const_cast<uint16_t *>(hp), yp);
   return hipGetLastError();

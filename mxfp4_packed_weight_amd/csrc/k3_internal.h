@@ -113,12 +113,16 @@ struct PermOut {
   int32_t *counts, *offsets, *pair_token, *pair_slot, *pair_pos;
   int32_t *item_e, *item_off, *item_cnt, *n_items, *n_bad;
 };
+// Work items of at most item_tok pairs of one expert; those of more than
+// pack_tok pairs come first (n_items[1] of them), then the others
+// (n_items[0] in all). pack_tok >= item_tok keeps plain expert order.
 hipError_t launch_permute(const int32_t *idx, int T, int k, int n,
-                          const PermOut &o, int item_tok, hipStream_t s);
+                          const PermOut &o, int item_tok, int pack_tok, hipStream_t s);
 // Batched gate/up and down on the matrix unit, over items of at most
 // gate_up_mfma_tok() tokens; X 16-byte aligned. hp: the three bf16 pieces
 // of h, [3][P][inter]; yp [P][hidden] fp32.
 int gate_up_mfma_tok();
+int down_mfma_pack_tok();  // items of at most this many pairs take the packed down launch
 hipError_t launch_gate_up_mfma(const uint16_t *X, const uint8_t *const *experts,
                                const PermOut &o, int max_items, long long P, int hidden,
                                int inter, uint16_t *hp, hipStream_t s);
