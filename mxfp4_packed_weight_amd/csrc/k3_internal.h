@@ -198,6 +198,22 @@ hipError_t launch_shared_down(const float *h, const uint16_t *const *shared, int
 // the logits, gate/up, down, combine. slots: 2 * kMaxSyncGrid arrival words
 // (moe_experts_grid() <= kMaxSyncGrid workgroups); val: this call's value,
 // never reused in the process.
+// Work items spread over the XCDs. Workgroups are dealt to the eight XCDs
+// round-robin by index (b % 8 runs on XCD b % 8), and each XCD has its own
+// L2. With a grid of xcd_grid(items, units) workgroups, xcd_unit(b, units)
+// gives workgroup b the unit item * units + j of item 8 (p / units) + b % 8,
+// j = p % units, p = b / 8: XCD x takes items x, x + 8, ... with all of an
+// item's units, so the activations an item's workgroups share come into one
+// L2 once, and every XCD gets an equal share of the items.
+constexpr int kXcds = 8;
+inline long long xcd_grid(long long items, long long units) {
+  return kXcds * ((items + kXcds - 1) / kXcds) * units;
+}
+__device__ __forceinline__ int xcd_unit(int b, int units) {
+  const int x = b % kXcds, p = b / kXcds;
+  return (kXcds * (p / units) + x) * units + p % units;
+}
+
 constexpr int kMaxSyncGrid = 1024;
 constexpr int kMaxDevices = 64;  // per-device state of the library
 // Runs `launch` (which enqueues one grid whose workgroups wait for each

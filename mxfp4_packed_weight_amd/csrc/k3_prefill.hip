@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_gemm_kernel(
   const ExpertLayout L = expert_layout(hidden, inter);
   const MatLayout &M = kGateUp ? L.gu : L.down;
   const int Tt = M.ntiles, ngrp = (Tt + kPfWaves - 1) / kPfWaves;
-  const int u = blockIdx.x;
+  const int u = xcd_unit(blockIdx.x, ngrp);
   if (u >= ldc(it.n) * ngrp) return;  // the whole workgroup leaves together
   const int wave = wave_id();
   const int item = u / ngrp, s = kPfWaves * (u % ngrp) + wave;
@@ -443,7 +443,7 @@ hipError_t launch_prefill_gate_up(const uint8_t *xq, const uint8_t *xsc,
   const ExpertLayout L = expert_layout(hidden, inter);
   const PfItems it{o.item_e, o.item_off, o.item_cnt, o.n_items};
   const long long ngrp = (L.gu.ntiles + kPfWaves - 1) / kPfWaves;
-  hipLaunchKernelGGL(prefill_gemm_kernel<true>, dim3((unsigned)(max_items * ngrp)),
+  hipLaunchKernelGGL(prefill_gemm_kernel<true>, dim3((unsigned)xcd_grid(max_items, ngrp)),
                      dim3(kPfWaves * 64),
                      0, s, xq, xsc, o.pair_token, experts, it, hidden, inter, hq,
                      hsc, h32, nullptr);
@@ -457,7 +457,7 @@ hipError_t launch_prefill_down(const uint8_t *hq, const uint8_t *hsc,
   const ExpertLayout L = expert_layout(hidden, inter);
   const PfItems it{o.item_e, o.item_off, o.item_cnt, o.n_items};
   const long long ngrp = (L.down.ntiles + kPfWaves - 1) / kPfWaves;
-  hipLaunchKernelGGL(prefill_gemm_kernel<false>, dim3((unsigned)(max_items * ngrp)),
+  hipLaunchKernelGGL(prefill_gemm_kernel<false>, dim3((unsigned)xcd_grid(max_items, ngrp)),
                      dim3(kPfWaves * 64), 0, s, hq, hsc, o.pair_token, experts, it, hidden,
                      inter, nullptr, nullptr, nullptr, yp);
   return hipGetLastError();
