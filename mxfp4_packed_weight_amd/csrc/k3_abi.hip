@@ -72,20 +72,24 @@ uint64_t next_layer_seq() {
 }
 
 // Permutation scratch of T*k pairs (after the caller's counts, offsets,
-// pair_token, pair_slot): pair_pos, item_e, item_off, item_cnt, n_items, n_bad.
+// pair_token, pair_slot): pair_pos, item_e, item_off, item_cnt, n_items,
+// n_bad, and the per-chunk table when the chunks are placed by workgroups of
+// their own (chunk_table 0 otherwise).
 struct PermWs {
-  size_t pair_pos, item_e, item_off, item_cnt, n_items, n_bad, total;
+  size_t pair_pos, item_e, item_off, item_cnt, n_items, n_bad, chunk_table, total;
 };
-PermWs perm_ws(size_t off, long long P) {
+PermWs perm_ws(size_t off, int T, int k) {
   PermWs W;
-  const size_t a = align256(sizeof(int32_t) * (size_t)P);
+  const size_t a = align256(sizeof(int32_t) * (size_t)T * k);
   W.pair_pos = off;
   W.item_e = W.pair_pos + a;
   W.item_off = W.item_e + a;
   W.item_cnt = W.item_off + a;
   W.n_items = W.item_cnt + a;
   W.n_bad = W.n_items + 256;
-  W.total = W.n_bad + 256;
+  const size_t ct = sizeof(int32_t) * (size_t)perm_chunk_table_ints(T);
+  W.chunk_table = ct ? W.n_bad + 256 : 0;
+  W.total = W.n_bad + 256 + align256(ct);
   return W;
 }
 
@@ -115,7 +119,7 @@ BatchWs batch_ws(int T, int n, int hidden, int inter, int k) {
   off += align256((size_t)P * sizeof(int32_t));
   B.pair_slot = off;
   off += align256((size_t)P * sizeof(int32_t));
-  B.perm = perm_ws(off, P);
+  B.perm = perm_ws(off, T, k);
   off = B.perm.total;
   B.h = off;
   off += align256((size_t)P * inter * sizeof(float));
@@ -151,7 +155,7 @@ PrefillWs prefill_ws(int T, int n, int hidden, int inter, int k) {
   B.offsets = take((size_t)n * sizeof(int32_t));
   B.pair_token = take((size_t)P * sizeof(int32_t));
   B.pair_slot = take((size_t)P * sizeof(int32_t));
-  B.perm = perm_ws(off, P);
+  B.perm = perm_ws(off, T, k);
   off = B.perm.total;
   B.xq = take((size_t)T * hidden / 2);
   B.xsc = take((size_t)T * hidden / 32);
@@ -175,6 +179,7 @@ PermOut perm_out(uint8_t *base, const PermWs &W, int32_t *counts,
   o.item_cnt = reinterpret_cast<int32_t *>(base + W.item_cnt);
   o.n_items = reinterpret_cast<int32_t *>(base + W.n_items);
   o.n_bad = reinterpret_cast<int32_t *>(base + W.n_bad);
+  o.chunk_table = W.chunk_table ? reinterpret_cast<int32_t *>(base + W.chunk_table) : nullptr;
   return o;
 }
 
@@ -928,7 +933,7 @@ static k3_status check_batch(const char *fn, int T, int n, int k) {
 
 size_t k3_moe_permute_workspace_bytes(int T, int k) {
   if (T < 1 || k < 1 || k > K3_MAX_TOPK || (long long)T * k > kMaxPairs) return 0;
-  return perm_ws(0, (long long)T * k).total;
+  return perm_ws(0, T, k).total;
 }
 
 k3_status k3_moe_permute(const int32_t *idx, int T, int k, int n_experts,
@@ -947,7 +952,7 @@ k3_status k3_moe_permute(const int32_t *idx, int T, int k, int n_experts,
   K3_NEED(fn, T >= 1 && k >= 1 && k <= K3_MAX_TOPK && (long long)T * k <= kMaxPairs,
           "%s: T=%d k=%d outside T >= 1, 1 <= k <= %d, T*k <= %d", fn, T, k,
           K3_MAX_TOPK, kMaxPairs);
-  const PermWs W = perm_ws(0, (long long)T * k);
+  const PermWs W = perm_ws(0, T, k);
   if (k3_status s = need_ws(fn, ws_bytes, W.total)) return s;
   uint8_t *base = static_cast<uint8_t *>(ws);
   K3_LAUNCH(fn, launch_permute(idx, T, k, n_experts,

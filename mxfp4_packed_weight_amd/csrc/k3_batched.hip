@@ -13,6 +13,8 @@ namespace k3 {
 namespace {
 
 constexpr int kPermThreads = 1024;
+constexpr int kPermCache = 32;  // chunks whose entries a thread can hold in registers
+constexpr int kPermMaxChunks = 256;  // chunks placed by workgroups of their own, at most
 
 // Inclusive prefix sum over the block's 1024 threads (wave scans + LDS).
 __device__ int block_scan_incl(int v, int *tmp) {
@@ -37,12 +39,130 @@ __device__ int block_scan_incl(int v, int *tmp) {
   return r;
 }
 
-// One workgroup. Pairs p = t*k + j with expert idx[p]; entries outside
+// Stable placement of one chunk of 64 tokens (pairs [c, c + cP)), given
+// start[e] in LDS = the position of expert e's first pair of the chunk;
+// advances start[] past the chunk's pairs. Every thread of the workgroup
+// takes part; entry(i) is the expert of pair c + i (a thread asks only for
+// the i it owns: i = tid + 1024 j). Fast path: bit t of mask[e] says token
+// t chose e, so a pair's rank among its expert's pairs is start[e] plus the
+// chosen bits below its token. A token that names an expert twice (never the
+// case for top-k output) or an entry outside [0, n) sends the chunk to the
+// exact path, which counts earlier equal entries one by one. The barriers
+// order LDS only: the pairs' stores need not be complete before the next
+// chunk (nothing here reads them).
+template <class Entry>
+__device__ __forceinline__ void place_chunk(Entry entry, int c, int cP, int k, int n, int *start,
+                                            unsigned long long *mask, int *chunk_e,
+                                            int &chunk_slow, int32_t *__restrict__ pair_token,
+                                            int32_t *__restrict__ pair_slot,
+                                            int32_t *__restrict__ pair_pos) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < n; e += kPermThreads) mask[e] = 0ull;
+  if (tid == 0) chunk_slow = 0;
+  lds_barrier();
+  for (int i = tid; i < cP; i += kPermThreads) {
+    const int e = entry(i);
+    if (e >= 0 && e < n) {
+      const unsigned long long bit = 1ull << (i / k);
+      if (atomicOr(&mask[e], bit) & bit) chunk_slow = 1;
+    } else {
+      chunk_slow = 1;
+    }
+  }
+  lds_barrier();
+  if (!chunk_slow) {
+    for (int i = tid; i < cP; i += kPermThreads) {
+      const int p = c + i, e = entry(i), tl = i / k;
+      const int q = start[e] + __popcll(mask[e] & ((1ull << tl) - 1ull));
+      pair_token[q] = p / k;
+      pair_slot[q] = p % k;
+      pair_pos[p] = q;
+    }
+    lds_barrier();
+    for (int e = tid; e < n; e += kPermThreads) start[e] += __popcll(mask[e]);
+    lds_barrier();
+    return;
+  }
+  for (int b = 0; b < cP; b += kPermThreads) {
+    const int p = c + b + tid;
+    const int e = b + tid < cP ? entry(b + tid) : -1;
+    const bool ok = e >= 0 && e < n;
+    chunk_e[tid] = ok ? e : -1;
+    lds_barrier();
+    if (ok) {
+      int r = 0;
+      for (int i = 0; i < tid; ++i) r += chunk_e[i] == e;
+      const int q = start[e] + r;
+      pair_token[q] = p / k;
+      pair_slot[q] = p % k;
+      pair_pos[p] = q;
+    } else if (b + tid < cP) {
+      pair_pos[p] = -1;
+    }
+    lds_barrier();
+    // advance each expert's base by its pairs here (its last entry writes)
+    if (ok) {
+      bool last = true;
+      for (int i = tid + 1; i < kPermThreads; ++i)
+        if (chunk_e[i] == e) {
+          last = false;
+          break;
+        }
+      if (last) {
+        int r = 0;
+        for (int i = 0; i <= tid; ++i) r += chunk_e[i] == e;
+        start[e] += r;
+      }
+    }
+    lds_barrier();
+  }
+}
+
+// Work items: ceil(cnt/tok) per expert, from cnt[] (LDS) and offsets[]
+// (written by this workgroup); those of more than pack pairs first, then
+// the others, each class in expert order. ni[0] = all items, ni[1] = the
+// first class's. Thread tid owns experts [e0, e1).
+__device__ __forceinline__ void cut_items(const int *cnt, const int32_t *offsets, int e0, int e1,
+                                          int tok, int pack, int *tmp, int &n_large,
+                                          int32_t *__restrict__ ie, int32_t *__restrict__ ioff,
+                                          int32_t *__restrict__ icnt, int32_t *__restrict__ ni) {
+  const int tid = threadIdx.x;
+  int nl = 0, ns = 0;
+  for (int e = e0; e < e1; ++e)
+    for (int s = 0; s < cnt[e]; s += tok) (min(tok, cnt[e] - s) > pack ? nl : ns) += 1;
+  const int lb = block_scan_incl(nl, tmp) - nl;
+  const int sb = block_scan_incl(ns, tmp) - ns;
+  if (tid == kPermThreads - 1) n_large = lb + nl;
+  __syncthreads();
+  int il = lb, is = n_large + sb;
+  for (int e = e0; e < e1; ++e) {
+    const int off = offsets[e];
+    for (int s = 0; s < cnt[e]; s += tok) {
+      const int c = min(tok, cnt[e] - s);
+      const int at = c > pack ? il++ : is++;
+      ie[at] = e;
+      ioff[at] = off + s;
+      icnt[at] = c;
+    }
+  }
+  if (tid == kPermThreads - 1) {
+    ni[0] = is;
+    ni[1] = n_large;
+  }
+}
+
+// The permutation. Pairs p = t*k + j with expert idx[p]; entries outside
 // [0, n) are not placed (they are counted in *n_bad).
 //   counts[e], offsets[e]        run length and start of expert e
 //   pair_token[q], pair_slot[q]  the q-th pair in (expert, pair index) order
 //   pair_pos[p]                  q of pair p (-1 when not placed)
 //   items: item_e/off/cnt[i]     expert, first q, tokens (<= item_tok)
+// permute_kernel does it all in one workgroup, a chunk of 64 tokens at a
+// time. For many chunks the chunks go to workgroups of their own in three
+// launches instead: perm_count_kernel (each chunk's pairs per expert),
+// perm_scan_kernel (one workgroup: runs, offsets, each chunk's start per
+// expert, items) and perm_place_kernel (each chunk placed from its starts).
+// The positions are the same.
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     const int32_t *__restrict__ idx, int T, int k, int n,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
@@ -61,12 +181,33 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   for (int e = tid; e < n; e += kPermThreads) cnt[e] = 0;
   if (tid == 0) bad = 0;
   __syncthreads();
-  for (int p = tid; p < P; p += kPermThreads) {
-    const int e = idx[p];
-    if (e >= 0 && e < n)
-      atomicAdd(&cnt[e], 1);
-    else
-      atomicAdd(&bad, 1);
+  // When a chunk of 64 tokens has at most one pair per thread and there are
+  // at most kPermCache chunks, each thread loads its pair of every chunk
+  // once, here: ec[c] is entry 64 k c + tid. The chunk loop then reads no
+  // global memory, so its waits do not wait for its stores either.
+  const int nchunks = (T + 63) / 64;
+  const bool cached = 64 * k <= kPermThreads && nchunks <= kPermCache;
+  int ec[kPermCache];
+  if (cached) {
+#pragma unroll
+    for (int c = 0; c < kPermCache; ++c)
+      ec[c] = c < nchunks && tid < min(64, T - 64 * c) * k ? idx[64 * k * c + tid] : 0;
+#pragma unroll
+    for (int c = 0; c < kPermCache; ++c)
+      if (c < nchunks && tid < min(64, T - 64 * c) * k) {
+        if (ec[c] >= 0 && ec[c] < n)
+          atomicAdd(&cnt[ec[c]], 1);
+        else
+          atomicAdd(&bad, 1);
+      }
+  } else {
+    for (int p = tid; p < P; p += kPermThreads) {
+      const int e = idx[p];
+      if (e >= 0 && e < n)
+        atomicAdd(&cnt[e], 1);
+      else
+        atomicAdd(&bad, 1);
+    }
   }
   __syncthreads();
   // exclusive scan of cnt over experts: each thread owns a contiguous span
@@ -82,103 +223,107 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     run += cnt[e];
   }
   __syncthreads();
-  // Stable placement, 64 tokens at a time. Fast path: bit t of mask[e] says
-  // token t0+t chose e, so a pair's rank among its expert's pairs is start[e]
-  // plus the chosen bits below its token. A token that names an expert twice
-  // (never the case for top-k output) or an entry outside [0, n) sends the
-  // chunk to the exact path, which counts earlier equal entries one by one.
-  for (int t0 = 0; t0 < T; t0 += 64) {
-    const int tn = min(64, T - t0);
-    const int c = t0 * k, cP = tn * k;  // this chunk's pairs [c, c + cP)
-    for (int e = tid; e < n; e += kPermThreads) mask[e] = 0ull;
-    if (tid == 0) chunk_slow = 0;
-    __syncthreads();
-    for (int i = tid; i < cP; i += kPermThreads) {
-      const int e = idx[c + i];
-      if (e >= 0 && e < n) {
-        const unsigned long long bit = 1ull << (i / k);
-        if (atomicOr(&mask[e], bit) & bit) chunk_slow = 1;
-      } else {
-        chunk_slow = 1;
-      }
+  // one loop instance per case, so that the cached one holds no global load
+  if (cached) {
+    for (int t0 = 0; t0 < T; t0 += 64) {
+      place_chunk([&](int) { return ec[0]; }, t0 * k, min(64, T - t0) * k, k, n, start, mask,
+                  chunk_e, chunk_slow, pair_token, pair_slot, pair_pos);
+#pragma unroll
+      for (int j = 0; j + 1 < kPermCache; ++j) ec[j] = ec[j + 1];
     }
-    __syncthreads();
-    if (!chunk_slow) {
-      for (int i = tid; i < cP; i += kPermThreads) {
-        const int p = c + i, e = idx[p], tl = i / k;
-        const int q = start[e] + __popcll(mask[e] & ((1ull << tl) - 1ull));
-        pair_token[q] = p / k;
-        pair_slot[q] = p % k;
-        pair_pos[p] = q;
-      }
-      __syncthreads();
-      for (int e = tid; e < n; e += kPermThreads) start[e] += __popcll(mask[e]);
-      __syncthreads();
-      continue;
-    }
-    for (int b = 0; b < cP; b += kPermThreads) {
-      const int p = c + b + tid;
-      const int e = b + tid < cP ? idx[p] : -1;
-      const bool ok = e >= 0 && e < n;
-      chunk_e[tid] = ok ? e : -1;
-      __syncthreads();
-      if (ok) {
-        int r = 0;
-        for (int i = 0; i < tid; ++i) r += chunk_e[i] == e;
-        const int q = start[e] + r;
-        pair_token[q] = p / k;
-        pair_slot[q] = p % k;
-        pair_pos[p] = q;
-      } else if (b + tid < cP) {
-        pair_pos[p] = -1;
-      }
-      __syncthreads();
-      // advance each expert's base by its pairs here (its last entry writes)
-      if (ok) {
-        bool last = true;
-        for (int i = tid + 1; i < kPermThreads; ++i)
-          if (chunk_e[i] == e) {
-            last = false;
-            break;
-          }
-        if (last) {
-          int r = 0;
-          for (int i = 0; i <= tid; ++i) r += chunk_e[i] == e;
-          start[e] += r;
-        }
-      }
-      __syncthreads();
+  } else {
+    for (int t0 = 0; t0 < T; t0 += 64) {
+      const int c = t0 * k;
+      place_chunk([&](int i) { return idx[c + i]; }, c, min(64, T - t0) * k, k, n, start, mask,
+                  chunk_e, chunk_slow, pair_token, pair_slot, pair_pos);
     }
   }
-  // work items: ceil(cnt/tok) per expert; those of more than pack pairs
-  // first, then the others, each class in expert order. ni[0] = all items,
-  // ni[1] = the first class's.
-  auto cut = [&](int tok, int pack, int32_t *ie, int32_t *ioff, int32_t *icnt, int32_t *ni) {
-    int nl = 0, ns = 0;
-    for (int e = e0; e < e1; ++e)
-      for (int s = 0; s < cnt[e]; s += tok) (min(tok, cnt[e] - s) > pack ? nl : ns) += 1;
-    const int lb = block_scan_incl(nl, tmp) - nl;
-    const int sb = block_scan_incl(ns, tmp) - ns;
-    if (tid == kPermThreads - 1) n_large = lb + nl;
-    __syncthreads();
-    int il = lb, is = n_large + sb;
-    for (int e = e0; e < e1; ++e) {
-      const int off = offsets[e];
-      for (int s = 0; s < cnt[e]; s += tok) {
-        const int c = min(tok, cnt[e] - s);
-        const int at = c > pack ? il++ : is++;
-        ie[at] = e;
-        ioff[at] = off + s;
-        icnt[at] = c;
-      }
-    }
-    if (tid == kPermThreads - 1) {
-      ni[0] = is;
-      ni[1] = n_large;
-    }
-  };
-  cut(item_tok, pack_tok, item_e, item_off, item_cnt, n_items);
+  cut_items(cnt, offsets, e0, e1, item_tok, pack_tok, tmp, n_large, item_e, item_off, item_cnt,
+            n_items);
   if (tid == 0) *n_bad = bad;
+}
+
+// Each chunk's pairs per expert: cs[chunk][e], and its entries outside
+// [0, n) in cs[nchunks][chunk]. One workgroup per chunk.
+__global__ __launch_bounds__(kPermThreads) void perm_count_kernel(
+    const int32_t *__restrict__ idx, int T, int k, int n, int32_t *__restrict__ cs) {
+  __shared__ int cnt[K3_MAX_EXPERTS];
+  __shared__ int bad;
+  const int tid = threadIdx.x, ch = blockIdx.x, nchunks = gridDim.x;
+  const int c = 64 * ch * k, cP = min(64, T - 64 * ch) * k;
+  for (int e = tid; e < n; e += kPermThreads) cnt[e] = 0;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  for (int i = tid; i < cP; i += kPermThreads) {
+    const int e = idx[c + i];
+    if (e >= 0 && e < n)
+      atomicAdd(&cnt[e], 1);
+    else
+      atomicAdd(&bad, 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < n; e += kPermThreads) cs[(size_t)ch * n + e] = cnt[e];
+  if (tid == 0) cs[(size_t)nchunks * n + ch] = bad;
+}
+
+// One workgroup: the runs (counts, offsets), each chunk's start per expert
+// (cs[chunk][e] becomes the position of expert e's first pair of the chunk),
+// the work items and *n_bad.
+__global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
+    int n, int nchunks, int32_t *__restrict__ cs, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ item_e, int32_t *__restrict__ item_off,
+    int32_t *__restrict__ item_cnt, int32_t *__restrict__ n_items, int32_t *__restrict__ n_bad,
+    int item_tok, int pack_tok) {
+  __shared__ int cnt[K3_MAX_EXPERTS];
+  __shared__ int tmp[kPermThreads / 64];
+  __shared__ int n_large;
+  const int tid = threadIdx.x;
+  const int per = (n + kPermThreads - 1) / kPermThreads;
+  const int e0 = min(n, tid * per), e1 = min(n, e0 + per);
+  int local = 0;
+  for (int e = e0; e < e1; ++e) {
+    int t = 0;
+    for (int ch = 0; ch < nchunks; ++ch) t += cs[(size_t)ch * n + e];
+    cnt[e] = t;
+    local += t;
+  }
+  int run = block_scan_incl(local, tmp) - local;
+  for (int e = e0; e < e1; ++e) {
+    counts[e] = cnt[e];
+    offsets[e] = run;
+    int at = run;
+    for (int ch = 0; ch < nchunks; ++ch) {
+      const int v = cs[(size_t)ch * n + e];
+      cs[(size_t)ch * n + e] = at;
+      at += v;
+    }
+    run += cnt[e];
+  }
+  if (tid == 0) {
+    int b = 0;
+    for (int ch = 0; ch < nchunks; ++ch) b += cs[(size_t)nchunks * n + ch];
+    *n_bad = b;
+  }
+  __syncthreads();
+  cut_items(cnt, offsets, e0, e1, item_tok, pack_tok, tmp, n_large, item_e, item_off, item_cnt,
+            n_items);
+}
+
+// One chunk per workgroup, placed from its starts cs[chunk][e].
+__global__ __launch_bounds__(kPermThreads) void perm_place_kernel(
+    const int32_t *__restrict__ idx, int T, int k, int n, const int32_t *__restrict__ cs,
+    int32_t *__restrict__ pair_token, int32_t *__restrict__ pair_slot,
+    int32_t *__restrict__ pair_pos) {
+  __shared__ int start[K3_MAX_EXPERTS];
+  __shared__ unsigned long long mask[K3_MAX_EXPERTS];
+  __shared__ int chunk_e[kPermThreads];
+  __shared__ int chunk_slow;
+  const int ch = blockIdx.x;
+  const int c = 64 * ch * k, cP = min(64, T - 64 * ch) * k;
+  for (int e = threadIdx.x; e < n; e += kPermThreads) start[e] = cs[(size_t)ch * n + e];
+  __syncthreads();
+  place_chunk([&](int i) { return idx[c + i]; }, c, cP, k, n, start, mask, chunk_e, chunk_slow,
+              pair_token, pair_slot, pair_pos);
 }
 
 struct Items {
@@ -229,8 +374,24 @@ __global__ __launch_bounds__(256) void combine_batched_kernel(
 
 }  // namespace
 
+int perm_chunk_table_ints(int T) {
+  const int nchunks = (T + 63) / 64;
+  return nchunks > 1 && nchunks <= kPermMaxChunks ? (nchunks + 1) * K3_MAX_EXPERTS : 0;
+}
+
 hipError_t launch_permute(const int32_t *idx, int T, int k, int n,
                           const PermOut &o, int item_tok, int pack_tok, hipStream_t s) {
+  const int nchunks = (T + 63) / 64;
+  if (o.chunk_table && perm_chunk_table_ints(T) > 0) {
+    hipLaunchKernelGGL(perm_count_kernel, dim3(nchunks), dim3(kPermThreads), 0, s, idx, T, k, n,
+                       o.chunk_table);
+    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kPermThreads), 0, s, n, nchunks,
+                       o.chunk_table, o.counts, o.offsets, o.item_e, o.item_off, o.item_cnt,
+                       o.n_items, o.n_bad, item_tok, pack_tok);
+    hipLaunchKernelGGL(perm_place_kernel, dim3(nchunks), dim3(kPermThreads), 0, s, idx, T, k, n,
+                       o.chunk_table, o.pair_token, o.pair_slot, o.pair_pos);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, s, idx, T,
                      k, n, o.counts, o.offsets, o.pair_token, o.pair_slot,
                      o.pair_pos, o.item_e, o.item_off, o.item_cnt, o.n_items,

@@ -112,7 +112,11 @@ hipError_t launch_down(const float *h, const uint8_t *const *experts,
 struct PermOut {
   int32_t *counts, *offsets, *pair_token, *pair_slot, *pair_pos;
   int32_t *item_e, *item_off, *item_cnt, *n_items, *n_bad;
+  int32_t *chunk_table;  // perm_chunk_table_ints(T) ints, or null: one workgroup does it all
 };
+// Scratch of the permutation's per-chunk counts when its chunks of 64 tokens
+// go to workgroups of their own (0: one workgroup places them all).
+int perm_chunk_table_ints(int T);
 // Work items of at most item_tok pairs of one expert; those of more than
 // pack_tok pairs come first (n_items[1] of them), then the others
 // (n_items[0] in all). pack_tok >= item_tok keeps plain expert order.

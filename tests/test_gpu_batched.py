@@ -48,8 +48,11 @@ def check_permutation(idx, n):
     return c
 
 
+# (2048, 16, 896) and (100, 64, 4096): chunks of 64 tokens placed by workgroups
+# of their own; (16448, 4, 64): 257 chunks, one workgroup places them all.
 @pytest.mark.parametrize("T,k,n", [(64, 16, 896), (1, 1, 1), (1, 16, 896), (3, 5, 7),
-                                   (2048, 16, 896), (100, 64, 4096), (37, 8, 13)])
+                                   (2048, 16, 896), (100, 64, 4096), (37, 8, 13),
+                                   (16448, 4, 64)])
 def test_permute_matches_oracle(T, k, n):
     say(f"permute T={T} k={k} n={n}")
     rng = np.random.default_rng(T * 1000 + k)
@@ -63,6 +66,28 @@ def test_permute_duplicates_within_a_token():
     rng = np.random.default_rng(7)
     idx = rng.integers(0, 5, size=(40, 6)).astype(np.int32)
     check_permutation(idx, 5)
+
+
+def test_permute_exact_and_fast_chunks_mixed():
+    """Chunks of 64 tokens that take the exact path (a repeated expert inside
+    a token, an out-of-range entry) between chunks that take the fast one,
+    with every entry of a chunk held by one thread, and 33 chunks (each entry
+    read from device memory)."""
+    rng = np.random.default_rng(11)
+    for T, k, n in ((300, 8, 896), (2112, 16, 896)):
+        say(f"permute with mixed chunks T={T} k={k} n={n}")
+        idx = np.stack([rng.choice(n, k, replace=False) for _ in range(T)]).astype(np.int32)
+        idx[5, 1] = idx[5, 0]          # chunk 0: repeated expert
+        idx[130, 3] = idx[130, 2]      # chunk 2
+        idx[200, 0] = n + 3            # chunk 3: out of range
+        keep = (idx >= 0) & (idx < n)
+        c, o, pt, ps = gpu_permute(idx, n)
+        ref = sorted(((t, j) for t in range(T) for j in range(k) if keep[t, j]),
+                     key=lambda p: (idx[p], p[0], p[1]))
+        assert c.sum() == keep.sum()
+        assert np.array_equal(c, np.bincount(idx[keep], minlength=n))
+        assert pt[:len(ref)].tolist() == [t for t, _ in ref]
+        assert ps[:len(ref)].tolist() == [j for _, j in ref]
 
 
 def test_permute_skips_out_of_range_entries():
