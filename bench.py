@@ -980,6 +980,9 @@ TRAFFIC = {
                        "k3_batched.hip", "k3_batched_mfma.hip")},
     "c5": {"json": "prefill_c5_traffic.json", "anchor": "prefill_gemm_kernel<true>",
            "kernels": {"top-k": "topk_kernel", "permutation": "permute_kernel",
+                       "permutation: chunk counts": "perm_count_kernel",
+                       "permutation: runs and starts": "perm_scan_kernel",
+                       "permutation: placement": "perm_place_kernel",
                        "x quantiser": "quant_kernel", "gate/up GEMM": "prefill_gemm_kernel<true>",
                        "down GEMM": "prefill_gemm_kernel<false>",
                        "combine": "combine_batched_kernel"},
