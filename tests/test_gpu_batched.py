@@ -165,6 +165,27 @@ def test_batched_from_logits_small(n, hidden, inter, k, T):
     say(f"batched small: max normwise {err:.3e}")
 
 
+@pytest.mark.parametrize("case", ["all_equal", "coarse"])
+def test_one_token_fused_topk_with_tied_logits(case):
+    """T = 1 from logits takes the decode layer's fused launch. Its top-k
+    either leaves the routing weights to the waves that combine (at most 64
+    candidates: key ties among them, "coarse") or computes them on its
+    single-wave path (more than 64: every logit equal). idx, w and y against
+    the oracle, ties to the lower expert index."""
+    cfg, seed = 73, 6
+    n, hidden, inter, k = 96, 256, 128, 8
+    say(f"fused top-k with tied logits ({case}) n={n} k={k}")
+    pool = D.build_expert_pool(seed, cfg, n, hidden, inter, 114, 120, workers=2)
+    X = W.tokens_bf16(seed, cfg, 1, hidden)
+    if case == "all_equal":
+        logits = np.full((1, n), 0.25)
+    else:
+        logits = np.round(W.zipf_router_logits(seed, 1, n, 1.1, cfg).astype(np.float64) * 4) / 4
+    out = run_batched(pool, X, n, hidden, inter, k, logits=logits)
+    check_tokens(out, X, logits, lambda e: W.expert_weights(seed, cfg, e, hidden, inter, 114, 120),
+                 k, hidden, inter, [0])
+
+
 def _edge_exponent_expert(seed, cfg, e, hidden, inter, xmax_col):
     """An expert whose gate/up and down exponent bytes include 0, 1, 2 and
     255 at random places, and gate rows 0, 1 and 2 with exponent bytes 253, 254 and
