@@ -52,7 +52,7 @@ __device__ __forceinline__ double wave_sum(double v) {
   return __hiloint2double(hi, lo);
 }
 
-constexpr int kRouterCPL = 16;  // 16-byte chunks per lane in flight
+constexpr int kRouterCPL = 8;  // 16-byte chunks per lane in flight
 constexpr int kRouterSplit = 4;  // waves per router row
 
 // This wave's share of one router row's logit: wave `part` of kRouterSplit
