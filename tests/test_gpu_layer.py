@@ -99,13 +99,16 @@ def assert_same(a, b):
         assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key
 
 
-def check_against_oracle(out, x, R, seed, cfg, n, hidden, inter, k, elo, ehi):
+def check_against_oracle(out, x, R, seed, cfg, n, hidden, inter, k, elo, ehi, weights=None):
+    """weights(e), when given, returns expert e's canonical weights (else
+    they are generated from seed, cfg, elo and ehi)."""
     lg_ref = oracle.router_logits(x, R)
     assert np.max(np.abs(out["logits"] - lg_ref)) <= 1e-12 * np.max(np.abs(lg_ref))
     idx_ref, _ = oracle.topk(lg_ref, k)
     assert np.array_equal(out["idx"], idx_ref), (out["idx"], idx_ref)
-    experts = {int(e): W.expert_weights(seed, cfg, int(e), hidden, inter, elo, ehi)
-               for e in idx_ref}
+    if weights is None:
+        weights = lambda e: W.expert_weights(seed, cfg, e, hidden, inter, elo, ehi)  # noqa: E731
+    experts = {int(e): weights(int(e)) for e in idx_ref}
     oracle.set_threads(16)
     y_ref, idx2, w_ref = oracle.moe_layer(x, R, experts, k, hidden, inter)
     assert np.array_equal(idx2, idx_ref)
@@ -149,6 +152,42 @@ def test_decode_layer_small(n, hidden, inter, k):
     x = gen.normal_bf16(gen.key(seed, cfg, gen.KIND_TOKENS), hidden)
     out = run_layer(pool, up(R), x, n, hidden, inter, k)
     check_against_oracle(out, x, R, seed, cfg, n, hidden, inter, k, 114, 120)
+
+
+def test_decode_layer_c3_shapes_with_exponent_255():
+    """Experts of the C3 shape (7168/1536, top-16, so both stages of the
+    expert launch run on the matrix unit) whose gate, up and down hold
+    exponent byte 255 in about 8% of their groups: such a group contributes
+    nothing ([A176] "What byte-identical actually costs"; [SAT] "Reduction
+    one"), which the matrix route does by zeroing the group's codes before
+    the product. Against the oracle, which skips the group; the layer's bits
+    equal the stage-by-stage calls' (run_layer)."""
+    import torch
+    from mxfp4_packed_weight_amd.pool import ExpertPool
+    cfg, seed, n, hidden, inter, k = 74, 9, 24, W.HIDDEN, W.INTER, W.TOPK
+    say(f"decode layer with exponent 255, n={n} hidden={hidden} inter={inter} k={k}")
+    pool = ExpertPool(n, hidden, inter)
+    ex = {}
+    rng = np.random.default_rng(2550)
+    for e in range(n):
+        E = W.expert_weights(seed, cfg, e, hidden, inter, 114, 120)
+        for part in ("gate", "up", "down"):
+            nib, sc = E[part]
+            sc = sc.copy()
+            sc[rng.random(sc.shape) < 0.08] = 255
+            E[part] = (nib, sc)
+        ex[e] = E
+        pool.load(e, E)
+    torch.cuda.synchronize()
+    R = gen.normal_bf16(gen.key(seed, cfg, gen.KIND_ROUTER), n * hidden, 0, 0.02).reshape(
+        n, hidden)
+    x = gen.normal_bf16(gen.key(seed, cfg, gen.KIND_TOKENS), hidden)
+    out = run_layer(pool, up(R), x, n, hidden, inter, k)
+    assert all(int((ex[int(e)][p][1] == 255).sum()) > 0 for e in out["idx"]
+               for p in ("gate", "up", "down"))
+    err, _ = check_against_oracle(out, x, R, seed, cfg, n, hidden, inter, k, 114, 120,
+                                  weights=lambda e: ex[e])
+    say(f"decode layer exponent 255: y {err:.3e}")
 
 
 def test_decode_layer_4096_experts_top64():
