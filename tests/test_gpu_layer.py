@@ -190,6 +190,39 @@ def test_decode_layer_c3_shapes_with_exponent_255():
     say(f"decode layer exponent 255: y {err:.3e}")
 
 
+def test_decode_layer_c3_shapes_activation_group_off_the_digit_range():
+    """x with one group of 32 values near 2^-100, below the range of the
+    matrix unit's activation digits (2^-87): the expert launch's gate/up
+    stage flags it while building x's digits and streams its tiles on the
+    vector ALU instead; down (h in range) stays on the matrix unit. C3
+    expert shape, top-16 of 24. Against the oracle; the layer's bits equal
+    the stage-by-stage calls', which make the same choice."""
+    cfg, seed, n, hidden, inter, k = 75, 10, 24, W.HIDDEN, W.INTER, W.TOPK
+    say(f"decode layer with an x group near 2^-100, n={n} hidden={hidden} inter={inter} k={k}")
+    pool = D.build_expert_pool(seed, cfg, n, hidden, inter, 114, 120, workers=4)
+    R = gen.normal_bf16(gen.key(seed, cfg, gen.KIND_ROUTER), n * hidden, 0, 0.02).reshape(
+        n, hidden)
+    x = gen.normal_bf16(gen.key(seed, cfg, gen.KIND_TOKENS), hidden)
+    f = (x.astype(np.uint32) << 16).view(np.float32)
+    f[32:64] *= np.float32(2.0 ** -100)  # exact: a power of two, far from underflow
+    x = (f.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.max(np.abs(f[32:64])) < 2.0 ** -87 and np.max(np.abs(f[32:64])) > 0
+    out = run_layer(pool, up(R), x, n, hidden, inter, k)
+    err, _ = check_against_oracle(out, x, R, seed, cfg, n, hidden, inter, k, 114, 120)
+    # The same token with that group zeroed (a zero group is in range) takes the
+    # matrix route: the selection is the same and y agrees to rounding, but
+    # not in every bit, since the two routes sum in different orders.
+    import torch
+    x0 = x.copy()
+    x0[32:64] = 0
+    ws = empty(K.k3_moe_workspace_bytes(1, n, hidden, inter, k), torch.uint8)
+    o0 = layer_outputs(pool, up(R), up(x0), n, hidden, inter, k, ws)
+    assert np.array_equal(o0["idx"], out["idx"])
+    assert normwise(o0["y32"], out["y32"]) <= TOL
+    assert not np.array_equal(o0["y32"].view(np.uint32), out["y32"].view(np.uint32))
+    say(f"decode layer, x group off the digit range: y {err:.3e}")
+
+
 def test_decode_layer_4096_experts_top64():
     """The largest selection the ABI takes: 4096 experts (beyond 1024 the
     layer ranks with the separate top-k launch), k = 64, small experts."""
