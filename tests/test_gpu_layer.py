@@ -223,6 +223,47 @@ def test_decode_layer_c3_shapes_activation_group_off_the_digit_range():
     say(f"decode layer, x group off the digit range: y {err:.3e}")
 
 
+def test_decode_layer_c3_shapes_h_group_off_the_digit_range():
+    """Every expert's gate and up rows 0..31 carry exponent byte 67
+    (weights near 2^-60), so h's first group of 32 is near 2^-108: below
+    the activation digits' range (2^-87), though an ordinary fp32 value.
+    The expert launch's down stage flags it while building h's digits and
+    streams on the vector ALU (its wait for the producers is then passed
+    again, at once); gate/up stays on the matrix unit. C3 expert shape,
+    top-16 of 24. Against the oracle; the layer's bits equal the
+    stage-by-stage calls'."""
+    import torch
+    from mxfp4_packed_weight_amd.pool import ExpertPool
+    cfg, seed, n, hidden, inter, k = 76, 11, 24, W.HIDDEN, W.INTER, W.TOPK
+    say(f"decode layer with an h group near 2^-108, n={n} hidden={hidden} inter={inter} k={k}")
+    pool = ExpertPool(n, hidden, inter)
+    ex = {}
+    for e in range(n):
+        E = W.expert_weights(seed, cfg, e, hidden, inter, 114, 120)
+        for part in ("gate", "up"):
+            nib, sc = E[part]
+            sc = sc.copy()
+            sc[:32, :] = 67
+            E[part] = (nib, sc)
+        ex[e] = E
+        pool.load(e, E)
+    torch.cuda.synchronize()
+    R = gen.normal_bf16(gen.key(seed, cfg, gen.KIND_ROUTER), n * hidden, 0, 0.02).reshape(
+        n, hidden)
+    x = gen.normal_bf16(gen.key(seed, cfg, gen.KIND_TOKENS), hidden)
+    out = run_layer(pool, up(R), x, n, hidden, inter, k)
+    err, _ = check_against_oracle(out, x, R, seed, cfg, n, hidden, inter, k, 114, 120,
+                                  weights=lambda e: ex[e])
+    # h's first group is in the flagged range for every selected expert
+    xf = oracle.bf16_to_f64(x)
+    for e in out["idx"][:4]:
+        g = oracle.gemv(*ex[int(e)]["gate"], xf)[:32]
+        u = oracle.gemv(*ex[int(e)]["up"], xf)[:32]
+        h = g / (1.0 + np.exp(-g)) * u
+        assert 0 < np.max(np.abs(h)) < 2.0 ** -87, np.max(np.abs(h))
+    say(f"decode layer, h group off the digit range: y {err:.3e}")
+
+
 def test_decode_layer_4096_experts_top64():
     """The largest selection the ABI takes: 4096 experts (beyond 1024 the
     layer ranks with the separate top-k launch), k = 64, small experts."""
