@@ -426,6 +426,19 @@ k3_status k3_moe_layer_shared(const uint16_t *x, const uint16_t *router_w,
                               int32_t *idx, float *w, double *logits, void *ws,
                               size_t ws_bytes, k3_stream_t stream);
 
+/* Bounded waits, and a way for tests to see them run out. The launches
+ * whose workgroups hand data to each other (the decode layer's expert
+ * launch behind k3_moe_layer and its peers, and k3_expert_swiglu_ws) poll
+ * for each hand-off at most K3_WAIT_LIMIT_DEFAULT times, about a second;
+ * if the polls run out the launch still ends, and writes NaN to y_f32 and
+ * 0x7FC0 to y instead of its result. k3_set_wait_limit sets that number of
+ * polls for later launches on the current device: 0 makes every such wait
+ * fail at once, so that report can be checked without holding the device
+ * for a second. K3_ERR_CONFIG for polls < 0. The value is copied to the device
+ * synchronously; a launch already running may use either value. */
+#define K3_WAIT_LIMIT_DEFAULT (1 << 20)
+k3_status k3_set_wait_limit(int polls);
+
 /* Calibration read for measurements: streams `bytes` (a positive multiple
  * of 16; buf 16-byte aligned, device) once with 16-byte non-temporal loads,
  * one 512-thread workgroup per compute unit. The HBM read rate it reaches is

@@ -20,6 +20,7 @@ _lib = None
 
 K3_OK, K3_ERR_ARG, K3_ERR_CONFIG, K3_ERR_MEMORY, K3_ERR_DEVICE = 0, 1, 2, 3, 4
 K3_MAX_EXPERTS, K3_MAX_TOPK, K3_MAX_SHARED = 4096, 64, 8
+K3_WAIT_LIMIT_DEFAULT = 1 << 20
 
 # (name, restype, argtypes) of every exported symbol in include/k3moe.h
 _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -77,6 +78,7 @@ SIGNATURES = [
     ("k3_moe_prefill", _i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp,
                             _vp, _vp, _vp, _sz, _vp]),
     ("k3_hbm_read_probe", _i, [_vp, _sz, _vp, _vp]),
+    ("k3_set_wait_limit", _i, [_i]),
     ("k3_shared_expert_bytes", _sz, [_i, _i]),
     ("k3_shared_experts", _i, [_vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
     ("k3_moe_layer_shared_workspace_bytes", _sz, [_i, _i, _i, _i, _i, _i]),
@@ -356,6 +358,10 @@ def k3_moe_prefill(X, logits, bias, experts, n_experts, hidden, inter, k, T, Y, 
 
 def k3_hbm_read_probe(buf, nbytes, sink, stream=None):
     _call("k3_hbm_read_probe", _dp(buf), nbytes, _dp(sink), _stream(stream))
+
+
+def k3_set_wait_limit(polls):
+    _call("k3_set_wait_limit", polls)
 
 
 # ---- shared experts ---------------------------------------------------------

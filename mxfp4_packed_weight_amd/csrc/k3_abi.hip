@@ -472,6 +472,14 @@ k3_status k3_hbm_read_probe(const void *buf, size_t bytes, uint32_t *sink,
   return K3_OK;
 }
 
+k3_status k3_set_wait_limit(int polls) {
+  const char *fn = "k3_set_wait_limit";
+  K3_NEED(fn, polls >= 0, "%s: polls=%d must be >= 0", fn, polls);
+  K3_LAUNCH(fn, set_expert_wait_limit(polls));
+  K3_LAUNCH(fn, set_expert_one_wait_limit(polls));
+  return K3_OK;
+}
+
 size_t k3_expert_dense_bytes(int hidden, int inter) {
   if (check_expert_dims("k3_expert_dense_bytes", hidden, inter) != K3_OK) return 0;
   return (size_t)3 * hidden * inter * sizeof(float);

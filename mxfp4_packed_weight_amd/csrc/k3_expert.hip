@@ -21,6 +21,10 @@
 
 namespace k3 {
 
+// Polls of each hand-off wait in this file's launches (per device; see
+// set_expert_wait_limit).
+__device__ int expert_wait_limit = kSpinLimit;
+
 namespace {
 
 constexpr int kThreads = kNW * 64;
@@ -334,7 +338,9 @@ __global__ __launch_bounds__(kThreads) void moe_experts_kernel(
         if (t0 < t1 && wave_id() == 0) {
           const int c_lo = tile_owner(t0 / Td * Tg, total_gu, G);
           const int c_hi = tile_owner(((t1 - 1) / Td + 1) * Tg - 1, total_gu, G);
-          if (!wave_wait_range(slots, c_lo, c_hi - c_lo + 1, val) && lane == 0) bad = 1;
+          if (!wave_wait_range(slots, c_lo, c_hi - c_lo + 1, val, expert_wait_limit) &&
+              lane == 0)
+            bad = 1;
         }
         lds_barrier();  // wave 0's poll has returned; the quads stay in flight
         hb = after_wait(hb);
@@ -361,11 +367,12 @@ __global__ __launch_bounds__(kThreads) void moe_experts_kernel(
   }
   for (int r = r_lo + wave_id(); r < r_hi; r += kNW) {
     const int owner = lane < k ? tile_owner(lane * Td + r, total, G) : 0;
-    if (!wave_wait_owners(done, owner, k, val) && lane == 0) bad = 1;
+    if (!wave_wait_owners(done, owner, k, val, expert_wait_limit) && lane == 0) bad = 1;
     if constexpr (kShared) {  // the workgroups that wrote these rows of ys
       const int s_lo = tile_owner(r * kTileRows, hidden, G);
       const int s_hi = tile_owner(min((r + 1) * kTileRows, hidden) - 1, hidden, G);
-      if (!wave_wait_range(done, s_lo, s_hi - s_lo + 1, val) && lane == 0) bad = 1;
+      if (!wave_wait_range(done, s_lo, s_hi - s_lo + 1, val, expert_wait_limit) && lane == 0)
+        bad = 1;
     }
     const int row = r * kTileRows + lane;
     if (row < hidden) {
@@ -472,6 +479,10 @@ hipError_t launch_gate_up_routed(const uint16_t *x, const double *logits,
 }
 
 unsigned moe_experts_grid() { return (unsigned)num_cus(); }
+
+hipError_t set_expert_wait_limit(int polls) {
+  return hipMemcpyToSymbol(HIP_SYMBOL(expert_wait_limit), &polls, sizeof(polls));
+}
 
 namespace {
 // Two launches whose workgroups wait for each other (this file's expert

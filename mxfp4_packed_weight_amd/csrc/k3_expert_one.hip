@@ -24,6 +24,10 @@
 
 namespace k3 {
 
+// Polls of the hand-off wait in this file's launch (per device; see
+// set_expert_one_wait_limit).
+__device__ int expert_one_wait_limit = kSpinLimit;
+
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -143,7 +147,9 @@ __global__ __launch_bounds__(kThreads) void expert_one_kernel(
   // every unit's partials are in: h = SiLU(g) * u into LDS. A thread takes
   // h values i and i + kThreads and issues the loads of both before adding
   // (in chunk order).
-  if (wave == 0 && !wave_wait_range(slots, 0, min(units, G), val) && lane == 0) bad = 1;
+  if (wave == 0 && !wave_wait_range(slots, 0, min(units, G), val, expert_one_wait_limit) &&
+      lane == 0)
+    bad = 1;
   __syncthreads();
   const float *P = after_wait(P1);
   for (int i0 = threadIdx.x; i0 < inter; i0 += 2 * kThreads) {
@@ -194,6 +200,10 @@ __global__ __launch_bounds__(kThreads) void expert_one_kernel(
 }
 
 }  // namespace
+
+hipError_t set_expert_one_wait_limit(int polls) {
+  return hipMemcpyToSymbol(HIP_SYMBOL(expert_one_wait_limit), &polls, sizeof(polls));
+}
 
 int expert_one_split(int hidden, int inter) {
   const ExpertLayout L = expert_layout(hidden, inter);

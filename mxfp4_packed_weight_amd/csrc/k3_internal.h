@@ -225,6 +225,10 @@ constexpr int kMaxDevices = 64;  // per-device state of the library
 // (k3_expert.hip).
 hipError_t grid_sync_launch(hipStream_t s, const std::function<hipError_t()> &launch);
 unsigned moe_experts_grid();
+// Poll limits of the hand-off waits on the current device: the expert
+// launch (k3_expert.hip) and the one-expert launch (k3_expert_one.hip).
+hipError_t set_expert_wait_limit(int polls);
+hipError_t set_expert_one_wait_limit(int polls);
 // The shared experts' down stage taken inside the expert launch: hs [n][inter]
 // from an earlier launch, ys [hidden] written here and added by the combine.
 struct SharedStage {

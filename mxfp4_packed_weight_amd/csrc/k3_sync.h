@@ -10,14 +10,16 @@
 // Arrival slots hold a per-call value chosen by the host (unique in the
 // process), so they never need clearing between calls; leftover memory
 // equals a call's value only by a 2^-64 chance. Every wait is bounded:
-// one that runs out reports failure instead of hanging the device.
+// one that runs out reports failure instead of hanging the device. The bound
+// is a number of polls passed by the caller: kSpinLimit, unless a test has
+// lowered it (k3_set_wait_limit) to see that failure reported.
 #pragma once
 
 #include "k3_stream.h"
 
 namespace k3 {
 
-constexpr int kSpinLimit = 1 << 20;  // polls of one wait (~1 s), then fail
+constexpr int kSpinLimit = K3_WAIT_LIMIT_DEFAULT;  // polls of one wait (~1 s), then fail
 
 template <typename T>
 __device__ __forceinline__ void st_dev(T *p, T v) {
@@ -46,12 +48,12 @@ __device__ __forceinline__ T *after_wait(T *p) {
 }
 
 // One wave: waits until slots[i] == val for all i in [first, first + count).
-// False if the poll limit runs out.
+// False if `limit` polls run out.
 __device__ __forceinline__ bool wave_wait_range(const uint64_t *slots,
                                                 int first, int count,
-                                                uint64_t val) {
+                                                uint64_t val, int limit) {
   const int lane = threadIdx.x & 63;
-  for (int it = 0; it < kSpinLimit; ++it) {
+  for (int it = 0; it < limit; ++it) {
     bool ok = true;
     for (int i0 = 0; i0 < count; i0 += 256) {  // four loads in flight per lane
       uint64_t v[4];
@@ -70,12 +72,12 @@ __device__ __forceinline__ bool wave_wait_range(const uint64_t *slots,
 }
 
 // One wave: waits until slots[owner] == val for every lane < count (each
-// lane names its own owner). False if the poll limit runs out.
+// lane names its own owner). False if `limit` polls run out.
 __device__ __forceinline__ bool wave_wait_owners(const uint64_t *slots,
                                                  int owner, int count,
-                                                 uint64_t val) {
+                                                 uint64_t val, int limit) {
   const int lane = threadIdx.x & 63;
-  for (int it = 0; it < kSpinLimit; ++it) {
+  for (int it = 0; it < limit; ++it) {
     const bool mine = lane >= count || ld_dev(slots + owner) == val;
     if (__ballot(!mine) == 0) return true;
     __builtin_amdgcn_s_sleep(1);

@@ -136,6 +136,11 @@ def test_refusals_before_launch(L):
     rc = L.k3_moe_layer(_fake(1), _fake(2), _fake(3), 896, 7168, 1536, 0, _fake(4), _fake(5),
                         need, s)
     assert rc == K.K3_ERR_CONFIG
+    rc = L.k3_set_wait_limit(-1)
+    assert rc == K.K3_ERR_CONFIG and "polls=-1" in K.last_error()
+    text = open(os.path.join(ROOT, "include", "k3moe.h")).read()
+    assert re.search(r"#define K3_WAIT_LIMIT_DEFAULT \(1 << 20\)", text)
+    assert K.K3_WAIT_LIMIT_DEFAULT == 1 << 20
 
 
 def test_refusals_at_the_size_limits(L):
