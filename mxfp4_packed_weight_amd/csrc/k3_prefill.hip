@@ -31,7 +31,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kNB = 4;                 // 16-token column blocks per work item
 constexpr int kPfTok = 16 * kNB;       // tokens per prefill work item
 #ifndef K3_PF_DEPTH
-#define K3_PF_DEPTH 4
+#define K3_PF_DEPTH 2
 #endif
 constexpr int kPfDepth = K3_PF_DEPTH;  // weight quads in flight per wave (LDS)
 constexpr int kPfBDepth = 2;           // activation quads in flight (registers)

@@ -139,8 +139,8 @@ def check_prefill(out, X, logits, experts_of, k, hidden, inter, tokens):
     return max(errs_h), max(errs_y)
 
 
-# The GEMM kernels take a steady path when K has at least 6 quads of 128
-# (K >= 768) and a short path below; tile groups of four are ragged when a
+# The GEMM kernels take a steady path when K has at least 4 quads of 128
+# (K >= 512, with the weight ring two quads deep) and a short path below; tile groups of four are ragged when a
 # matrix's tile count is not a multiple of 4, and the last quad is partial
 # when K % 128 != 0. The last three cases put the steady path on gate/up,
 # then on down (with experts of more than 64 tokens, two items each), with
