@@ -430,8 +430,8 @@ k3_status k3_moe_layer_shared(const uint16_t *x, const uint16_t *router_w,
  * whose workgroups hand data to each other (the decode layer's expert
  * launch behind k3_moe_layer and its peers, and k3_expert_swiglu_ws) poll
  * for each hand-off at most K3_WAIT_LIMIT_DEFAULT times, about a second;
- * if the polls run out the launch still ends, and writes NaN to y_f32 and
- * 0x7FC0 to y instead of its result. k3_set_wait_limit sets that number of
+ * if the polls run out the launch still ends, and writes NaN to its fp32
+ * output (0x7FC0 to a bf16 one) instead of its result. k3_set_wait_limit sets that number of
  * polls for later launches on the current device: 0 makes every such wait
  * fail at once, so that report can be checked without holding the device
  * for a second. K3_ERR_CONFIG for polls < 0. The value is copied to the device
