@@ -57,3 +57,26 @@ def make_cache(pool, host, n_slots):
     for e in range(pool.n_experts):
         K.k3_cache_set_source(c, e, host[e * eb:(e + 1) * eb])
     return c
+
+
+def layer_outputs(pool, R_d, xd, n, hidden, inter, k, ws):
+    """One decode-layer call (k3_moe_layer_ex) on device inputs; its outputs on the host."""
+    import torch
+    import mxfp4_packed_weight_amd as K
+    y = empty(hidden, torch.int16)
+    y32 = empty(hidden, torch.float32)
+    idx = empty(k, torch.int32)
+    w = empty(k, torch.float32)
+    lg = empty(n, torch.float64)
+    K.k3_moe_layer_ex(xd, R_d, pool.table, n, hidden, inter, k, y, ws, y_f32=y32, idx=idx, w=w,
+                      logits=lg)
+    return dict(y=y.cpu().numpy().view(np.uint16), y32=y32.cpu().numpy(),
+                idx=idx.cpu().numpy(), w=w.cpu().numpy(), logits=lg.cpu().numpy())
+
+
+def assert_same(a, b):
+    """Two layer_outputs results bit for bit."""
+    for key in ("y", "idx"):
+        assert np.array_equal(a[key], b[key]), key
+    for key in ("y32", "w", "logits"):
+        assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key

@@ -19,7 +19,8 @@ import mxfp4_packed_weight_amd as K
 import oracle
 from gen import device as D
 from gen import workloads as W
-from tests._gpu import TOL, empty, make_cache, normwise, pinned_copy, say, up
+from tests._gpu import (TOL, assert_same, empty, layer_outputs, make_cache, normwise,
+                        pinned_copy, say, up)
 
 pytestmark = pytest.mark.gpu
 
@@ -60,19 +61,6 @@ def run_layer(pool, R_d, x, n, hidden, inter, k):
     return out
 
 
-def layer_outputs(pool, R_d, xd, n, hidden, inter, k, ws):
-    import torch
-    y = empty(hidden, torch.int16)
-    y32 = empty(hidden, torch.float32)
-    idx = empty(k, torch.int32)
-    w = empty(k, torch.float32)
-    lg = empty(n, torch.float64)
-    K.k3_moe_layer_ex(xd, R_d, pool.table, n, hidden, inter, k, y, ws, y_f32=y32, idx=idx, w=w,
-                      logits=lg)
-    return dict(y=y.cpu().numpy().view(np.uint16), y32=y32.cpu().numpy(),
-                idx=idx.cpu().numpy(), w=w.cpu().numpy(), logits=lg.cpu().numpy())
-
-
 def stage_outputs(pool, R_d, xd, n, hidden, inter, k):
     """The layer as separate public calls: router, routed gate/up, down,
     combine (two launches where the layer folds them into one)."""
@@ -90,13 +78,6 @@ def stage_outputs(pool, R_d, xd, n, hidden, inter, k):
     K.k3_moe_combine(yp, w, k, hidden, y, y32)
     return dict(y=y.cpu().numpy().view(np.uint16), y32=y32.cpu().numpy(),
                 idx=idx.cpu().numpy(), w=w.cpu().numpy(), logits=lg.cpu().numpy())
-
-
-def assert_same(a, b):
-    for key in ("y", "idx"):
-        assert np.array_equal(a[key], b[key]), key
-    for key in ("y32", "w", "logits"):
-        assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key
 
 
 def check_against_oracle(out, x, R, seed, cfg, n, hidden, inter, k, elo, ehi, weights=None):

@@ -16,8 +16,7 @@ import pytest
 import gen
 import mxfp4_packed_weight_amd as K
 from gen import device as D
-from tests._gpu import empty, say, up
-from tests.test_gpu_layer import assert_same, layer_outputs
+from tests._gpu import assert_same, empty, layer_outputs, say, up
 
 pytestmark = pytest.mark.gpu
 
